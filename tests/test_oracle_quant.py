@@ -1,0 +1,186 @@
+"""Pins of the oracle producers: brute force on tiny tensors, the 2D32
+orientation invariant, finer-scale boundary cases, and the 1D negative control."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import formats as F
+from oracle import quant as Q
+from oracle import philox as P
+
+
+def brute_block(vals, mode="rtn", draws=None, e_override=None):
+    """Quantize one 32-value block with rationals: smallest admissible exponent,
+    then nearest grid value (ties to even code) or SR with the given words."""
+    fr = [Fraction(float(v)) for v in vals]
+    amax = max(abs(v) for v in fr)
+    if e_override is not None:
+        e = e_override
+    elif amax == 0:
+        e = -127
+    else:
+        e = next(e for e in range(-127, 128) if amax <= 6 * Fraction(2) ** e)
+    grid = [Fraction(g) for g in F.E2M1_GRID]
+    nibs = []
+    for j, v in enumerate(fr):
+        y = min(abs(v) / Fraction(2) ** e, Fraction(6))
+        if mode == "rtn":
+            d = [abs(y - g) for g in grid]
+            m = min(d)
+            cands = [c for c in range(8) if d[c] == m]
+            code = min(cands, key=lambda c: (c % 2, c))
+        else:
+            lo = max(c for c in range(8) if grid[c] <= y)
+            if grid[lo] == y:
+                code = lo
+            else:
+                frac = (y - grid[lo]) / (grid[lo + 1] - grid[lo])
+                code = lo + 1 if Fraction(int(draws[j])) < frac * 2**32 else lo
+        neg = np.signbit(float(vals[j]))
+        nibs.append(code | (8 if neg else 0))
+    return nibs, e
+
+
+def test_rows_rtn_brute_force():
+    x = synthetic.tensor((4, 64), std=1.0, seed=3, outlier_rate=0.05, outlier_scale=30.0)
+    x[0, :32] = 0                       # an all-zero block
+    x[1, 5] = 0x8000                    # -0
+    codes, scales = Q.quantize_rows(x)
+    nib = F.unpack_nibbles(codes)
+    xv = F.bf16_bits_to_f64(x)
+    for r in range(4):
+        for b in range(2):
+            exp_nib, e = brute_block(xv[r, 32 * b:32 * b + 32])
+            assert nib[r, 32 * b:32 * b + 32].tolist() == exp_nib
+            assert scales[r, b] == e + 127
+
+
+def test_rows_sr_brute_force_and_index_layout():
+    x = synthetic.tensor((3, 64), std=1e-3, seed=4)
+    seed, offset = 77, 5
+    codes, scales = Q.quantize_rows(x, mode=Q.SR, seed=seed, offset=offset)
+    nib = F.unpack_nibbles(codes)
+    xv = F.bf16_bits_to_f64(x)
+    for r in range(3):
+        for b in range(2):
+            idx = np.arange(r * 64 + 32 * b, r * 64 + 32 * b + 32, dtype=np.uint64)
+            u = P.draws(seed, offset, idx)
+            exp_nib, e = brute_block(xv[r, 32 * b:32 * b + 32], mode="sr", draws=u)
+            assert nib[r, 32 * b:32 * b + 32].tolist() == exp_nib
+            assert scales[r, b] == e + 127
+
+
+def test_sr_scale_is_deterministic_and_equals_rtn_scale():
+    x = synthetic.tensor((16, 256), std=1e-3, seed=5)
+    _, s_rtn = Q.quantize_rows(x)
+    _, s_sr1 = Q.quantize_rows(x, mode=Q.SR, seed=1, offset=0)
+    _, s_sr2 = Q.quantize_rows(x, mode=Q.SR, seed=2, offset=9)
+    assert np.array_equal(s_rtn, s_sr1) and np.array_equal(s_rtn, s_sr2)
+
+
+def test_sr_resume_split_equals_whole():
+    # Draws depend on (seed, offset, logical index) only: quantizing the rows in
+    # two calls with row-offset indices equals one call -- here expressed by
+    # checking the draws of a row range against the draws of the full tensor.
+    idx = np.arange(10 * 64, dtype=np.uint64)
+    whole = P.draws(3, 11, idx)
+    part = P.draws(3, 11, idx[320:])
+    assert np.array_equal(whole[320:], part)
+
+
+def test_cols_equals_rows_of_transpose():
+    x = synthetic.tensor((96, 64), std=1.0, seed=6)
+    c_codes, c_scales = Q.quantize_cols(x)
+    r_codes, r_scales = Q.quantize_rows(np.ascontiguousarray(x.T))
+    assert np.array_equal(c_codes, r_codes) and np.array_equal(c_scales, r_scales)
+
+
+def test_cols_h32_brute_force_from_transform():
+    from oracle.hadamard import h32_fixed_sign
+    x = synthetic.tensor((64, 8), std=1.0, seed=7, outlier_rate=0.05, outlier_scale=20.0)
+    mask = 0xA5C3
+    codes, scales = Q.quantize_cols(x, hadamard=32, sign_mask16=mask)
+    nib = F.unpack_nibbles(codes)
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    for c in range(8):
+        for b in range(2):
+            t = h32_fixed_sign(xf[32 * b:32 * b + 32, c][None, :], mask)[0]
+            exp_nib, e = brute_block(t.astype(np.float64))
+            assert nib[c, 32 * b:32 * b + 32].tolist() == exp_nib
+            assert scales[c, b] == e + 127
+
+
+def test_w2d32_orientation_invariant():
+    w = synthetic.tensor((96, 128), std=0.02, seed=8)
+    rc, rs, cc, cs = Q.quantize_w2d32(w, 0.87)
+    dec_row = F.decode(rc, rs)
+    dec_col = F.decode(cc, cs)
+    assert np.array_equal(dec_row, dec_col.T)                   # Eq. 8
+    assert np.array_equal(F.unpack_nibbles(rc), F.unpack_nibbles(cc).T)
+    # replicated tile scales
+    tiles = rs.reshape(3, 32, 4)
+    assert np.all(tiles == tiles[:, :1, :])
+    assert np.array_equal(rs[::32], cs[::32].T)
+
+
+def test_w2d32_negative_control_1d_quantizers_differ():
+    # Independent 1D encodings along K and along N decode to different weights.
+    w = synthetic.tensor((64, 64), std=0.02, seed=9)
+    k_codes, k_scales = Q.quantize_rows(w)
+    n_codes, n_scales = Q.quantize_cols(w)
+    assert not np.array_equal(F.decode(k_codes, k_scales), F.decode(n_codes, n_scales).T)
+
+
+def test_w2d32_finer_rule_boundaries():
+    # A tile whose maximum scaled by 2^-e_up is 5.1875 or 5.21875 takes the finer
+    # exponent (r < 0.87, i.e. a*2^-e_up < 5.22); 5.25 keeps e_up.
+    for amax, finer in [(5.1875, True), (5.21875, True), (5.25, False), (6.0, False), (3.5, True)]:
+        w = np.zeros((32, 32), dtype=np.float32)
+        w[3, 7] = amax
+        w[0, 0] = 1.0
+        bits = synthetic.bf16_bits(w)
+        rc, rs, cc, cs = Q.quantize_w2d32(bits, 0.87)
+        e_up = int(F.upward_exponent(np.array([amax]))[0])
+        assert int(rs[0, 0]) - 127 == (e_up - 1 if finer else e_up), amax
+    # finer_ratio = 0 disables: every tile uses e_up, which never saturates
+    w = synthetic.tensor((64, 64), std=0.02, seed=10)
+    rc, rs, _, _ = Q.quantize_w2d32(w, 0.0)
+    tiles = F.bf16_bits_to_f64(w).reshape(2, 32, 2, 32)
+    e_up = F.upward_exponent(np.abs(tiles).max(axis=(1, 3)))
+    assert np.array_equal(rs[::32].astype(int) - 127, e_up)
+    y = np.abs(F.decode(rc, rs))
+    assert np.all(y <= 6.0 * np.ldexp(1.0, np.repeat(np.repeat(e_up, 32, 0), 32, 1)))
+
+
+def test_w2d32_brute_force_and_saturation():
+    w = synthetic.tensor((64, 64), std=0.02, seed=11)
+    rc, rs, _, _ = Q.quantize_w2d32(w, 0.87)
+    wv = F.bf16_bits_to_f64(w)
+    nib = F.unpack_nibbles(rc)
+    sat = 0
+    for ti in range(2):
+        for tk in range(2):
+            e = int(rs[32 * ti, tk]) - 127
+            tile = wv[32 * ti:32 * ti + 32, 32 * tk:32 * tk + 32]
+            for r in range(0, 32, 7):
+                exp_nib, _ = brute_block(tile[r], e_override=e)
+                assert nib[32 * ti + r, 32 * tk:32 * tk + 32].tolist() == exp_nib
+            y = np.abs(tile) * 2.0 ** -e
+            sat += int((y > 6).sum())
+            # every element above 6 * 2^e encodes as code 7 (+-6 * 2^e)
+            got = nib[32 * ti:32 * ti + 32, 32 * tk:32 * tk + 32] & 7
+            assert np.all(got[y > 5] == 7)
+    assert sat > 0            # N(0, 0.02) tiles mostly take the finer scale and clip
+
+
+def test_w2d32_finer_rule_fraction_of_tiles():
+    # With W ~ N(0, 0.02) most 32x32 tiles take the finer exponent.
+    w = synthetic.tensor((512, 512), std=0.02, seed=12)
+    _, rs, _, _ = Q.quantize_w2d32(w, 0.87)
+    tiles = F.bf16_bits_to_f64(w).reshape(16, 32, 16, 32)
+    e_up = F.upward_exponent(np.abs(tiles).max(axis=(1, 3)))
+    finer = (rs[::32].astype(int) - 127) == e_up - 1
+    assert 0.5 < finer.mean() <= 1.0
