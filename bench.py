@@ -1,0 +1,333 @@
+"""Benchmark of the MXFP4 producer + block-scaled E2M1 GEMM hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic input.
+The default workload is the full Llama-3-8B SwiGLU FFN step (T 8192, D 4096,
+F 14336): forward (row quantize X, 2D32 W1/W3/W2, fused SwiGLU producer emitting
+h row- and column-facing, W2 Fprop) and backward (row-SR and column-H32 dY, W2
+Dgrad and Wgrad, SwiGLU backward, row-SR and column-H32 dA/dB, column-H32 X,
+W1/W3 Dgrad with accumulation, W1/W3 Wgrad): nine contractions, 8.66 TFLOP.
+
+Prints one JSON line.  `value` = GEMM FLOPs of the step / step time (the
+"quantize+GEMM TFLOP/s": producer time is inside the step).  Timing uses HIP
+events on the stream the kernels run on; inputs are resident in HBM before the
+timed region.  The roofline object covers the dominant kernel (the GEMM);
+cpu_baseline times the CPU oracle on a bounded sample of the same step.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MXFP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA, published
+PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E, published
+METRIC = "MXFP4 quantize+GEMM TFLOP/s (Fprop/Dgrad/Wgrad) and quantizer GB/s, % of peak"
+
+# Algorithmic bytes per element (what the producer must move):
+B_SINGLE = 2 + 0.5 + 1 / 32          # bf16 in, one orientation of codes + scales
+B_2D32 = 2 + 2 * (0.5 + 1 / 32)      # bf16 in, two layouts
+B_SWIGLU_BWD = 4 + 2 + 2 + 2 + 2     # dH fp32, a, b in; dA, dB out
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="ffn_step_8192x4096x14336")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--seed", type=int, default=None)
+    return p.parse_args()
+
+
+class Step:
+    """Holds device inputs/outputs and enqueues one step as a list of named calls."""
+
+    def __init__(self, name, seed, mx, torch):
+        import synthetic
+        self.mx, self.torch = mx, torch
+        self.name = name
+        self.host = synthetic.workload(name, seed=seed)
+        self.seed = synthetic.WORKLOADS[name]["seed"] if seed is None else seed
+        self.mask = mx.fp4_sign_mask_from_seed(self.seed)
+        dev = torch.device("cuda:0")
+        self.d = {k: torch.from_numpy(v.view(np.int16)).to(dev) for k, v in self.host.items()}
+        self.o = {}
+        self.calls = []          # (label, kind, units, fn)
+        getattr(self, "_build_" + name.split("_")[0])()
+
+    def e(self, shape, dtype):
+        key = len(self.o)
+        t = self.torch.empty(shape, dtype=dtype, device="cuda:0")
+        self.o[key] = t
+        return t
+
+    def u8(self, *shape):
+        return self.e(shape, self.torch.uint8)
+
+    def q_rows(self, label, x, mode=0, offset=0):
+        mx, (R, C) = self.mx, x.shape
+        out = (self.u8(R, C // 2), self.u8(R, C // 32))
+        self.calls.append((label, "quant", R * C * B_SINGLE,
+                           lambda: mx.fp4_quantize_rows(x, mode, self.seed, offset, codes=out[0], scales=out[1])))
+        return out
+
+    def q_cols(self, label, x):
+        mx, (R, C) = self.mx, x.shape
+        out = (self.u8(C, R // 2), self.u8(C, R // 32))
+        self.calls.append((label, "quant", R * C * B_SINGLE,
+                           lambda: mx.fp4_quantize_cols(x, 32, self.mask, codes_t=out[0], scales_t=out[1])))
+        return out
+
+    def q_w(self, label, w, row_codes=None, row_scales=None):
+        mx, (N, K) = self.mx, w.shape
+        rc = row_codes if row_codes is not None else self.u8(N, K // 2)
+        rs = row_scales if row_scales is not None else self.u8(N, K // 32)
+        out = (rc, rs, self.u8(K, N // 2), self.u8(K, N // 32))
+        self.calls.append((label, "quant", N * K * B_2D32,
+                           lambda: mx.fp4_quantize_w2d32(w, 0.87, *out)))
+        return out
+
+    def gemm(self, label, a, b, c=None, accumulate=False):
+        mx = self.mx
+        m, n, k = a[0].shape[0], b[0].shape[0], 2 * a[0].shape[1]
+        if c is None:
+            c = self.e((m, n), self.torch.float32)
+        self.calls.append((label, "gemm", 2.0 * m * n * k,
+                           lambda: mx.fp4_gemm(a[0], a[1], b[0], b[1], c=c, accumulate=accumulate)))
+        return c
+
+    # -------------------------------------------------------------- workloads
+    def _build_fprop(self):                      # fprop_256x512x512: 1x32 blocks for X and W
+        xr = self.q_rows("rows(X)", self.d["X"])
+        wr = self.q_rows("rows(W)", self.d["W"])
+        self.gemm("Fprop", xr, wr)
+
+    def _build_attn(self):                       # attn_proj: Fprop + Dgrad
+        xr = self.q_rows("rows(X)", self.d["X"])
+        wq = self.q_w("w2d32(W)", self.d["W"])
+        dyr = self.q_rows("rows(dY,SR)", self.d["dY"], 1, 0)
+        self.gemm("Fprop", xr, wq[:2])
+        self.gemm("Dgrad", dyr, wq[2:])
+
+    def _build_wgrad(self):                      # wgrad_h32: paired H32 Wgrad
+        dyc = self.q_cols("cols(dY,H32)", self.d["dY"])
+        xc = self.q_cols("cols(X,H32)", self.d["X"])
+        self.gemm("Wgrad", dyc, xc)
+
+    def _build_ffn(self):                        # full SwiGLU FFN step
+        torch, mx = self.torch, self.mx
+        X, W1, W3, W2, dY = (self.d[k] for k in ("X", "W1", "W3", "W2", "dY"))
+        T, D = X.shape
+        F = W1.shape[0]
+        xr = self.q_rows("rows(X)", X)
+        w13_rc, w13_rs = self.u8(2 * F, D // 2), self.u8(2 * F, D // 32)
+        w1 = self.q_w("w2d32(W1)", W1, w13_rc[:F], w13_rs[:F])
+        w3 = self.q_w("w2d32(W3)", W3, w13_rc[F:], w13_rs[F:])
+        w2 = self.q_w("w2d32(W2)", W2)
+        a, b = self.e((T, F), torch.int16), self.e((T, F), torch.int16)
+        hr = (self.u8(T, F // 2), self.u8(T, F // 32))
+        hc = (self.u8(F, T // 2), self.u8(F, T // 32))
+        self.calls.append(("swiglu_producer", "producer", 2.0 * T * 2 * F * D,
+                           lambda: mx.fp4_swiglu_producer(xr[0], xr[1], w13_rc, w13_rs, self.mask, True,
+                                                          a, b, hr[0], hr[1], hc[0], hc[1])))
+        self.gemm("W2 Fprop", hr, w2[:2])
+        dyr = self.q_rows("rows(dY,SR)", dY, 1, 0)
+        dyc = self.q_cols("cols(dY,H32)", dY)
+        dh = self.gemm("W2 Dgrad", dyr, w2[2:])
+        self.gemm("W2 Wgrad", dyc, hc)
+        da, db = self.e((T, F), torch.int16), self.e((T, F), torch.int16)
+        self.calls.append(("swiglu_backward", "quant", T * F * B_SWIGLU_BWD,
+                           lambda: mx.fp4_swiglu_backward(dh, a, b, da, db)))
+        dar = self.q_rows("rows(dA,SR)", da, 1, 1)
+        dbr = self.q_rows("rows(dB,SR)", db, 1, 2)
+        dac = self.q_cols("cols(dA,H32)", da)
+        dbc = self.q_cols("cols(dB,H32)", db)
+        xc = self.q_cols("cols(X,H32)", X)
+        dx = self.gemm("W1 Dgrad", dar, w1[2:])
+        self.gemm("W3 Dgrad (+=)", dbr, w3[2:], c=dx, accumulate=True)
+        self.gemm("W1 Wgrad", dac, xc)
+        self.gemm("W3 Wgrad", dbc, xc)
+
+    def run(self, events=None):
+        for i, (_, _, _, fn) in enumerate(self.calls):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    def gemm_flops(self):
+        return sum(u for _, k, u, _ in self.calls if k in ("gemm", "producer"))
+
+
+CPU_SAMPLE_SHAPES = {
+    # reduced instances of each workload: same laws, fewer rows
+    "ffn": dict(T=64, F=1024),
+    "attn": dict(T=64),
+    "wgrad": dict(T=64),
+    "fprop": dict(),
+}
+
+
+def oracle_step(name, h, seed, mask):
+    """The CPU oracle's version of one step on host tensors; returns GEMM FLOPs."""
+    from oracle import gemm as G
+    from oracle import quant as Q
+    from oracle import swiglu as S
+
+    def mm(a, b):
+        return G.gemm_ref(a[0], a[1], b[0], b[1])[0], 2.0 * a[0].shape[0] * b[0].shape[0] * a[0].shape[1] * 2
+
+    kind = name.split("_")[0]
+    flops = 0.0
+    if kind == "fprop":
+        _, f = mm(Q.quantize_rows(h["X"]), Q.quantize_rows(h["W"]))
+        return f
+    if kind == "attn":
+        xr, w = Q.quantize_rows(h["X"]), Q.quantize_w2d32(h["W"])
+        dyr = Q.quantize_rows(h["dY"], Q.SR, seed, 0)
+        for a, b in ((xr, w[:2]), (dyr, w[2:])):
+            flops += mm(a, b)[1]
+        return flops
+    if kind == "wgrad":
+        return mm(Q.quantize_cols(h["dY"], 32, mask), Q.quantize_cols(h["X"], 32, mask))[1]
+    X, W1, W3, W2, dY = (h[k] for k in ("X", "W1", "W3", "W2", "dY"))
+    F = W1.shape[0]
+    xr = Q.quantize_rows(X)
+    w1, w3, w2 = Q.quantize_w2d32(W1), Q.quantize_w2d32(W3), Q.quantize_w2d32(W2)
+    ab, f = mm(xr, (np.concatenate([w1[0], w3[0]]), np.concatenate([w1[1], w3[1]])))
+    flops += f
+    a = S.f32_to_bf16_rne(ab[:, :F].astype(np.float32))
+    b = S.f32_to_bf16_rne(ab[:, F:].astype(np.float32))
+    hb = S.swiglu_h(a, b)
+    hr, hc = Q.quantize_rows(hb), Q.quantize_cols(hb, 32, mask)
+    flops += mm(hr, w2[:2])[1]
+    dyr, dyc = Q.quantize_rows(dY, Q.SR, seed, 0), Q.quantize_cols(dY, 32, mask)
+    dh, f = mm(dyr, w2[2:])
+    flops += f + mm(dyc, hc)[1]
+    da, db = S.swiglu_backward(dh.astype(np.float32), a, b)
+    dar, dbr = Q.quantize_rows(da, Q.SR, seed, 1), Q.quantize_rows(db, Q.SR, seed, 2)
+    dac, dbc, xc = Q.quantize_cols(da, 32, mask), Q.quantize_cols(db, 32, mask), Q.quantize_cols(X, 32, mask)
+    for a_, b_ in ((dar, w1[2:]), (dbr, w3[2:]), (dac, xc), (dbc, xc)):
+        flops += mm(a_, b_)[1]
+    return flops
+
+
+def cpu_baseline(step):
+    """Time the CPU oracle on a bounded sample: the same step on a reduced
+    instance of the workload (same laws and model width, fewer tokens / FFN
+    columns), reported as GEMM FLOPs of that instance per second."""
+    import threadpoolctl
+    import synthetic
+    kind = step.name.split("_")[0]
+    spec = synthetic.WORKLOADS[step.name]["tensors"]
+    red = CPU_SAMPLE_SHAPES[kind]
+    shapes = {}
+    for nm, (R, C, *_rest) in spec.items():
+        if kind == "ffn":
+            T, F = red["T"], red["F"]
+            shapes[nm] = {"X": (T, C), "dY": (T, C), "W1": (F, C), "W3": (F, C), "W2": (R, F)}[nm]
+        elif nm in ("X", "dY") and "T" in red:
+            shapes[nm] = (red["T"], C)
+    h = synthetic.workload(step.name, seed=step.seed, shapes=shapes)
+    t0 = time.perf_counter()
+    flops = oracle_step(step.name, h, step.seed, step.mask)
+    dt = time.perf_counter() - t0
+    info = threadpoolctl.threadpool_info()
+    blas_threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    desc = ", ".join(f"{k} {v[0]}x{v[1]}" for k, v in (shapes or {k: v[:2] for k, v in spec.items()}).items())
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"whole step on a reduced instance ({desc}), {flops / 1e9:.2f} GFLOP in {dt:.1f} s",
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "gpus_requested": args.gpus}))
+        sys.exit(2)
+    import torch
+    import precision_mxfp4_producers_amd as mx
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    mx.load()
+    torch.cuda.set_device(0)
+    print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
+    step = Step(args.workload, args.seed, mx, torch)
+    ncalls = len(step.calls)
+    print(f"[bench] warmup {args.warmup} steps, {ncalls} calls per step", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(ncalls)]
+          for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step.run(ev[s])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    print(f"[bench] {args.steps} steps in {total_ms:.2f} ms", file=sys.stderr, flush=True)
+
+    per = []
+    for i, (label, kind, units, _) in enumerate(step.calls):
+        ms = float(np.median([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+        entry = {"call": label, "ms": round(ms, 4)}
+        if kind in ("gemm", "producer"):
+            entry["tflops"] = round(units / ms / 1e9, 1)
+            entry["frac_mfma_peak"] = round(units / ms / 1e9 / PEAK_MXFP4_TFLOPS, 4)
+        else:
+            entry["gbps"] = round(units / ms / 1e6, 1)
+            entry["frac_hbm_peak"] = round(units / ms / 1e6 / PEAK_HBM_GBPS, 4)
+        per.append(entry)
+
+    flops = step.gemm_flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    gemm_ms = sum(e["ms"] for e, c in zip(per, step.calls) if c[1] == "gemm")
+    gemm_flops = sum(c[2] for c in step.calls if c[1] == "gemm")
+    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
+    q_bytes = sum(c[2] for c in step.calls if c[1] == "quant")
+    q_ms = sum(e["ms"] for e, c in zip(per, step.calls) if c[1] == "quant")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e2m1/e8m0 operands, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "gemm_tflop_per_step": round(flops / 1e12, 3),
+                   "quantizer_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1) if q_ms > 0 else None,
+                   "quantizer_frac_hbm_peak": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if q_ms > 0 else None},
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel", "achieved": round(achieved, 1),
+                     "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MXFP4_TFLOPS, 4),
+                     "traffic": None},
+        "breakdown": per,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(step)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

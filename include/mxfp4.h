@@ -1,0 +1,184 @@
+/*
+ * mxfp4.h -- C ABI of the MXFP4 operand producers and the block-scaled E2M1
+ * GEMM for one linear layer's Fprop, Dgrad and Wgrad on gfx950 (MI355X).
+ *
+ * Method: "Format-Aware Fusion for Fast FP4 Pretraining" (arXiv 2610.00053).
+ *   - §2.2 (Eq. 1): x_hat = delta * Q_E2M1(x / delta); delta is an E8M0 power
+ *     of two shared by 32 values; Q_E2M1 rounds to {0,.5,1,1.5,2,3,4,6} and
+ *     saturates at 6.
+ *   - §2.2.1: activation/gradient scales rounded upward; 2D32 weight tiles may
+ *     take the finer scale when a_T/s_T < 0.87.
+ *   - §2.3 (Eq. 4-6): row-facing and column-facing views feed Fprop, Dgrad and
+ *     Wgrad.
+ *   - §2.4 (Eq. 7-8): one 2D32 weight encoding, both layouts, equal decode.
+ *   - §2.5 (Eq. 9-10): SR only on the row-facing dY for Dgrad; paired
+ *     fixed-sign H32 only on the Wgrad operands.
+ *   - §3.1-§3.2: producers emit every layout, scale and saved value the next
+ *     contraction needs; the gated-FFN producer emits the W2 input directly.
+ *   - App. A.1: SR state is a seed plus a counter offset; explicit buffer
+ *     ownership keeps asynchronous lifetimes safe.
+ *
+ * Data conventions (all calls):
+ *   - Tensors are DEVICE pointers allocated and owned by the caller.  The
+ *     library allocates and frees nothing and keeps no state except a
+ *     thread-local last HIP error.
+ *   - bf16 tensors are passed as their 16-bit patterns (uint16_t).
+ *   - "codes" hold two E2M1 nibbles per byte: element 2j in bits 0-3, element
+ *     2j+1 in bits 4-7; bit 3 of a nibble is the sign (the input's sign bit,
+ *     so -0 and negatives rounding to zero encode as 0x8).
+ *   - "scales" hold one E8M0 byte per 32 values: value 2^(byte-127).  Bytes
+ *     lie in [0, 253]; 0xFF is never written.
+ *   - Row-major everywhere; ld* are leading dimensions in ELEMENTS.
+ *   - Every blocked dimension must be a positive multiple of 32.  Pointers
+ *     must be 16-byte aligned and ld* multiples of 8 (bf16) / 4 (fp32).
+ *   - Outputs must not alias inputs or each other.
+ *   - Inputs must be finite; Inf/NaN inputs give unspecified codes.
+ *   - Each call validates its arguments on the host, enqueues its kernels on
+ *     `stream` (a hipStream_t; NULL = default stream) and returns without
+ *     synchronising.  Results are valid once the stream has reached them.
+ *   - Errors: FP4_EINVAL (null pointer or bad enum), FP4_ESHAPE (dimension
+ *     not a positive multiple of 32, or ld smaller than the row length),
+ *     FP4_EALIGN (alignment), FP4_EHIP (launch failed; fp4_last_hip_error()
+ *     returns the hipError_t value).  Kernels report no data-dependent errors.
+ *     On any error nothing has been enqueued (except after FP4_EHIP, where
+ *     earlier kernels of the same call may have been).
+ */
+#ifndef MXFP4_H_
+#define MXFP4_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP4_OK = 0,
+  FP4_EINVAL = 1,
+  FP4_ESHAPE = 2,
+  FP4_EALIGN = 3,
+  FP4_EHIP = 4
+} fp4_status;
+
+/* Rounding of row-facing producers. */
+enum { FP4_RTN = 0, FP4_SR = 1 };
+
+/*
+ * Row-facing MXFP4 (Q_r): blocks of 32 consecutive values along `cols`, the
+ * reduced (K) axis of the consuming GEMM.  §2.2.1 upward E8M0 scale
+ *   e = smallest integer with amax <= 6 * 2^e, clamped to [-127, 127],
+ * then round-to-nearest-even E2M1 (mode FP4_RTN; activations, weights) or
+ * adjacent-bin stochastic rounding (mode FP4_SR; §2.5 Eq. 9, only for the dY
+ * consumed by Dgrad).  The scale never depends on the rounding mode.
+ * SR draws: Philox4x32-10 keyed by (lo32(seed), hi32(seed)) at counter
+ * (lo32(i>>2), hi32(i>>2), lo32(offset), hi32(offset)), word i&3, with
+ * i = r*cols + c the element's logical row-major index; an element rounds up
+ * iff its word u < frac * 2^32 (exact).  Callers advance `offset` per call and
+ * checkpoint (seed, offset) so resumed runs never reuse draws (App. A.1).
+ *   x       [rows][ldx] bf16, reads rows x cols
+ *   codes   [rows][cols/2] u8,   scales [rows][cols/32] u8
+ */
+fp4_status fp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* codes, uint8_t* scales,
+                             int mode, uint64_t seed, uint64_t offset, void* stream);
+
+/*
+ * Column-facing MXFP4 (Q_c) for the Wgrad operands: blocks of 32 consecutive
+ * ROWS (tokens) of one column, stored transposed so that the token axis is
+ * contiguous (the K axis of Wgrad).  Always deterministic (RTN, upward scale).
+ * hadamard = 32 applies the fixed-sign H32 of §2.5 (Eq. 10) in fp32 before the
+ * scale: v_j = d_(j mod 16) x_j (d_j = -1 iff bit j of sign_mask16 is set),
+ * butterflies (lo,hi) <- (lo+hi, lo-hi) at strides 1,2,4,8,16 in that order,
+ * then t_j = v_j * RN_fp32(2^-2.5).  Both operands of one Wgrad must use the
+ * same sign_mask16.  hadamard = 0 quantizes the values directly.
+ *   x        [rows][ldx] bf16
+ *   codes_t  [cols][rows/2] u8,   scales_t [cols][rows/32] u8
+ */
+fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* codes_t, uint8_t* scales_t,
+                             int hadamard, uint32_t sign_mask16, void* stream);
+
+/*
+ * 2D32 weight producer (§2.4, Eq. 7-8; adaptive rule of §2.2.1).  One
+ * exponent per 32x32 tile: e_up from the tile maximum a_T; the finer exponent
+ * e_up - 1 is taken iff (a_T/6)/2^e_up < finer_ratio (exact comparison) and
+ * e_up > -127 (finer_ratio = 0.87 on the pages; 0 disables).  Values beyond
+ * 6 * 2^e saturate to +-6 * 2^e.  One encoding is emitted in both layouts;
+ * col codes at (k, n) hold the same nibble as row codes at (n, k) and every
+ * scale byte is its tile's byte.
+ *   w           [n][ldw] bf16 (W of Y = X W^T: n outputs, k inputs)
+ *   row_codes   [n][k/2],  row_scales [n][k/32]   (Fprop view, K-major)
+ *   col_codes   [k][n/2],  col_scales [k][n/32]   (Dgrad view, N-major)
+ */
+fp4_status fp4_quantize_w2d32(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
+                              uint8_t* row_codes, uint8_t* row_scales,
+                              uint8_t* col_codes, uint8_t* col_scales,
+                              float finer_ratio, void* stream);
+
+/*
+ * Block-scaled E2M1 GEMM, NT form (§2.3 Eq. 4-6): with both operands stored
+ * K-major with 1x32 E8M0 scales along K,
+ *   C[m][n] = sum_k dec(A)[m][k] * dec(B)[n][k]          (accumulate = 0)
+ *   C[m][n] = C[m][n] + sum_k ...                        (accumulate = 1)
+ * in fp32.  Fprop: A = Q_r(X), B = Q_r(W).  Dgrad: A = Q_r(dY), B = W col
+ * layout.  Wgrad: A = Q_c(dY), B = Q_c(X).  Deterministic (no split-K).
+ *   a_codes [m][k/2], a_scales [m][k/32]; b_codes [n][k/2], b_scales [n][k/32]
+ *   c       [m][ldc] fp32
+ */
+fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k,
+                    const uint8_t* a_codes, const uint8_t* a_scales,
+                    const uint8_t* b_codes, const uint8_t* b_scales,
+                    float* c, int64_t ldc, int accumulate, void* stream);
+
+/*
+ * Fused gated-FFN producer (§3.2): a = X W1^T and b = X W3^T computed together
+ * on the block-scaled MFMA, rounded to bf16 (RNE) and saved for backward; then
+ *   sig = 1/(1 + exp(-a)), s = a*sig, h = bf16(s*b)
+ * in fp32 with single roundings and no fused multiply-add (exp: Cody-Waite
+ * reduction with LN2 split 355/512 + remainder, degree-7 Taylor polynomial in
+ * Horner form, two-step power-of-two scaling; x > 89 -> inf, x < -104 -> 0).
+ * h is emitted directly as MXFP4: row-facing RTN (input of W2 Fprop) and,
+ * if ht_codes is non-NULL, column-facing with H32 (input of W2 Wgrad).
+ *   x_codes [t][d/2], x_scales [t][d/32]       (Q_r(X))
+ *   w13_codes [2f][d/2], w13_scales [2f][d/32] (rows 0..f-1: W1, f..2f-1: W3,
+ *                                               2D32 row layout)
+ *   a_bf16, b_bf16 [t][f]
+ *   h_codes [t][f/2], h_scales [t][f/32]
+ *   ht_codes [f][t/2], ht_scales [f][t/32]     (optional; both or neither)
+ */
+fp4_status fp4_swiglu_producer(int64_t t, int64_t f, int64_t d,
+                               const uint8_t* x_codes, const uint8_t* x_scales,
+                               const uint8_t* w13_codes, const uint8_t* w13_scales,
+                               uint16_t* a_bf16, uint16_t* b_bf16,
+                               uint8_t* h_codes, uint8_t* h_scales,
+                               uint8_t* ht_codes, uint8_t* ht_scales,
+                               uint32_t sign_mask16, void* stream);
+
+/*
+ * SwiGLU backward, elementwise (§3.2), from the fp32 W2 Dgrad output dH and
+ * the saved bf16 a, b, in fp32 with single roundings and no FMA:
+ *   dA = bf16(((dH*b)*sig) * (1 + a*(1 - sig))),   dB = bf16(dH*(a*sig))
+ *   dh [t][lddh] fp32; a_bf16, b_bf16, da_bf16, db_bf16 [t][f]
+ */
+fp4_status fp4_swiglu_backward(int64_t t, int64_t f, const float* dh, int64_t lddh,
+                               const uint16_t* a_bf16, const uint16_t* b_bf16,
+                               uint16_t* da_bf16, uint16_t* db_bf16, void* stream);
+
+/*
+ * Fixed 16-entry sign vector for H32 as a bit mask (bit j set => d_j = -1):
+ * the low 16 bits of word 0 of Philox4x32-10 at counter (0,0,0,0) under key
+ * (lo32(seed), hi32(seed)).  Host-only, no device work.
+ */
+uint32_t fp4_sign_mask_from_seed(uint64_t seed);
+
+/* hipError_t of the last FP4_EHIP on this thread (0 if none). */
+int fp4_last_hip_error(void);
+
+/* ABI version: (major << 16) | minor. */
+int fp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H_ */

@@ -41,12 +41,14 @@ def _encode_blocks(vals64, e, mode, u=None):
     return F.sign_nibble(vals64, code)
 
 
-def quantize_rows(x_bits, mode=RTN, seed=0, offset=0):
+def quantize_rows(x_bits, mode=RTN, seed=0, offset=0, row_ids=None):
     """Row-facing MXFP4 of a bf16 tensor x_bits [R][C] (uint16 bit patterns).
 
     RTN for activations and weights; SR (Eq. 9) for the Dgrad-facing gradient,
     with draws from Philox at (seed, offset) indexed by the element's row-major
-    index r*C + c.  Returns (codes [R][C/2] uint8, scales [R][C/32] uint8).
+    index r*C + c in the full tensor.  `row_ids` gives the full-tensor row
+    numbers when x_bits holds only some of the rows (sampled checks).
+    Returns (codes [R][C/2] uint8, scales [R][C/32] uint8).
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     R, C = x_bits.shape
@@ -56,7 +58,8 @@ def quantize_rows(x_bits, mode=RTN, seed=0, offset=0):
     e = F.upward_exponent(amax)
     u = None
     if mode == SR:
-        idx = (np.arange(R, dtype=np.uint64)[:, None] * np.uint64(C)
+        rows = np.arange(R) if row_ids is None else np.asarray(row_ids)
+        idx = (rows.astype(np.uint64)[:, None] * np.uint64(C)
                + np.arange(C, dtype=np.uint64)[None, :])
         u = P.draws(seed, offset, idx).reshape(R, C // 32, 32)
     nib = _encode_blocks(x, e, mode, u).reshape(R, C)

@@ -1,0 +1,191 @@
+"""Python binding of libmxfp4: MXFP4 producers and block-scaled E2M1 GEMM on gfx950.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in include/mxfp4.h.  torch provides device memory and the current
+stream.  There is no fallback: if the shared library is missing or no GPU is
+visible, the calls raise.
+
+Functions carry the C names.  Output buffers may be passed in (the ABI's
+explicit-ownership form) or are allocated with torch.empty.  bf16 tensors may
+be torch.bfloat16 or int16/uint16 bit patterns.
+"""
+
+import ctypes
+import os
+
+import torch
+
+from .build import lib_path
+
+FP4_RTN, FP4_SR = 0, 1
+STATUS = {0: "FP4_OK", 1: "FP4_EINVAL", 2: "FP4_ESHAPE", 3: "FP4_EALIGN", 4: "FP4_EHIP"}
+
+_lib = None
+
+_i64, _u64, _u32, _int, _vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p
+
+_SIGS = {
+    "fp4_quantize_rows": [_vp, _i64, _i64, _i64, _vp, _vp, _int, _u64, _u64, _vp],
+    "fp4_quantize_cols": [_vp, _i64, _i64, _i64, _vp, _vp, _int, _u32, _vp],
+    "fp4_quantize_w2d32": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.c_float, _vp],
+    "fp4_gemm": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _int, _vp],
+    "fp4_swiglu_producer": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u32, _vp],
+    "fp4_swiglu_backward": [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp],
+    "fp4_sign_mask_from_seed": [_u64],
+    "fp4_last_hip_error": [],
+    "fp4_abi_version": [],
+}
+EXPORTS = tuple(_SIGS)
+
+
+class Fp4Error(RuntimeError):
+    pass
+
+
+def load(path=None):
+    """Load the shared library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or lib_path()
+    if not os.path.exists(path):
+        raise Fp4Error(f"{path} is missing: build it with __graft_entry__.build() "
+                       "or python -m precision_mxfp4_producers_amd.build")
+    lib = ctypes.CDLL(path)
+    for name, args in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_uint32 if name == "fp4_sign_mask_from_seed" else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        msg = STATUS.get(status, str(status))
+        if status == 4:
+            msg += f" (hipError {load().fp4_last_hip_error()})"
+        raise Fp4Error(msg)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise Fp4Error(f"{name} must be a CUDA (HIP) tensor")
+    return t
+
+
+def _bf16_2d(x, name):
+    _dev(x, name)
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise Fp4Error(f"{name} must hold bf16 values or their 16-bit patterns")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise Fp4Error(f"{name} must be 2-D with unit column stride")
+    return x
+
+
+def _out(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dev(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise Fp4Error(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    return t
+
+
+def _p(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def fp4_quantize_rows(x, mode=FP4_RTN, seed=0, offset=0, codes=None, scales=None):
+    x = _bf16_2d(x, "x")
+    rows, cols = x.shape
+    codes = _out(codes, (rows, cols // 2), torch.uint8, x.device, "codes")
+    scales = _out(scales, (rows, cols // 32), torch.uint8, x.device, "scales")
+    _check(load().fp4_quantize_rows(_p(x), rows, cols, x.stride(0), _p(codes), _p(scales), int(mode),
+                                    int(seed), int(offset), _stream()))
+    return codes, scales
+
+
+def fp4_quantize_cols(x, hadamard=0, sign_mask16=0, codes_t=None, scales_t=None):
+    x = _bf16_2d(x, "x")
+    rows, cols = x.shape
+    codes_t = _out(codes_t, (cols, rows // 2), torch.uint8, x.device, "codes_t")
+    scales_t = _out(scales_t, (cols, rows // 32), torch.uint8, x.device, "scales_t")
+    _check(load().fp4_quantize_cols(_p(x), rows, cols, x.stride(0), _p(codes_t), _p(scales_t), int(hadamard),
+                                    int(sign_mask16), _stream()))
+    return codes_t, scales_t
+
+
+def fp4_quantize_w2d32(w, finer_ratio=0.87, row_codes=None, row_scales=None, col_codes=None, col_scales=None):
+    w = _bf16_2d(w, "w")
+    n, k = w.shape
+    row_codes = _out(row_codes, (n, k // 2), torch.uint8, w.device, "row_codes")
+    row_scales = _out(row_scales, (n, k // 32), torch.uint8, w.device, "row_scales")
+    col_codes = _out(col_codes, (k, n // 2), torch.uint8, w.device, "col_codes")
+    col_scales = _out(col_scales, (k, n // 32), torch.uint8, w.device, "col_scales")
+    _check(load().fp4_quantize_w2d32(_p(w), n, k, w.stride(0), _p(row_codes), _p(row_scales), _p(col_codes),
+                                     _p(col_scales), float(finer_ratio), _stream()))
+    return row_codes, row_scales, col_codes, col_scales
+
+
+def fp4_gemm(a_codes, a_scales, b_codes, b_scales, c=None, accumulate=False):
+    for t, nm in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
+        _dev(t, nm)
+        if t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 2:
+            raise Fp4Error(f"{nm} must be a contiguous 2-D uint8 tensor")
+    m, k2 = a_codes.shape
+    n = b_codes.shape[0]
+    k = 2 * k2
+    if b_codes.shape[1] != k2 or tuple(a_scales.shape) != (m, k // 32) or tuple(b_scales.shape) != (n, k // 32):
+        raise Fp4Error("operand shapes disagree")
+    if c is None:
+        if accumulate:
+            raise Fp4Error("accumulate needs an output tensor")
+        c = torch.empty((m, n), dtype=torch.float32, device=a_codes.device)
+    else:
+        _dev(c, "c")
+        if c.dtype != torch.float32 or c.dim() != 2 or c.stride(1) != 1 or tuple(c.shape) != (m, n):
+            raise Fp4Error("c must be fp32 [m][n] with unit column stride")
+    _check(load().fp4_gemm(m, n, k, _p(a_codes), _p(a_scales), _p(b_codes), _p(b_scales), _p(c), c.stride(0),
+                           1 if accumulate else 0, _stream()))
+    return c
+
+
+def fp4_swiglu_producer(x_codes, x_scales, w13_codes, w13_scales, sign_mask16=0, emit_cols=True,
+                        a=None, b=None, h_codes=None, h_scales=None, ht_codes=None, ht_scales=None):
+    t, d2 = x_codes.shape
+    d = 2 * d2
+    f = w13_codes.shape[0] // 2
+    dev = x_codes.device
+    a = _out(a, (t, f), torch.int16, dev, "a") if a is not None else torch.empty((t, f), dtype=torch.int16, device=dev)
+    b = _out(b, (t, f), torch.int16, dev, "b") if b is not None else torch.empty((t, f), dtype=torch.int16, device=dev)
+    h_codes = _out(h_codes, (t, f // 2), torch.uint8, dev, "h_codes")
+    h_scales = _out(h_scales, (t, f // 32), torch.uint8, dev, "h_scales")
+    if emit_cols:
+        ht_codes = _out(ht_codes, (f, t // 2), torch.uint8, dev, "ht_codes")
+        ht_scales = _out(ht_scales, (f, t // 32), torch.uint8, dev, "ht_scales")
+    else:
+        ht_codes = ht_scales = None
+    _check(load().fp4_swiglu_producer(t, f, d, _p(x_codes), _p(x_scales), _p(w13_codes), _p(w13_scales), _p(a),
+                                      _p(b), _p(h_codes), _p(h_scales), _p(ht_codes), _p(ht_scales),
+                                      int(sign_mask16), _stream()))
+    return a, b, h_codes, h_scales, ht_codes, ht_scales
+
+
+def fp4_swiglu_backward(dh, a, b, da=None, db=None):
+    _dev(dh, "dh")
+    t, f = a.shape
+    if dh.dtype != torch.float32 or dh.dim() != 2 or dh.stride(1) != 1 or tuple(dh.shape) != (t, f):
+        raise Fp4Error("dh must be fp32 [t][f] with unit column stride")
+    da = _out(da, (t, f), torch.int16, a.device, "da") if da is not None else torch.empty((t, f), dtype=torch.int16, device=a.device)
+    db = _out(db, (t, f), torch.int16, a.device, "db") if db is not None else torch.empty((t, f), dtype=torch.int16, device=a.device)
+    _check(load().fp4_swiglu_backward(t, f, _p(dh), dh.stride(0), _p(a), _p(b), _p(da), _p(db), _stream()))
+    return da, db
+
+
+def fp4_sign_mask_from_seed(seed):
+    return int(load().fp4_sign_mask_from_seed(int(seed)))

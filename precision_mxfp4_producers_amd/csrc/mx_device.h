@@ -1,0 +1,137 @@
+// Device helpers for the MXFP4 producers on gfx950: E8M0 upward exponent,
+// E2M1 round-to-nearest and stochastic rounding, Philox4x32-10, the SwiGLU
+// exponential, bf16 rounding and wave-level reductions.
+//
+// Method: "Format-Aware Fusion for Fast FP4 Pretraining", §2.2 (Eq. 1),
+// §2.2.1 (upward scales), §2.5 (Eq. 9 adjacent-bin SR), App. A.1 (seed plus
+// counter offset).  Philox4x32-10 follows Salmon et al., SC'11.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// ---------------------------------------------------------------- bf16 / fp32
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t b = __float_as_uint(x);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------- E8M0 scale
+// Upward exponent of a block maximum given as fp32 bits (finite, >= 0):
+// smallest e with amax <= 6 * 2^e, clamped below at -127.  For a normal
+// amax = 1.f * 2^E this is E - 2 + (f > 1.5); zero and subnormal maxima give
+// -127 through the clamp.  Finite bf16/fp32 maxima never exceed e = 126.
+__device__ __forceinline__ int upward_exp(uint32_t amax_bits) {
+  int E = (int)(amax_bits >> 23) - 127;
+  int e = E - 2 + ((amax_bits & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+  return e < -127 ? -127 : e;
+}
+
+// 2^-e as fp32 for e in [-127, 126] (exact, normal).
+__device__ __forceinline__ float inv_pow2(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// ---------------------------------------------------------------- E2M1 codes
+// Round-to-nearest-even E2M1 magnitude code of y >= 0 (exact comparisons with
+// the grid midpoints; ties go to the even code; y > 5 saturates to code 7).
+__device__ __forceinline__ uint32_t e2m1_rtn(float y) {
+  return (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
+         (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) +
+         (uint32_t)(y > 5.0f);
+}
+
+// Adjacent-bin SR code of y in [0, 6] with 32-bit draw u.  q- is the largest
+// grid value <= y; if y is off the grid it rounds up iff u < ceil(frac * 2^32),
+// frac = (y - q-)/(q+ - q-).  (y - q-) * 2^32/(q+ - q-) is exact in fp32 for a
+// normal y (y has at most 24 significant bits; every step is a power of two).
+// `nonzero` tells whether the unscaled input was non-zero: an input so small
+// that y underflowed to 0 still has 0 < frac * 2^32 < 1, i.e. threshold 1.
+__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u, bool nonzero) {
+  uint32_t lo = (uint32_t)(y >= 0.5f) + (uint32_t)(y >= 1.0f) + (uint32_t)(y >= 1.5f) +
+                (uint32_t)(y >= 2.0f) + (uint32_t)(y >= 3.0f) + (uint32_t)(y >= 4.0f) +
+                (uint32_t)(y >= 6.0f);
+  // q- and 2^32 / (q+ - q-) per lower code
+  float q = lo < 4 ? 0.5f * (float)lo : (lo == 4 ? 2.0f : (lo == 5 ? 3.0f : (lo == 6 ? 4.0f : 6.0f)));
+  float inv_step = lo < 4 ? 8589934592.0f : (lo < 6 ? 4294967296.0f : 2147483648.0f);
+  float fr = __fmul_rn(__fsub_rn(y, q), inv_step);       // exact, < 2^32 - 2^24
+  uint32_t thr = (uint32_t)ceilf(fr);
+  if (thr == 0u && lo == 0u && nonzero) thr = 1u;
+  if (lo == 7u) thr = 0u;                                  // y == 6: on the grid
+  return lo + (u < thr ? 1u : 0u);
+}
+
+// ---------------------------------------------------------------- Philox
+struct u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    uint32_t hi0 = __umulhi(M0, c.x), lo0 = M0 * c.x;
+    uint32_t hi1 = __umulhi(M1, c.z), lo1 = M1 * c.z;
+    u32x4 n;
+    n.x = hi1 ^ c.y ^ k0;
+    n.y = lo1;
+    n.z = hi0 ^ c.w ^ k1;
+    n.w = lo0;
+    c = n;
+    k0 += W0;
+    k1 += W1;
+  }
+  return c;
+}
+
+// Four SR words for elements 4*blk .. 4*blk+3 of a tensor.
+__device__ __forceinline__ u32x4 sr_words(uint64_t blk, uint64_t seed, uint64_t offset) {
+  u32x4 c{(uint32_t)blk, (uint32_t)(blk >> 32), (uint32_t)offset, (uint32_t)(offset >> 32)};
+  return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+// ---------------------------------------------------------------- exp
+// Cody-Waite exponential used by the SwiGLU producer and its backward; every
+// operation is one fp32 IEEE rounding (no contraction), matching the oracle.
+__device__ __forceinline__ float pow2_i(int n) { return __uint_as_float((uint32_t)(n + 127) << 23); }
+
+__device__ __forceinline__ float exp_spec(float x) {
+  const float LOG2E = 0x1.715476p+0f;                      // RN(1/ln 2)
+  const float LN2_HI = 0.693359375f;                       // 355/512
+  const float LN2_LO = -0x1.bd0106p-13f;                   // RN(ln 2 - 355/512)
+  if (x > 89.0f) return __builtin_inff();
+  if (x < -104.0f) return 0.0f;
+  float n = rintf(__fmul_rn(x, LOG2E));
+  float r = __fsub_rn(__fsub_rn(x, __fmul_rn(n, LN2_HI)), __fmul_rn(n, LN2_LO));
+  float p = 0x1.a01a02p-13f;                               // RN(1/7!)
+  p = __fadd_rn(__fmul_rn(p, r), 0x1.6c16c2p-10f);          // RN(1/6!)
+  p = __fadd_rn(__fmul_rn(p, r), 0x1.111112p-7f);           // RN(1/5!)
+  p = __fadd_rn(__fmul_rn(p, r), 0x1.555556p-5f);           // RN(1/4!)
+  p = __fadd_rn(__fmul_rn(p, r), 0x1.555556p-3f);           // RN(1/3!)
+  p = __fadd_rn(__fmul_rn(p, r), 0.5f);                    // 1/2!
+  p = __fadd_rn(__fmul_rn(p, r), 1.0f);                    // 1/1!
+  p = __fadd_rn(__fmul_rn(p, r), 1.0f);                    // 1/0!
+  int ni = (int)n;
+  int n1 = ni >> 1;                                        // floor(n/2)
+  int n2 = ni - n1;
+  return __fmul_rn(__fmul_rn(p, pow2_i(n1)), pow2_i(n2));
+}
+
+// sig = 1/(1+exp(-a)), s = a*sig
+__device__ __forceinline__ void sigmoid_silu(float a, float& sig, float& s) {
+  sig = __fdiv_rn(1.0f, __fadd_rn(1.0f, exp_spec(-a)));
+  s = __fmul_rn(a, sig);
+}
+
+// ---------------------------------------------------------------- reductions
+// max over groups of 4 / 32 consecutive lanes (unsigned, all lanes active)
+__device__ __forceinline__ uint32_t max_quad(uint32_t v) {
+  v = max(v, (uint32_t)__shfl_xor((int)v, 1));
+  v = max(v, (uint32_t)__shfl_xor((int)v, 2));
+  return v;
+}
+
+}  // namespace mx

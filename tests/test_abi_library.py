@@ -1,0 +1,73 @@
+"""The C-ABI library loads on the CPU and exports every symbol include/*.h
+declares (no compute calls: there is no GPU here)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "precision_mxfp4_producers_amd", "libmxfp4.so")
+
+
+def declared_functions():
+    names = set()
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*[A-Za-z_][\w\s\*]*?\b(fp4_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_hot_path_calls():
+    names = declared_functions()
+    for n in ("fp4_quantize_rows", "fp4_quantize_cols", "fp4_quantize_w2d32", "fp4_gemm",
+              "fp4_swiglu_producer", "fp4_swiglu_backward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    if not os.path.exists(LIB):
+        pytest.fail("libmxfp4.so is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_signatures_cover_the_header():
+    import precision_mxfp4_producers_amd as mx
+    assert set(mx.EXPORTS) == declared_functions()
+
+
+def test_host_only_calls():
+    import numpy as np
+    import precision_mxfp4_producers_amd as mx
+    from oracle import philox as P
+    lib = mx.load(LIB)
+    assert lib.fp4_abi_version() >> 16 == 1
+    # the library's host sign-mask helper agrees with the oracle's generator
+    for seed in (0, 1, 2 ** 40 + 7):
+        assert mx.fp4_sign_mask_from_seed(seed) == P.sign_mask_from_seed(seed)
+
+
+def test_argument_errors_are_reported_without_gpu_work():
+    import precision_mxfp4_producers_amd as mx
+    lib = mx.load(LIB)
+    v = ctypes.c_void_p
+    # null pointers -> FP4_EINVAL; bad shape -> FP4_ESHAPE; misalignment -> FP4_EALIGN
+    assert lib.fp4_quantize_rows(None, 32, 32, 32, None, None, 0, 0, 0, None) == 1
+    assert lib.fp4_quantize_rows(v(4096), 32, 33, 40, v(4096), v(4096), 0, 0, 0, None) == 2
+    assert lib.fp4_quantize_rows(v(4098), 32, 32, 32, v(4096), v(4096), 0, 0, 0, None) == 3
+    assert lib.fp4_quantize_rows(v(4096), 32, 32, 32, v(4096), v(4096), 7, 0, 0, None) == 1
+    assert lib.fp4_quantize_cols(v(4096), 48, 32, 32, v(4096), v(4096), 0, 0, None) == 2
+    assert lib.fp4_quantize_cols(v(4096), 32, 32, 32, v(4096), v(4096), 16, 0, None) == 1
+    assert lib.fp4_quantize_w2d32(v(4096), 32, 32, 16, v(4096), v(4096), v(4096), v(4096),
+                                  ctypes.c_float(0.87), None) == 2
+    assert lib.fp4_gemm(32, 32, 48, v(4096), v(4096), v(4096), v(4096), v(4096), 32, 0, None) == 2
+    assert lib.fp4_gemm(32, 32, 32, v(4096), v(4096), v(4096), v(4096), v(4096), 32, 2, None) == 1
+    assert lib.fp4_swiglu_producer(32, 32, 32, v(4096), v(4096), v(4096), v(4096), v(4096), v(4096),
+                                   v(4096), v(4096), v(4096), None, 0, None) == 1
+    assert lib.fp4_swiglu_backward(32, 32, v(4096), 16, v(4096), v(4096), v(4096), v(4096), None) == 2

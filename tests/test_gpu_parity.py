@@ -1,0 +1,249 @@
+"""GPU parity of every hot-path call against the oracle, at sizes the oracle
+finishes in seconds that still span several workgroup tiles plus a ragged tail.
+
+Bar: codes, scales, SR outputs, SwiGLU h/dA/dB bit-exact; GEMM outputs within
+|C - C_ref| <= 1e-5 * sum_k |a_k b_k| per element.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import formats as F
+from oracle import gemm as G
+from oracle import philox as P
+from oracle import quant as Q
+from oracle import swiglu as S
+
+pytestmark = pytest.mark.gpu
+
+
+def dev16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def host16(t):
+    return host(t).view(np.uint16)
+
+
+def assert_same(got, want, what):
+    got = host(got)
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got != want)
+        raise AssertionError(f"{what}: {len(bad)} mismatches, first at {bad[:5].tolist()}: "
+                             f"got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}")
+
+
+def check_gemm(c_gpu, a, b, c_prev=None, what="gemm"):
+    ref, e = G.gemm_ref(host(a[0]), host(a[1]), host(b[0]), host(b[1]))
+    ok = G.within_bound(host(c_gpu), ref, e, c_prev=c_prev)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} elements outside bound; first {i}: "
+                             f"got {host(c_gpu)[i]} ref {ref[i]} E {e[i]}")
+
+
+ROW_SHAPES = [(256, 512), (320, 544), (96, 4128), (32, 32)]
+
+
+@pytest.mark.parametrize("shape", ROW_SHAPES)
+def test_rows_rtn(gpu_lib, shape):
+    x = synthetic.tensor(shape, std=1.0, seed=11, outlier_rate=0.001, outlier_scale=20.0)
+    x[0, :32] = 0
+    x[-1, 3] = 0x8000
+    codes, scales = gpu_lib.fp4_quantize_rows(dev16(x))
+    want = Q.quantize_rows(x)
+    assert_same(codes, want[0], "codes")
+    assert_same(scales, want[1], "scales")
+
+
+@pytest.mark.parametrize("shape", ROW_SHAPES)
+@pytest.mark.parametrize("seed,offset", [(0, 0), (12345, 7), (2 ** 40 + 3, 2 ** 33 + 1)])
+def test_rows_sr(gpu_lib, shape, seed, offset):
+    dy = synthetic.tensor(shape, std=1e-3, seed=12, outlier_rate=0.01, outlier_scale=50.0)
+    codes, scales = gpu_lib.fp4_quantize_rows(dev16(dy), gpu_lib.FP4_SR, seed, offset)
+    want = Q.quantize_rows(dy, Q.SR, seed, offset)
+    assert_same(codes, want[0], "SR codes")
+    assert_same(scales, want[1], "SR scales")
+
+
+def test_rows_strided_input(gpu_lib):
+    full = synthetic.tensor((64, 640), std=1.0, seed=13)
+    xd = dev16(full)[:, 64:576]                          # ldx = 640, cols = 512
+    codes, scales = gpu_lib.fp4_quantize_rows(xd)
+    want = Q.quantize_rows(np.ascontiguousarray(full[:, 64:576]))
+    assert_same(codes, want[0], "codes")
+    assert_same(scales, want[1], "scales")
+
+
+def test_rows_extreme_values(gpu_lib):
+    # subnormals, huge values and tiny-next-to-huge blocks (SR threshold at 1)
+    rng = np.random.default_rng(3)
+    x = rng.integers(0, 0x7F80, size=(64, 256), dtype=np.uint16)
+    x |= (rng.integers(0, 2, size=x.shape, dtype=np.uint16) << 15)
+    x[5, :32] = np.arange(1, 33, dtype=np.uint16)       # bf16 subnormals
+    x[6, 0] = 0x7F7F                                    # largest finite
+    x[6, 1:32] = 0x0001
+    for mode in (Q.RTN, Q.SR):
+        codes, scales = gpu_lib.fp4_quantize_rows(dev16(x), mode, 99, 5)
+        want = Q.quantize_rows(x, mode, 99, 5)
+        assert_same(codes, want[0], f"codes mode {mode}")
+        assert_same(scales, want[1], f"scales mode {mode}")
+
+
+@pytest.mark.parametrize("shape", [(256, 512), (320, 544), (4128, 96), (32, 32)])
+@pytest.mark.parametrize("had", [0, 32])
+def test_cols(gpu_lib, shape, had):
+    x = synthetic.tensor(shape, std=1.0, seed=14, outlier_rate=0.01, outlier_scale=30.0)
+    mask = P.sign_mask_from_seed(0)
+    codes, scales = gpu_lib.fp4_quantize_cols(dev16(x), had, mask)
+    want = Q.quantize_cols(x, had, mask)
+    assert_same(codes, want[0], "col codes")
+    assert_same(scales, want[1], "col scales")
+
+
+@pytest.mark.parametrize("shape", [(512, 512), (352, 416), (32, 64), (4096, 160)])
+@pytest.mark.parametrize("ratio", [0.87, 0.0])
+def test_w2d32(gpu_lib, shape, ratio):
+    w = synthetic.tensor(shape, std=0.02, seed=15)
+    got = gpu_lib.fp4_quantize_w2d32(dev16(w), ratio)
+    want = Q.quantize_w2d32(w, ratio)
+    for g, wv, nm in zip(got, want, ("row_codes", "row_scales", "col_codes", "col_scales")):
+        assert_same(g, wv, nm)
+
+
+def test_w2d32_orientation_invariant_on_gpu(gpu_lib):
+    w = synthetic.tensor((384, 640), std=0.02, seed=16)
+    rc, rs, cc, cs = gpu_lib.fp4_quantize_w2d32(dev16(w), 0.87)
+    assert np.array_equal(F.decode(host(rc), host(rs)), F.decode(host(cc), host(cs)).T)
+
+
+@pytest.mark.parametrize("mnk", [(256, 512, 512), (288, 352, 544), (512, 256, 1024), (32, 32, 32), (96, 544, 288)])
+def test_gemm(gpu_lib, mnk):
+    m, n, k = mnk
+    x = synthetic.tensor((m, k), std=1.0, seed=17, outlier_rate=0.001, outlier_scale=20.0)
+    w = synthetic.tensor((n, k), std=0.02, seed=18)
+    a = gpu_lib.fp4_quantize_rows(dev16(x))
+    b = gpu_lib.fp4_quantize_rows(dev16(w))
+    c = gpu_lib.fp4_gemm(a[0], a[1], b[0], b[1])
+    check_gemm(c, a, b)
+    prev = host(c).copy()
+    c2 = gpu_lib.fp4_gemm(a[0], a[1], b[0], b[1], c=c, accumulate=True)
+    check_gemm(c2, a, b, c_prev=prev, what="accumulate")
+
+
+def test_gemm_layout_one_hot(gpu_lib):
+    # one non-zero product per output element pins the MFMA register layout
+    m, n, k = 64, 96, 256
+    ac = np.zeros((m, k // 2), dtype=np.uint8)
+    bc = np.zeros((n, k // 2), dtype=np.uint8)
+    for i in range(m):
+        kk = (7 * i) % k
+        ac[i, kk // 2] |= (2 if kk % 2 == 0 else 0x20)           # value 1.0
+    rng = np.random.default_rng(5)
+    bc[:] = rng.integers(0, 256, size=bc.shape, dtype=np.uint8)
+    as_ = np.full((m, k // 32), 127, dtype=np.uint8)
+    bs = rng.integers(120, 135, size=(n, k // 32), dtype=np.uint8)
+    t = [torch.from_numpy(v).cuda() for v in (ac, as_, bc, bs)]
+    c = gpu_lib.fp4_gemm(*t)
+    ref, _ = G.gemm_ref(ac, as_, bc, bs)
+    assert np.array_equal(host(c).astype(np.float64), ref)
+
+
+def test_linear_fprop_dgrad_wgrad(gpu_lib):
+    """Eq. 4-6 with the producers feeding the GEMMs: Fprop Q_r(X)Q_r(W)^T,
+    Dgrad Q_r(dY, SR)Q_c(W) with the 2D32 column layout, Wgrad Q_c(dY)^T Q_c(X)
+    with paired H32."""
+    T, D, N = 320, 288, 224
+    x = synthetic.tensor((T, D), std=1.0, seed=19)
+    w = synthetic.tensor((N, D), std=0.02, seed=20)
+    dy = synthetic.tensor((T, N), std=1e-3, seed=21)
+    mask = P.sign_mask_from_seed(0)
+    xr = gpu_lib.fp4_quantize_rows(dev16(x))
+    wq = gpu_lib.fp4_quantize_w2d32(dev16(w), 0.87)
+    dyr = gpu_lib.fp4_quantize_rows(dev16(dy), gpu_lib.FP4_SR, 0, 1)
+    dyc = gpu_lib.fp4_quantize_cols(dev16(dy), 32, mask)
+    xc = gpu_lib.fp4_quantize_cols(dev16(x), 32, mask)
+    check_gemm(gpu_lib.fp4_gemm(xr[0], xr[1], wq[0], wq[1]), xr, wq[:2], what="Fprop")
+    check_gemm(gpu_lib.fp4_gemm(dyr[0], dyr[1], wq[2], wq[3]), dyr, wq[2:], what="Dgrad")
+    check_gemm(gpu_lib.fp4_gemm(dyc[0], dyc[1], xc[0], xc[1]), dyc, xc, what="Wgrad")
+
+
+@pytest.mark.parametrize("tfd", [(256, 128, 512), (288, 160, 320), (512, 384, 256), (32, 32, 32)])
+@pytest.mark.parametrize("emit_cols", [True, False])
+def test_swiglu_producer(gpu_lib, tfd, emit_cols):
+    t, f, d = tfd
+    x = synthetic.tensor((t, d), std=1.0, seed=22)
+    w13 = synthetic.tensor((2 * f, d), std=0.02, seed=23)
+    mask = P.sign_mask_from_seed(0)
+    xr = gpu_lib.fp4_quantize_rows(dev16(x))
+    wq = gpu_lib.fp4_quantize_w2d32(dev16(w13), 0.87)
+    a, b, hc, hs, htc, hts = gpu_lib.fp4_swiglu_producer(xr[0], xr[1], wq[0], wq[1], mask, emit_cols)
+    # a, b: bf16 of an fp32 value within the GEMM bound of the reference
+    ref, e = G.gemm_ref(host(xr[0]), host(xr[1]), host(wq[0]), host(wq[1]))
+    tol = G.GEMM_REL_TOL * e
+    for got, lo_hi in ((host16(a), (ref[:, :f] - tol[:, :f], ref[:, :f] + tol[:, :f])),
+                       (host16(b), (ref[:, f:] - tol[:, f:], ref[:, f:] + tol[:, f:]))):
+        lo = F.bf16_bits_to_f64(S.f32_to_bf16_rne(lo_hi[0].astype(np.float32)))
+        hi = F.bf16_bits_to_f64(S.f32_to_bf16_rne(lo_hi[1].astype(np.float32)))
+        g = F.bf16_bits_to_f64(got)
+        assert np.all((g >= lo) & (g <= hi))
+    h = S.swiglu_h(host16(a), host16(b))
+    want_r = Q.quantize_rows(h)
+    assert_same(hc, want_r[0], "h row codes")
+    assert_same(hs, want_r[1], "h row scales")
+    if emit_cols:
+        want_c = Q.quantize_cols(h, 32, mask)
+        assert_same(htc, want_c[0], "h col codes")
+        assert_same(hts, want_c[1], "h col scales")
+
+
+@pytest.mark.parametrize("tf", [(64, 288), (256, 512), (32, 32)])
+def test_swiglu_backward(gpu_lib, tf):
+    t, f = tf
+    a = synthetic.tensor((t, f), std=1.3, seed=24)
+    b = synthetic.tensor((t, f), std=1.3, seed=25)
+    a[0, :8] = np.array([0x0000, 0x8000, 0x4300, 0xC300, 0x42C8, 0xC2C8, 0x7F7F, 0xFF7F], dtype=np.uint16)
+    rng = np.random.default_rng(26)
+    dh = (rng.standard_normal((t, f)) * 1e-3).astype(np.float32)
+    da, db = gpu_lib.fp4_swiglu_backward(torch.from_numpy(dh).cuda(), dev16(a), dev16(b))
+    want_da, want_db = S.swiglu_backward(dh, a, b)
+    assert np.array_equal(host16(da), want_da)
+    assert np.array_equal(host16(db), want_db)
+
+
+def test_run_twice_bitwise_deterministic(gpu_lib):
+    x = synthetic.tensor((512, 1024), std=1.0, seed=27)
+    w = synthetic.tensor((768, 1024), std=0.02, seed=28)
+    xd, wd = dev16(x), dev16(w)
+    outs = []
+    for _ in range(2):
+        xr = gpu_lib.fp4_quantize_rows(xd, gpu_lib.FP4_SR, 3, 4)
+        wq = gpu_lib.fp4_quantize_w2d32(wd)
+        outs.append([host(t) for t in xr + wq + (gpu_lib.fp4_gemm(xr[0], xr[1], wq[0], wq[1]),)])
+    for u, v in zip(*outs):
+        assert np.array_equal(u, v)
+
+
+def test_outputs_fully_written(gpu_lib):
+    # sentinel-filled outputs: every byte must be overwritten
+    x = synthetic.tensor((160, 352), std=1.0, seed=29)
+    codes = torch.full((160, 176), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((160, 11), 0xFF, dtype=torch.uint8, device="cuda")
+    gpu_lib.fp4_quantize_rows(dev16(x), codes=codes, scales=scales)
+    want = Q.quantize_rows(x)
+    assert_same(codes, want[0], "codes")
+    assert_same(scales, want[1], "scales")
+    ct = torch.full((352, 80), 0xAB, dtype=torch.uint8, device="cuda")
+    st = torch.full((352, 5), 0xFF, dtype=torch.uint8, device="cuda")
+    gpu_lib.fp4_quantize_cols(dev16(x), 32, 0x1234, codes_t=ct, scales_t=st)
+    want = Q.quantize_cols(x, 32, 0x1234)
+    assert_same(ct, want[0], "col codes")
+    assert_same(st, want[1], "col scales")
