@@ -1,5 +1,5 @@
 // Block-scaled E2M1 GEMM on the gfx950 scaled MFMA, and the fused SwiGLU
-// producer built on the same main loop.
+// producer built on the same main loops.
 //
 // "Format-Aware Fusion for Fast FP4 Pretraining":
 //   §2.3 (Eq. 4-6)  Fprop, Dgrad and Wgrad are all C = dec(A) dec(B)^T with
@@ -7,18 +7,30 @@
 //   §3.2            the gated FFN pairs W1 and W3 and emits the SiLU-gated
 //                   output directly as the FP4 input of W2.
 //
-// Main loop.  A 256-lane workgroup owns a 256x256 output tile and walks K in
-// steps of 256 values (128 code bytes + 8 scale bytes per row).  Each step is
-// staged global -> registers -> LDS (double-buffered, one barrier per step);
-// 16-byte chunks are XOR-swizzled so that the fragment reads of 16 consecutive
-// rows hit distinct banks.  Each wave computes a 128x128 sub-tile as 4x4
-// v_mfma_scale_f32_32x32x64_f8f6f4 tiles (both operands FP4, fp32 accumulate).
-// A lane of that instruction supplies 32 K-values of one row plus their E8M0
-// scale byte; lanes 0-31 and 32-63 supply two different 32-blocks.  Within a
-// K step, lane half h takes blocks 4h..4h+3 for the four sub-steps, so each
-// lane's four scale bytes are one aligned dword and the sub-step selects the
-// byte (op_sel).  Applying the same block assignment to A and B leaves the
-// sum over K unchanged.
+// A workgroup owns a 256x256 output tile (256 tokens x 128 FFN columns for
+// the SwiGLU producer, whose B tile holds the matching W1 and W3 rows) and
+// walks K in steps of 256 values: 128 code bytes + 8 scale bytes per row.
+// MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 with both operands FP4 (E2M1) and
+// E8M0 scales, fp32 accumulate.  A lane supplies 32 K-values of one row plus
+// their scale byte; lanes 0-31 and 32-63 supply two different 32-blocks.
+// Within a K step, lane half h takes blocks 4h..4h+3 for the four sub-steps,
+// so each lane's four scale bytes are one aligned dword and the sub-step
+// selects the byte (op_sel).  Applying the same block assignment to A and B
+// leaves the sum over K unchanged.  B enters the instruction as its first
+// operand and A as its second, so each 32x32 result is the transposed tile: a
+// lane holds one row of C and, per group of four registers, four consecutive
+// columns, which the epilogues write with 16- or 8-byte stores.
+//
+// Two main loops:
+//   generic  (any K multiple of 32): 4 waves of 128x128, global -> registers
+//            -> LDS with per-chunk predicates.
+//   fast     (K % 256 == 0): 8 waves of 128x64, two per SIMD so one wave's
+//            waits are covered by the other's MFMAs; raw buffer loads (rows
+//            beyond M/N read as zero), LDS writes and loads software-pipelined
+//            under the MFMAs, fragments read one sub-step ahead.
+// Both stage tiles through the same LDS layout family: 128-byte rows whose
+// 16-byte chunks are XOR-swizzled so that 16 consecutive rows read at one
+// logical chunk hit 16 distinct bank groups.
 #include <hip/hip_runtime.h>
 
 #include "abi_common.h"
@@ -32,10 +44,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256;
 constexpr int BKB = 128;                    // code bytes per row per K step (256 values)
-constexpr int kGemmThreads = 256;
+constexpr int kGemmThreads = 256;           // generic path
+constexpr int kFastThreads = 512;           // fast path
 constexpr int kStageBytes = BM * BKB + BN * BKB + BM * 8 + BN * 8;    // 69632
-constexpr int kHPitch = 272;
-static_assert(2 * kStageBytes == 139264, "LDS budget");                // bytes per row of the staged h tile (256 + 16)
+constexpr int kSmemBytes = 2 * kStageBytes;                            // 139264
+constexpr int kHPitch = 272;                // bytes per row of the staged h tile (256 + 16)
+static_assert(256 * kHPitch <= kSmemBytes, "h tile fits in the stage buffers");
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
@@ -165,7 +179,7 @@ __device__ __forceinline__ void compute_substep(const uint8_t* la, const uint8_t
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          widen(af[i]), widen(bf[j]), acc[i][j], 4, 4, S, (int)sa[i], S, (int)sb[j]);
+          widen(bf[j]), widen(af[i]), acc[i][j], 4, 4, S, (int)sb[j], S, (int)sa[i]);
     }
   }
 }
@@ -239,146 +253,135 @@ __device__ __forceinline__ void main_loop_generic(uint8_t* buf0, uint8_t* buf1, 
   }
 }
 
-// ------------------------------------------------------------------ DMA main loop
-// Fast path for K % 128 == 0.  Code and scale tiles move global -> LDS with
-// buffer_load ... lds: no staging registers; rows beyond M/N and chunks beyond
-// K get an out-of-range buffer offset and read as zero.  The DMA is issued
-// with inline asm so that the compiler's wait-count pass, which cannot tell
-// the two stage buffers apart, does not stall every LDS read behind it; the
-// single wait it needs (vmcnt(0) before each stage barrier) is explicit.
-//
-// LDS layout (stage-interleaved per operand so the stage is an immediate
-// offset of the fragment reads):
-//   A stage 0 | A stage 1 | B stage 0 | B stage 1 | SA 0 | SA 1 | SB 0 | SB 1
-//   32 KB each (256 rows x 128 B, 16-byte chunks swizzled), 2 KB per scale tile
-// Per K step each wave issues 8 + 8 16-byte code DMAs (1 KB blocks of 8 rows)
-// and 2 + 2 4-byte scale DMAs (256 B blocks of 32 rows x 2 dwords).  Fragments
-// are read from LDS one sub-step ahead of the MFMAs that use them; the DMA of
-// step it+2 is issued right after the barrier that ends step it and overlaps
-// a whole step of MFMA work.
+
+// ------------------------------------------------------------------ fast main loop
+// LDS layout, stage-major per operand (the stage is an immediate offset):
+//   A[2] 32 KB each (256 rows x 128 B) | B[2] | SA[2] 2 KB (256 rows x 8 B) | SB[2]
+// Step it+1 is loaded global -> VGPRs during step it-1 (raw buffer loads),
+// written to its stage during sub-steps 1-2 of step it, and the loads of step
+// it+2 go out right after those writes: each load has about one and a half
+// steps to land.  (Direct global->LDS transfers measured at half this path's
+// throughput on gfx950.)
 constexpr int kLdsA = 0, kLdsB = 2 * BM * BKB, kLdsSA = 4 * BM * BKB, kLdsSB = kLdsSA + 2 * BM * 8;
-constexpr int kLdsTotal = kLdsSB + 2 * BN * 8;          // 139264
-constexpr uint32_t kOOB = 0x80000000u;                  // beyond every num_records below
-constexpr int kDmaPerStage = 20;                        // DMA instructions per wave per K step
+static_assert(kLdsSB + 2 * BN * 8 == kSmemBytes, "fast path LDS layout");
 
 // s_waitcnt immediate (gfx9 encoding: vmcnt[3:0]+[15:14], expcnt[6:4], lgkmcnt[11:8])
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 14) | 0x70 | ((lgkm & 0xF) << 8); }
 
-// Raw buffer descriptor (stride 0, range-checked on the byte offset), uniform.
-__device__ __forceinline__ v4i buffer_rsrc(const void* base, int64_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF);
-  v4i r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32) & 0xFFFF);
-  r[2] = __builtin_amdgcn_readfirstlane((int)n);
-  r[3] = 0x00020000;
-  return r;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
-__device__ __forceinline__ void dma_b128(v4i rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-}
-__device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-}
-
-struct DmaPlan {
-  v4i ra, rb, rsa, rsb;          // this wave's descriptors (B: W1 or W3 half for the SwiGLU producer)
-  uint32_t va0, va1, vb0, vb1;   // lane code offsets for even / odd DMA j
-  uint32_t vsa, vsb;             // lane scale offsets
-  uint32_t ldb8, lds32;          // 8 code rows, 32 scale rows (bytes)
-  uint32_t lds_base;             // LDS address of the tile buffers
-  bool hi0, hi1;                 // lane's chunk (even / odd j) lies in the upper half of a K step
-  int w;                         // wave index (uniform)
+struct FastPlan {
+  __amdgpu_buffer_rsrc_t ra, rb, rs;   // A codes, this wave's B codes, this wave's scales
+  uint32_t va, vb;                     // lane code offsets of load j = 0 (j adds 8 rows)
+  uint32_t vs;                         // lane scale offset
+  uint32_t ldb8;                       // 8 code rows (bytes)
+  uint32_t wa0, wa1;                   // lane LDS offsets (even / odd j) of its code chunk
+  uint32_t ws;                         // lane LDS offset of its scale row (stage 0)
 };
 
+struct Staged8 {
+  v4i a[4], b[4];
+  uint2 s;
+};
+
+// Wave w loads code rows 32w..32w+31 of both tiles (load j: rows 32w + 8j +
+// l/8, chunk l&7; 8 lanes cover a 128-byte row) and the scale rows 64(w&3) +
+// l of A (waves 0-3) or B (waves 4-7).  For the SwiGLU producer, B tile rows
+// 0..127 are W1 rows n0.. and rows 128..255 are W3 rows f+n0..
 template <bool kSwiGLU>
-__device__ __forceinline__ void make_plan(DmaPlan& p, const uint8_t* smem, const Operand& A, const Operand& B,
-                                          int64_t m0, int64_t n0, int64_t f, int64_t K) {
+__device__ __forceinline__ void make_fast_plan(FastPlan& p, const Operand& A, const Operand& B, int64_t m0,
+                                               int64_t n0, int64_t f, int64_t K) {
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int l = threadIdx.x & 63;
   const int64_t ldb = K >> 1, lsc = K >> 5;
   const int64_t rows_a = min((int64_t)BM, A.rows - m0);
+  const int64_t rows_b = kSwiGLU ? min((int64_t)128, f - n0) : min((int64_t)BN, B.rows - n0);
   p.ra = buffer_rsrc(A.codes + m0 * ldb, rows_a * ldb);
-  p.rsa = buffer_rsrc(A.scales + m0 * lsc, rows_a * lsc);
-  int brow_shift = 0;                                    // B tile rows handled by this wave start here
+  int bshift = 0;
   if constexpr (kSwiGLU) {
-    const int64_t rows_b = min((int64_t)128, f - n0);
-    const int64_t g0 = (w >= 2 ? f : 0) + n0;            // W1 rows n0.. or W3 rows f+n0..
+    const int64_t g0 = (w >= 4 ? f : 0) + n0;
     p.rb = buffer_rsrc(B.codes + g0 * ldb, rows_b * ldb);
-    p.rsb = buffer_rsrc(B.scales + g0 * lsc, rows_b * lsc);
-    brow_shift = w >= 2 ? 128 : 0;
+    bshift = w >= 4 ? 128 : 0;
   } else {
-    const int64_t rows_b = min((int64_t)BN, B.rows - n0);
     p.rb = buffer_rsrc(B.codes + n0 * ldb, rows_b * ldb);
-    p.rsb = buffer_rsrc(B.scales + n0 * lsc, rows_b * lsc);
   }
-  // DMA j of wave w covers rows 8i..8i+7, i = 8w + j; lane l takes row 8i + l/8
-  // and LDS slot l&7, which holds logical chunk (l&7) ^ swizzle(row).
-  const int row0 = 64 * w + (l >> 3);
-  const int c0 = (l & 7) ^ (l >> 3);                     // j even (swizzle bit 3 of the row is 0)
-  const int c1 = c0 ^ 1;                                 // j odd
-  p.va0 = (uint32_t)(row0 * ldb + c0 * 16);
-  p.va1 = (uint32_t)(row0 * ldb + c1 * 16);
-  p.vb0 = (uint32_t)((row0 - brow_shift) * ldb + c0 * 16);
-  p.vb1 = (uint32_t)((row0 - brow_shift) * ldb + c1 * 16);
-  p.hi0 = c0 >= 4;
-  p.hi1 = c1 >= 4;
-  // scale DMA j of wave w covers rows 32i..32i+31 (i = 2w + j), lane l: row 32i + l/2, dword l&1
-  const int srow0 = 64 * w + (l >> 1);
-  p.vsa = (uint32_t)(srow0 * lsc + 4 * (l & 1));
-  p.vsb = (uint32_t)((srow0 - brow_shift) * lsc + 4 * (l & 1));
+  const int srow = 64 * (w & 3) + l;
+  if (w < 4) {
+    p.rs = buffer_rsrc(A.scales + m0 * lsc, rows_a * lsc);
+    p.vs = (uint32_t)(srow * lsc);
+    p.ws = (uint32_t)(kLdsSA + srow * 8);
+  } else {
+    int sshift = 0;
+    if constexpr (kSwiGLU) {
+      const int64_t g0 = (w >= 6 ? f : 0) + n0;
+      p.rs = buffer_rsrc(B.scales + g0 * lsc, rows_b * lsc);
+      sshift = w >= 6 ? 128 : 0;
+    } else {
+      p.rs = buffer_rsrc(B.scales + n0 * lsc, rows_b * lsc);
+    }
+    p.vs = (uint32_t)((srow - sshift) * lsc);
+    p.ws = (uint32_t)(kLdsSB + srow * 8);
+  }
+  const int row0 = 32 * w + (l >> 3), c = l & 7;
+  p.va = (uint32_t)(row0 * ldb + c * 16);
+  p.vb = (uint32_t)((row0 - bshift) * ldb + c * 16);
   p.ldb8 = (uint32_t)(8 * ldb);
-  p.lds32 = (uint32_t)(32 * lsc);
-  p.lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)smem;
-  p.w = w;
+  // LDS slot of the chunk: c ^ ((row & 7) ^ ((row >> 3) & 1)) with row & 7 = l/8
+  // and (row >> 3) & 1 = j & 1
+  p.wa0 = (uint32_t)(row0 * BKB + ((c ^ (l >> 3)) * 16));
+  p.wa1 = (uint32_t)(row0 * BKB + ((c ^ (l >> 3) ^ 1) * 16));
 }
 
-// `none` (uniform) turns every offset out of range: the DMA then only writes
-// zeros into a stage that is no longer read, which keeps the loop branch-free.
-__device__ __forceinline__ void dma_stage(const DmaPlan& p, int stg, int kit, bool half, bool none = false) {
+// Loads of K step `kit` into registers (the caller clamps kit to the last step,
+// which keeps the loop branch-free: a re-loaded last step is never read).
+__device__ __forceinline__ void load_step8(const FastPlan& p, int kit, Staged8& st) {
   const uint32_t so = (uint32_t)kit * BKB, sso = (uint32_t)kit * 8u;
-  const bool odd_lane = (threadIdx.x & 1) != 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = 8 * p.w + j;
-    uint32_t va = ((j & 1) ? p.va1 : p.va0) + (uint32_t)j * p.ldb8;
-    uint32_t vb = ((j & 1) ? p.vb1 : p.vb0) + (uint32_t)j * p.ldb8;
-    if (none || (half && ((j & 1) ? p.hi1 : p.hi0))) va = vb = kOOB;
-    dma_b128(p.ra, p.lds_base + kLdsA + stg * BM * BKB + i * 1024, va, so);
-    dma_b128(p.rb, p.lds_base + kLdsB + stg * BN * BKB + i * 1024, vb, so);
+  for (int j = 0; j < 4; ++j) {
+    st.a[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(p.ra, p.va + (uint32_t)j * p.ldb8, so, 0));
+    st.b[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(p.rb, p.vb + (uint32_t)j * p.ldb8, so, 0));
   }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = 2 * p.w + j;
-    uint32_t va = p.vsa + (uint32_t)j * p.lds32;
-    uint32_t vb = p.vsb + (uint32_t)j * p.lds32;
-    if (none || (half && odd_lane)) va = vb = kOOB;
-    dma_b32(p.rsa, p.lds_base + kLdsSA + stg * BM * 8 + i * 256, va, sso);
-    dma_b32(p.rsb, p.lds_base + kLdsSB + stg * BN * 8 + i * 256, vb, sso);
-  }
+  st.s = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(p.rs, p.vs, sso, 0));
 }
 
-struct Frags {
-  v4i a[4], b[4];
+// Write half H (loads 2H, 2H+1; H = 1 adds the scale row) into stage `stg`.
+template <int H>
+__device__ __forceinline__ void write_half8(uint8_t* smem, const FastPlan& p, uint32_t stg, const Staged8& st) {
+#pragma unroll
+  for (int j = 2 * H; j < 2 * H + 2; ++j) {
+    const uint32_t off = ((j & 1) ? p.wa1 : p.wa0) + (uint32_t)j * 1024u + stg * (BM * BKB);
+    *reinterpret_cast<v4i*>(smem + kLdsA + off) = st.a[j];
+    *reinterpret_cast<v4i*>(smem + kLdsB + off) = st.b[j];
+  }
+  if constexpr (H == 1) *reinterpret_cast<uint2*>(smem + p.ws + stg * (BM * 8)) = st.s;
+}
+
+struct Frags8 {
+  v4i a[4], b[2];
 };
 
-// Lane-constant LDS offsets of this wave's fragments for sub-step s (chunk
-// 4h + s of its row, swizzled) and of its scale dwords.
-struct FragAddr {
+// Lane-constant LDS offsets of this wave's fragments for sub-step s and of its
+// scale dwords (stage 0).  Wave (wm, wn) = (w / 4, w % 4) computes tokens
+// wm*128.. against B rows wn*64.. (GEMM: columns wn*64 .. +63) or against W1
+// rows wn*32.. and W3 rows 128 + wn*32.. (SwiGLU: a and b of FFN columns
+// wn*32 .. +31).
+struct FragAddr8 {
   uint32_t a[4], b[4];
   uint32_t sa, sb;
 };
 
 template <bool kSwiGLU>
-__device__ __forceinline__ void make_frag_addr(FragAddr& fa, int wm, int wn, int r, int h) {
-  const int g = (r & 7) ^ ((r >> 3) & 1);                // swizzle of rows r + 32k (same low 4 bits)
+__device__ __forceinline__ constexpr int bsub8(int j) { return kSwiGLU ? 128 * j : 32 * j; }
+
+template <bool kSwiGLU>
+__device__ __forceinline__ void make_frag_addr8(FragAddr8& fa, int wm, int wn, int r, int h) {
+  const int g = (r & 7) ^ ((r >> 3) & 1);               // swizzle of rows r + 32k
   const int x = (4 * h) ^ g;
   const int arow = wm * 128 + r;
-  const int brow = (kSwiGLU ? wn * 64 : wn * 128) + r;
+  const int brow = (kSwiGLU ? wn * 32 : wn * 64) + r;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     fa.a[s] = (uint32_t)(kLdsA + arow * BKB + ((x ^ s) * 16));
@@ -389,41 +392,36 @@ __device__ __forceinline__ void make_frag_addr(FragAddr& fa, int wm, int wn, int
 }
 
 template <bool kSwiGLU>
-__device__ __forceinline__ constexpr int b_sub_off(int j) {
-  // byte offset of B sub-tile j relative to the wave's first B row
-  return kSwiGLU ? ((j < 2) ? 32 * j * BKB : (128 + 32 * (j - 2)) * BKB) : 32 * j * BKB;
-}
-
-template <bool kSwiGLU>
-__device__ __forceinline__ void read_frags(const uint8_t* smem, const FragAddr& fa, Frags& fr, int s, uint32_t soff) {
-  const uint8_t* pa = smem + (fa.a[s] + soff);
-  const uint8_t* pb = smem + (fa.b[s] + soff);
+__device__ __forceinline__ void read_frags8(const uint8_t* smem, const FragAddr8& fa, Frags8& fr, int s,
+                                            uint32_t stg) {
+  const uint8_t* pa = smem + (fa.a[s] + stg * (BM * BKB));
+  const uint8_t* pb = smem + (fa.b[s] + stg * (BN * BKB));
 #pragma unroll
   for (int i = 0; i < 4; ++i) fr.a[i] = *reinterpret_cast<const v4i*>(pa + i * 32 * BKB);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fr.b[j] = *reinterpret_cast<const v4i*>(pb + b_sub_off<kSwiGLU>(j));
+  for (int j = 0; j < 2; ++j) fr.b[j] = *reinterpret_cast<const v4i*>(pb + bsub8<kSwiGLU>(j) * BKB);
 }
 
 template <bool kSwiGLU>
-__device__ __forceinline__ void read_scales(const uint8_t* smem, const FragAddr& fa, uint32_t (&sa)[4],
-                                            uint32_t (&sb)[4], uint32_t stg) {
+__device__ __forceinline__ void read_scales8(const uint8_t* smem, const FragAddr8& fa, uint32_t (&sa)[4],
+                                             uint32_t (&sb)[2], uint32_t stg) {
   const uint8_t* pa = smem + (fa.sa + stg * (BM * 8));
   const uint8_t* pb = smem + (fa.sb + stg * (BN * 8));
 #pragma unroll
   for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(pa + i * 32 * 8);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(pb + (b_sub_off<kSwiGLU>(j) / BKB) * 8);
+  for (int j = 0; j < 2; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(pb + bsub8<kSwiGLU>(j) * 8);
 }
 
 template <int S, int I0, int I1>
-__device__ __forceinline__ void mfma_rows(const Frags& fr, const uint32_t (&sa)[4], const uint32_t (&sb)[4],
-                                          v16f (&acc)[4][4]) {
+__device__ __forceinline__ void mfma8(const Frags8& fr, const uint32_t (&sa)[4], const uint32_t (&sb)[2],
+                                      v16f (&acc)[4][2]) {
 #pragma unroll
   for (int i = I0; i < I1; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(fr.a[i]), widen(fr.b[j]), acc[i][j], 4, 4, S,
-                                                                 (int)sa[i], S, (int)sb[j]);
+    for (int j = 0; j < 2; ++j) {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(fr.b[j]), widen(fr.a[i]), acc[i][j], 4, 4, S,
+                                                                 (int)sb[j], S, (int)sa[i]);
     }
   }
   // Pin the group here: MFMAs are pure, and without a consumer at this point
@@ -431,135 +429,130 @@ __device__ __forceinline__ void mfma_rows(const Frags& fr, const uint32_t (&sa)[
 #pragma unroll
   for (int i = I0; i < I1; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+    for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
-// Scheduling region: the 8 fragment reads of the next sub-step go out first,
-// then the 16 MFMAs of this one (which cover their latency).
-__device__ __forceinline__ void reads_then_mfma() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS read
-  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMA
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// One K step on stage `stg` (its sub-step 0 fragments and scales are already
-// in registers): prefetches sub-step 0 of the next step from the other stage
-// and issues the DMA of step it+2 into this stage once every wave is done with
-// it.  No branch encloses MFMA work, so the accumulators stay in AGPRs.
+// One K step on stage it&1 (its sub-step 0 fragments and scales already in
+// registers; `st` holds step it+1).
 template <bool kSwiGLU>
-__device__ __forceinline__ void dma_step(const uint8_t* smem, const DmaPlan& p, const FragAddr& fa, int it, int nk,
-                                         bool k_half, int stg, Frags& f0, Frags& f1, uint32_t (&sa)[4],
-                                         uint32_t (&sb)[4], v16f (&acc)[4][4]) {
-  const uint32_t cur = (uint32_t)stg * (BM * BKB), nxt = (uint32_t)(stg ^ 1) * (BM * BKB);
-  // sched_barrier(0) fences keep each sub-step's LDS reads ahead of the
-  // previous sub-step's MFMAs (the scheduler would otherwise hoist every read
-  // and sink every MFMA below the stage barrier).
-  read_frags<kSwiGLU>(smem, fa, f1, 1, cur);
-  mfma_rows<0, 0, 4>(f0, sa, sb, acc);
-  reads_then_mfma();
-  read_frags<kSwiGLU>(smem, fa, f0, 2, cur);
-  mfma_rows<1, 0, 4>(f1, sa, sb, acc);
-  reads_then_mfma();
-  read_frags<kSwiGLU>(smem, fa, f1, 3, cur);
-  mfma_rows<2, 0, 4>(f0, sa, sb, acc);
-  reads_then_mfma();
-  mfma_rows<3, 0, 2>(f1, sa, sb, acc);
+__device__ __forceinline__ void fast_step(uint8_t* smem, const FastPlan& p, const FragAddr8& fa, int it, int nk,
+                                          Staged8& st, Frags8& f0, Frags8& f1, uint32_t (&sa)[4], uint32_t (&sb)[2],
+                                          v16f (&acc)[4][2]) {
+  const uint32_t cur = (uint32_t)(it & 1), nxt = cur ^ 1u;
+  read_frags8<kSwiGLU>(smem, fa, f1, 1, cur);
+  mfma8<0, 0, 4>(f0, sa, sb, acc);
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);    // DS read
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);    // MFMA
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));       // own DMA of step it+1 landed, own reads done
+  read_frags8<kSwiGLU>(smem, fa, f0, 2, cur);
+  write_half8<0>(smem, p, nxt, st);
+  mfma8<1, 0, 4>(f1, sa, sb, acc);
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);    // DS write
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags8<kSwiGLU>(smem, fa, f1, 3, cur);
+  write_half8<1>(smem, p, nxt, st);
+  load_step8(p, min(it + 2, nk - 1), st);
+  mfma8<2, 0, 4>(f0, sa, sb, acc);
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  __builtin_amdgcn_sched_group_barrier(0x200, 5, 0);
+  __builtin_amdgcn_sched_group_barrier(0x020, 9, 0);    // VMEM read
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma8<3, 0, 2>(f1, sa, sb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  // every wave has written step it+1 and finished reading step it
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  uint32_t sa_n[4], sb_n[4];
-  read_frags<kSwiGLU>(smem, fa, f0, 0, nxt);             // harmless past the last step
-  read_scales<kSwiGLU>(smem, fa, sa_n, sb_n, (uint32_t)(stg ^ 1));
-  dma_stage(p, stg, it + 2, k_half && it + 2 == nk - 1, it + 2 >= nk);
-  __builtin_amdgcn_sched_barrier(0);
-  mfma_rows<3, 2, 4>(f1, sa, sb, acc);
+  uint32_t sa_n[4], sb_n[2];
+  read_frags8<kSwiGLU>(smem, fa, f0, 0, nxt);            // harmless past the last step
+  read_scales8<kSwiGLU>(smem, fa, sa_n, sb_n, nxt);
+  mfma8<3, 2, 4>(f1, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sa[i] = sa_n[i];
-    sb[i] = sb_n[i];
-  }
+  for (int i = 0; i < 4; ++i) sa[i] = sa_n[i];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sb[j] = sb_n[j];
 }
 
 template <bool kSwiGLU>
-__device__ __forceinline__ void main_loop_dma(uint8_t* smem, const Operand& A, const Operand& B, int64_t m0,
-                                              int64_t n0, int64_t f, int64_t K, v16f (&acc)[4][4], int wm, int wn) {
+__device__ __forceinline__ void main_loop_fast(uint8_t* smem, const Operand& A, const Operand& B, int64_t m0,
+                                               int64_t n0, int64_t f, int64_t K, v16f (&acc)[4][2], int wm, int wn) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
   const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
-  const int nk = (int)((K + 255) / 256);
-  const bool k_half = (K & 255) != 0;                    // the last step holds 128 values
-  DmaPlan p;
-  make_plan<kSwiGLU>(p, smem, A, B, m0, n0, f, K);
-  FragAddr fa;
-  make_frag_addr<kSwiGLU>(fa, wm, wn, r, h);
-  dma_stage(p, 0, 0, k_half && nk == 1);
-  if (nk > 1) {
-    dma_stage(p, 1, 1, k_half && nk == 2);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kDmaPerStage, 15));
-  } else {
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-  }
+  const int nk = (int)(K / 256);
+  FastPlan p;
+  make_fast_plan<kSwiGLU>(p, A, B, m0, n0, f, K);
+  FragAddr8 fa;
+  make_frag_addr8<kSwiGLU>(fa, wm, wn, r, h);
+  Staged8 st;
+  load_step8(p, 0, st);
+  write_half8<0>(smem, p, 0u, st);
+  write_half8<1>(smem, p, 0u, st);
+  load_step8(p, min(1, nk - 1), st);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   __builtin_amdgcn_s_barrier();
-  Frags f0, f1;
-  uint32_t sa[4], sb[4];
-  read_frags<kSwiGLU>(smem, fa, f0, 0, 0u);
-  read_scales<kSwiGLU>(smem, fa, sa, sb, 0u);
-  for (int it = 0; it < nk; ++it)
-    dma_step<kSwiGLU>(smem, p, fa, it, nk, k_half, it & 1, f0, f1, sa, sb, acc);
+  Frags8 f0, f1;
+  uint32_t sa[4], sb[2];
+  read_frags8<kSwiGLU>(smem, fa, f0, 0, 0u);
+  read_scales8<kSwiGLU>(smem, fa, sa, sb, 0u);
+  for (int it = 0; it < nk; ++it) fast_step<kSwiGLU>(smem, p, fa, it, nk, st, f0, f1, sa, sb, acc);
   __syncthreads();
 }
 
-// ------------------------------------------------------------------ GEMM
-template <bool kDMA>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
-    int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
-    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, float* __restrict__ c,
-    int64_t ldc, int accumulate) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
-  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int64_t tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  Operand A{a_codes, a_scales, M}, B{b_codes, b_scales, N};
-  v16f acc[4][4];
-  if constexpr (kDMA) main_loop_dma<false>(smem, A, B, m0, n0, 0, K, acc, wm, wn);
-  else main_loop_generic<false>(smem, smem + kStageBytes, A, B, m0, n0, 0, K, acc, wm, wn);
-
-  // 32x32 accumulator layout: lane holds column (lane & 31); register q holds
-  // row 8*(q/4) + 4*(lane/32) + (q%4).
-  const int hl = lane >> 5;
+// ------------------------------------------------------------------ epilogues
+// Result layout (operands entered as (B, A)): lane holds row (lane & 31) of A
+// sub-tile i; registers 4g..4g+3 hold columns 8g + 4*(lane/32) + 0..3 of B
+// sub-tile j.  `cols` is the tile-local first column of sub-tile j.
+__device__ __forceinline__ void store_c_row(float* crow, const v16f& acc, int hl, bool accumulate) {
+  float* p = crow + 4 * hl;
+  if (accumulate) {
+    float4 prev[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int g = 0; g < 4; ++g) prev[g] = *reinterpret_cast<const float4*>(p + 8 * g);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + 32 * j + (lane & 31);
-      if (col >= N) continue;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t row = m0 + wm * 128 + 32 * i + 8 * (q >> 2) + 4 * hl + (q & 3);
-        if (row < M) {
-          float* p = c + row * ldc + col;
-          *p = accumulate ? __fadd_rn(*p, acc[i][j][q]) : acc[i][j][q];
-        }
-      }
+    for (int g = 0; g < 4; ++g) {
+      float4 v;
+      v.x = __fadd_rn(prev[g].x, acc[4 * g]);
+      v.y = __fadd_rn(prev[g].y, acc[4 * g + 1]);
+      v.z = __fadd_rn(prev[g].z, acc[4 * g + 2]);
+      v.w = __fadd_rn(prev[g].w, acc[4 * g + 3]);
+      *reinterpret_cast<float4*>(p + 8 * g) = v;
     }
+  } else {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(p + 8 * g) = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
   }
 }
 
-// ------------------------------------------------------------------ SwiGLU producer
-// Output tile: 256 tokens x 128 FFN columns.  Wave (wm, wn) holds a and b for
-// tokens wm*128.. and columns wn*64.. in matching registers (sub-tiles j and
-// j+2), so h is formed in registers; a and b are saved as bf16 and h is staged
-// in LDS as bf16, then quantized row-facing (32 columns per block) and, if
-// requested, column-facing with H32 (32 tokens per block).
+// SwiGLU: from the fp32 a (acc_a) and b (acc_b) of one row segment of four
+// columns, save bf16 a and b and stage bf16 h = bf16(SiLU(a) * b) in LDS.
+__device__ __forceinline__ void swiglu_quad(const v16f& acc_a, const v16f& acc_b, int g, uint8_t* hdst, uint16_t* adst,
+                                            uint16_t* bdst, bool store) {
+  uint32_t ab[4], bb[4], hb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    ab[u] = f32_to_bf16_rne(acc_a[4 * g + u]);
+    bb[u] = f32_to_bf16_rne(acc_b[4 * g + u]);
+    float sig, sl;
+    sigmoid_silu(bf16_bits_to_f32(ab[u]), sig, sl);
+    hb[u] = f32_to_bf16_rne(__fmul_rn(sl, bf16_bits_to_f32(bb[u])));
+  }
+  *reinterpret_cast<uint2*>(hdst) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+  if (store) {
+    *reinterpret_cast<uint2*>(adst) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
+    *reinterpret_cast<uint2*>(bdst) = make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
+  }
+}
+
 __device__ __forceinline__ void h32_block(float (&f)[32]) {
 #pragma unroll
   for (int s = 1; s < 32; s <<= 1) {
@@ -594,110 +587,176 @@ __device__ __forceinline__ uint4 encode_block_rtn(const float (&f)[32], int& e_o
   return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
-template <bool kDMA>
-__global__ __launch_bounds__(kGemmThreads) void swiglu_producer_kernel(
+// Quantize the staged 256 x 128 bf16 h tile: row-facing RTN (1024 blocks of
+// 32 columns) and, if requested, column-facing with the fixed-sign H32 (128
+// columns x 8 token blocks).  NT threads share the blocks.
+template <int NT>
+__device__ __forceinline__ void quantize_h_tile(const uint8_t* smem, int64_t m0, int64_t n0, int64_t T, int64_t Fdim,
+                                                uint8_t* h_codes, uint8_t* h_scales, uint8_t* ht_codes,
+                                                uint8_t* ht_scales, uint32_t sign_mask16) {
+  const int tid = threadIdx.x;
+  for (int b = tid; b < 1024; b += NT) {
+    const int lr = b & 255, blk = b >> 8;
+    const int64_t row = m0 + lr, col0 = n0 + 32 * blk;
+    if (row >= T || col0 >= Fdim) continue;
+    float fv[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 d = *reinterpret_cast<const uint4*>(smem + lr * kHPitch + blk * 64 + q * 16);
+      const uint32_t w4[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        fv[8 * q + 2 * u] = bf16_bits_to_f32(w4[u] & 0xFFFFu);
+        fv[8 * q + 2 * u + 1] = bf16_bits_to_f32(w4[u] >> 16);
+      }
+    }
+    int e;
+    const uint4 code = encode_block_rtn(fv, e);
+    *reinterpret_cast<uint4*>(h_codes + row * (Fdim >> 1) + (col0 >> 1)) = code;
+    h_scales[row * (Fdim >> 5) + (col0 >> 5)] = (uint8_t)(e + 127);
+  }
+  if (ht_codes == nullptr) return;
+  for (int b = tid; b < 512; b += NT) {
+    const int cp = b & 63, tb = b >> 6;                  // columns 2cp, 2cp+1; tokens 32tb..
+    const int64_t r0 = m0 + 32 * tb;
+    if (r0 >= T) continue;
+    uint32_t v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = *reinterpret_cast<const uint32_t*>(smem + (32 * tb + i) * kHPitch + cp * 4);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int64_t col = n0 + 2 * cp + c;
+      if (col >= Fdim) continue;
+      float fv[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        uint32_t bits = (v[i] >> (16 * c)) & 0xFFFFu;
+        bits ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;
+        fv[i] = bf16_bits_to_f32(bits);
+      }
+      h32_block(fv);
+      int e;
+      const uint4 code = encode_block_rtn(fv, e);
+      *reinterpret_cast<uint4*>(ht_codes + col * (T >> 1) + (r0 >> 1)) = code;
+      ht_scales[col * (T >> 5) + (r0 >> 5)] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ kernels
+__global__ __launch_bounds__(kGemmThreads) void gemm_generic_kernel(
+    int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, float* __restrict__ c, int64_t ldc,
+    int accumulate) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  int64_t tm, tn;
+  tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1, hl = lane >> 5;
+  Operand A{a_codes, a_scales, M}, B{b_codes, b_scales, N};
+  v16f acc[4][4];
+  main_loop_generic<false>(smem, smem + kStageBytes, A, B, m0, n0, 0, K, acc, wm, wn);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = m0 + wm * 128 + 32 * i + (lane & 31);
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = n0 + wn * 128 + 32 * j;
+      if (col < N) store_c_row(c + row * ldc + col, acc[i][j], hl, accumulate != 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kFastThreads) void gemm_fast_kernel(
+    int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, float* __restrict__ c, int64_t ldc,
+    int accumulate) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  int64_t tm, tn;
+  tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 2, wn = wave & 3, hl = lane >> 5;
+  Operand A{a_codes, a_scales, M}, B{b_codes, b_scales, N};
+  v16f acc[4][2];
+  main_loop_fast<false>(smem, A, B, m0, n0, 0, K, acc, wm, wn);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = m0 + wm * 128 + 32 * i + (lane & 31);
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + wn * 64 + 32 * j;
+      if (col < N) store_c_row(c + row * ldc + col, acc[i][j], hl, accumulate != 0);
+    }
+  }
+}
+
+// SwiGLU producer output tile: 256 tokens x 128 FFN columns.
+__global__ __launch_bounds__(kGemmThreads) void swiglu_generic_kernel(
     int64_t T, int64_t Fdim, int64_t D, const uint8_t* __restrict__ x_codes, const uint8_t* __restrict__ x_scales,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, uint16_t* __restrict__ a_out,
     uint16_t* __restrict__ b_out, uint8_t* __restrict__ h_codes, uint8_t* __restrict__ h_scales,
     uint8_t* __restrict__ ht_codes, uint8_t* __restrict__ ht_scales, uint32_t sign_mask16) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];   // h tile staged here afterwards
-  const int64_t tiles_m = (T + BM - 1) / BM, tiles_n = (Fdim + 127) / 128;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   int64_t tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords((T + BM - 1) / BM, (Fdim + 127) / 128, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * 128;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1, hl = lane >> 5;
   Operand A{x_codes, x_scales, T}, B{w_codes, w_scales, 2 * Fdim};
   v16f acc[4][4];
-  if constexpr (kDMA) main_loop_dma<true>(smem, A, B, m0, n0, Fdim, D, acc, wm, wn);
-  else main_loop_generic<true>(smem, smem + kStageBytes, A, B, m0, n0, Fdim, D, acc, wm, wn);
-  // (main_loop ends with a barrier: LDS is free for the h tile)
-
-  const int hl = lane >> 5;
+  main_loop_generic<true>(smem, smem + kStageBytes, A, B, m0, n0, Fdim, D, acc, wm, wn);
+  // wave (wm, wn): a in sub-tiles j = 0, 1 and b in j + 2, FFN columns wn*64 + 32j ..
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const int lr = wm * 128 + 32 * i + (lane & 31);
+    const int64_t row = m0 + lr;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int lc = wn * 64 + 32 * j + (lane & 31);            // column within the 128-wide tile
-      const int64_t col = n0 + lc;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int lr = wm * 128 + 32 * i + 8 * (q >> 2) + 4 * hl + (q & 3);
-        const int64_t row = m0 + lr;
-        const uint32_t ab = f32_to_bf16_rne(acc[i][j][q]);
-        const uint32_t bb = f32_to_bf16_rne(acc[i][j + 2][q]);
-        float sig, s;
-        sigmoid_silu(bf16_bits_to_f32(ab), sig, s);
-        const uint32_t hb = f32_to_bf16_rne(__fmul_rn(s, bf16_bits_to_f32(bb)));
-        *reinterpret_cast<uint16_t*>(smem + lr * kHPitch + lc * 2) = (uint16_t)hb;
-        if (row < T && col < Fdim) {
-          a_out[row * Fdim + col] = (uint16_t)ab;
-          b_out[row * Fdim + col] = (uint16_t)bb;
-        }
+      for (int g = 0; g < 4; ++g) {
+        const int lc = wn * 64 + 32 * j + 8 * g + 4 * hl;
+        const int64_t col = n0 + lc;
+        swiglu_quad(acc[i][j], acc[i][j + 2], g, smem + lr * kHPitch + lc * 2, a_out + row * Fdim + col,
+                    b_out + row * Fdim + col, row < T && col < Fdim);
       }
+  }
+  __syncthreads();
+  quantize_h_tile<kGemmThreads>(smem, m0, n0, T, Fdim, h_codes, h_scales, ht_codes, ht_scales, sign_mask16);
+}
+
+__global__ __launch_bounds__(kFastThreads) void swiglu_fast_kernel(
+    int64_t T, int64_t Fdim, int64_t D, const uint8_t* __restrict__ x_codes, const uint8_t* __restrict__ x_scales,
+    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, uint16_t* __restrict__ a_out,
+    uint16_t* __restrict__ b_out, uint8_t* __restrict__ h_codes, uint8_t* __restrict__ h_scales,
+    uint8_t* __restrict__ ht_codes, uint8_t* __restrict__ ht_scales, uint32_t sign_mask16) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  int64_t tm, tn;
+  tile_coords((T + BM - 1) / BM, (Fdim + 127) / 128, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * 128;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 2, wn = wave & 3, hl = lane >> 5;
+  Operand A{x_codes, x_scales, T}, B{w_codes, w_scales, 2 * Fdim};
+  v16f acc[4][2];
+  main_loop_fast<true>(smem, A, B, m0, n0, Fdim, D, acc, wm, wn);
+  // wave (wm, wn): a in sub-tile 0 and b in sub-tile 1, FFN columns wn*32 ..
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lr = wm * 128 + 32 * i + (lane & 31);
+    const int64_t row = m0 + lr;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int lc = wn * 32 + 8 * g + 4 * hl;
+      const int64_t col = n0 + lc;
+      swiglu_quad(acc[i][0], acc[i][1], g, smem + lr * kHPitch + lc * 2, a_out + row * Fdim + col,
+                  b_out + row * Fdim + col, row < T && col < Fdim);
     }
   }
   __syncthreads();
-
-  // row-facing h: lane tid owns token row tid, four 32-column blocks
-  {
-    const int lr = tid;
-    const int64_t row = m0 + lr;
-    if (row < T) {
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        const int64_t col0 = n0 + 32 * blk;
-        if (col0 >= Fdim) break;
-        float fv[32];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 d = *reinterpret_cast<const uint4*>(smem + lr * kHPitch + blk * 64 + q * 16);
-          const uint32_t w4[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            fv[8 * q + 2 * u] = bf16_bits_to_f32(w4[u] & 0xFFFFu);
-            fv[8 * q + 2 * u + 1] = bf16_bits_to_f32(w4[u] >> 16);
-          }
-        }
-        int e;
-        const uint4 code = encode_block_rtn(fv, e);
-        *reinterpret_cast<uint4*>(h_codes + row * (Fdim >> 1) + (col0 >> 1)) = code;
-        h_scales[row * (Fdim >> 5) + (col0 >> 5)] = (uint8_t)(e + 127);
-      }
-    }
-  }
-
-  // column-facing h with H32: lane owns columns 2cp, 2cp+1 and token blocks 2g, 2g+1
-  if (ht_codes != nullptr) {
-    const int cp = tid & 63, g = tid >> 6;
-#pragma unroll
-    for (int tb2 = 0; tb2 < 2; ++tb2) {
-      const int tb = 2 * g + tb2;
-      const int64_t r0 = m0 + 32 * tb;
-      if (r0 >= T) continue;
-      uint32_t v[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i)
-        v[i] = *reinterpret_cast<const uint32_t*>(smem + (32 * tb + i) * kHPitch + cp * 4);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int64_t col = n0 + 2 * cp + c;
-        if (col >= Fdim) continue;
-        float fv[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          uint32_t b = (v[i] >> (16 * c)) & 0xFFFFu;
-          b ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;
-          fv[i] = bf16_bits_to_f32(b);
-        }
-        h32_block(fv);
-        int e;
-        const uint4 code = encode_block_rtn(fv, e);
-        *reinterpret_cast<uint4*>(ht_codes + col * (T >> 1) + (r0 >> 1)) = code;
-        ht_scales[col * (T >> 5) + (r0 >> 5)] = (uint8_t)(e + 127);
-      }
-    }
-  }
+  quantize_h_tile<kFastThreads>(smem, m0, n0, T, Fdim, h_codes, h_scales, ht_codes, ht_scales, sign_mask16);
 }
 
 }  // namespace mx
@@ -717,14 +776,14 @@ fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, con
     return FP4_EALIGN;
   const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   if (tiles > 0x7FFFFFFF) return FP4_ESHAPE;
-  // the DMA path needs K % 128 == 0 and byte offsets below 2^31
-  const bool dma = (k % 128) == 0 && m * (k / 2) < 0x7FFFFFFF && n * (k / 2) < 0x7FFFFFFF;
-  if (dma)
-    hipLaunchKernelGGL(gemm_kernel<true>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, as_stream(stream), m, n, k,
-                       a_codes, a_scales, b_codes, b_scales, c, ldc, accumulate);
+  hipStream_t s = as_stream(stream);
+  // the fast path needs K % 256 == 0 and buffer offsets below 2^31 per tile
+  if ((k % 256) == 0 && 256 * (k / 2) < 0x7FFFFFFF)
+    hipLaunchKernelGGL(gemm_fast_kernel, dim3((unsigned)tiles), dim3(kFastThreads), 0, s, m, n, k, a_codes, a_scales,
+                       b_codes, b_scales, c, ldc, accumulate);
   else
-    hipLaunchKernelGGL(gemm_kernel<false>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, as_stream(stream), m, n, k,
-                       a_codes, a_scales, b_codes, b_scales, c, ldc, accumulate);
+    hipLaunchKernelGGL(gemm_generic_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, m, n, k, a_codes,
+                       a_scales, b_codes, b_scales, c, ldc, accumulate);
   return launch_status();
 }
 
@@ -737,20 +796,19 @@ fp4_status fp4_swiglu_producer(int64_t t, int64_t f, int64_t d, const uint8_t* x
   if ((ht_codes == nullptr) != (ht_scales == nullptr)) return FP4_EINVAL;
   if (!mult32(t) || !mult32(f) || !mult32(d)) return FP4_ESHAPE;
   if (!aligned16(x_codes) || !aligned16(w13_codes) || !aligned16(h_codes) || !aligned16(x_scales) ||
-      !aligned16(w13_scales) ||
-      (ht_codes && !aligned16(ht_codes)))
+      !aligned16(w13_scales) || !aligned16(a_bf16) || !aligned16(b_bf16) || (ht_codes && !aligned16(ht_codes)))
     return FP4_EALIGN;
   const int64_t tiles = ((t + BM - 1) / BM) * ((f + 127) / 128);
   if (tiles > 0x7FFFFFFF) return FP4_ESHAPE;
-  const bool dma = (d % 128) == 0 && t * (d / 2) < 0x7FFFFFFF && 2 * f * (d / 2) < 0x7FFFFFFF;
-  if (dma)
-    hipLaunchKernelGGL(swiglu_producer_kernel<true>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, as_stream(stream),
-                       t, f, d, x_codes, x_scales, w13_codes, w13_scales, a_bf16, b_bf16, h_codes, h_scales, ht_codes,
-                       ht_scales, sign_mask16 & 0xFFFFu);
+  hipStream_t s = as_stream(stream);
+  if ((d % 256) == 0 && 256 * (d / 2) < 0x7FFFFFFF)
+    hipLaunchKernelGGL(swiglu_fast_kernel, dim3((unsigned)tiles), dim3(kFastThreads), 0, s, t, f, d, x_codes, x_scales,
+                       w13_codes, w13_scales, a_bf16, b_bf16, h_codes, h_scales, ht_codes, ht_scales,
+                       sign_mask16 & 0xFFFFu);
   else
-    hipLaunchKernelGGL(swiglu_producer_kernel<false>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, as_stream(stream),
-                       t, f, d, x_codes, x_scales, w13_codes, w13_scales, a_bf16, b_bf16, h_codes, h_scales, ht_codes,
-                       ht_scales, sign_mask16 & 0xFFFFu);
+    hipLaunchKernelGGL(swiglu_generic_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, t, f, d, x_codes,
+                       x_scales, w13_codes, w13_scales, a_bf16, b_bf16, h_codes, h_scales, ht_codes, ht_scales,
+                       sign_mask16 & 0xFFFFu);
   return launch_status();
 }
 
