@@ -570,21 +570,27 @@ __device__ __forceinline__ void h32_block(float (&f)[32]) {
   for (int j = 0; j < 32; ++j) f[j] = __fmul_rn(f[j], cn);
 }
 
+// RTN MXFP4 of one 32-value fp32 block: upward scale of its maximum, codes.
 __device__ __forceinline__ uint4 encode_block_rtn(const float (&f)[32], int& e_out) {
+  float am = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(f[j]));
+  const int e = upward_exp(__float_as_uint(am));
+  const float sc = pow2_scale(e);
+  e_out = e;
+  return make_uint4(rtn8_f32(f, sc), rtn8_f32(f + 8, sc), rtn8_f32(f + 16, sc), rtn8_f32(f + 24, sc));
+}
+
+// RTN MXFP4 of one 32-value bf16 block given as 16 packed words.
+__device__ __forceinline__ uint4 encode_block_bf16(const uint32_t (&w)[16], int& e_out) {
   uint32_t m = 0;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) m = max(m, __float_as_uint(f[j]) & 0x7FFFFFFFu);
-  const int e = upward_exp(m);
-  const float inv = inv_pow2(e);
-  uint32_t out[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t b = __float_as_uint(f[j]);
-    const float y = __uint_as_float(b & 0x7FFFFFFFu) * inv;
-    out[j >> 3] |= (e2m1_rtn(y) | ((b >> 28) & 8u)) << (4 * (j & 7));
-  }
+  for (int j = 0; j < 16; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+  const int e = upward_exp(m << 16);
+  const float sc = pow2_scale(e);
   e_out = e;
-  return make_uint4(out[0], out[1], out[2], out[3]);
+  return make_uint4(rtn8_bf16(w[0], w[1], w[2], w[3], sc), rtn8_bf16(w[4], w[5], w[6], w[7], sc),
+                    rtn8_bf16(w[8], w[9], w[10], w[11], sc), rtn8_bf16(w[12], w[13], w[14], w[15], sc));
 }
 
 // Quantize the staged 256 x 128 bf16 h tile: row-facing RTN (1024 blocks of
@@ -599,19 +605,14 @@ __device__ __forceinline__ void quantize_h_tile(const uint8_t* smem, int64_t m0,
     const int lr = b & 255, blk = b >> 8;
     const int64_t row = m0 + lr, col0 = n0 + 32 * blk;
     if (row >= T || col0 >= Fdim) continue;
-    float fv[32];
+    uint32_t wv[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint4 d = *reinterpret_cast<const uint4*>(smem + lr * kHPitch + blk * 64 + q * 16);
-      const uint32_t w4[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        fv[8 * q + 2 * u] = bf16_bits_to_f32(w4[u] & 0xFFFFu);
-        fv[8 * q + 2 * u + 1] = bf16_bits_to_f32(w4[u] >> 16);
-      }
+      wv[4 * q] = d.x; wv[4 * q + 1] = d.y; wv[4 * q + 2] = d.z; wv[4 * q + 3] = d.w;
     }
     int e;
-    const uint4 code = encode_block_rtn(fv, e);
+    const uint4 code = encode_block_bf16(wv, e);
     *reinterpret_cast<uint4*>(h_codes + row * (Fdim >> 1) + (col0 >> 1)) = code;
     h_scales[row * (Fdim >> 5) + (col0 >> 5)] = (uint8_t)(e + 127);
   }

@@ -37,31 +37,61 @@ __device__ __forceinline__ int upward_exp(uint32_t amax_bits) {
 __device__ __forceinline__ float inv_pow2(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
 
 // ---------------------------------------------------------------- E2M1 codes
-// Round-to-nearest-even E2M1 magnitude code of y >= 0 (exact comparisons with
-// the grid midpoints; ties go to the even code; y > 5 saturates to code 7).
-__device__ __forceinline__ uint32_t e2m1_rtn(float y) {
-  return (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
-         (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) +
-         (uint32_t)(y > 5.0f);
+// Round-to-nearest-even E2M1 uses the gfx950 converter
+// v_cvt_scalef32_pk_fp4_{bf16,f32}: two values divided by a power-of-two
+// scale, rounded to nearest even, saturated at 6, sign kept (so -0 and small
+// negatives give 0x8), packed low element first into the selected byte.  Its
+// results were checked against the rounding contract on every bf16 pattern at
+// every exponent in [-127, 126] and on 4M random fp32 inputs; the GPU parity
+// tests compare every producer with the CPU reference.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// 2^e as fp32 for e in [-127, 126] (2^-127 is the subnormal 0x00400000).
+__device__ __forceinline__ float pow2_scale(int e) {
+  return __uint_as_float(e > -127 ? (uint32_t)(e + 127) << 23 : 0x00400000u);
 }
 
-// Adjacent-bin SR code of y in [0, 6] with 32-bit draw u.  q- is the largest
-// grid value <= y; if y is off the grid it rounds up iff u < ceil(frac * 2^32),
-// frac = (y - q-)/(q+ - q-).  (y - q-) * 2^32/(q+ - q-) is exact in fp32 for a
-// normal y (y has at most 24 significant bits; every step is a power of two).
-// `nonzero` tells whether the unscaled input was non-zero: an input so small
-// that y underflowed to 0 still has 0 < frac * 2^32 < 1, i.e. threshold 1.
+// Eight bf16 values (four packed words, element 2j in the low half of word j)
+// -> eight RTN nibbles in one word (element k in bits 4k..4k+3).
+__device__ __forceinline__ uint32_t rtn8_bf16(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, float scale) {
+  uint32_t o = 0;
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, __builtin_bit_cast(bf16x2_t, w0), scale, 0);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, __builtin_bit_cast(bf16x2_t, w1), scale, 1);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, __builtin_bit_cast(bf16x2_t, w2), scale, 2);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, __builtin_bit_cast(bf16x2_t, w3), scale, 3);
+  return o;
+}
+
+// Eight fp32 values -> eight RTN nibbles in one word.
+__device__ __forceinline__ uint32_t rtn8_f32(const float* f, float scale) {
+  uint32_t o = 0;
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[0], f[1], scale, 0);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[2], f[3], scale, 1);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[4], f[5], scale, 2);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, f[6], f[7], scale, 3);
+  return o;
+}
+
+// Adjacent-bin SR code of y in [0, 6] with 32-bit draw u (software: the
+// hardware SR converter uses its random bits differently from the contract).
+// q- is the largest grid value <= y: code floor(2y) below 2, else
+// 2E + 2 + (first fraction bit) for y = 1.f * 2^E.  If y is off the grid it
+// rounds up iff u < ceil(frac * 2^32), frac = (y - q-)/(q+ - q-); the product
+// (y - q-) * 2^32/(q+ - q-) is exact in fp32 (y has at most 24 significant
+// bits, every step is a power of two).  `nonzero` tells whether the unscaled
+// input was non-zero: an input so small that y underflowed to 0 still has
+// 0 < frac * 2^32 < 1, i.e. threshold 1.  Branch-free.
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u, bool nonzero) {
-  uint32_t lo = (uint32_t)(y >= 0.5f) + (uint32_t)(y >= 1.0f) + (uint32_t)(y >= 1.5f) +
-                (uint32_t)(y >= 2.0f) + (uint32_t)(y >= 3.0f) + (uint32_t)(y >= 4.0f) +
-                (uint32_t)(y >= 6.0f);
-  // q- and 2^32 / (q+ - q-) per lower code
-  float q = lo < 4 ? 0.5f * (float)lo : (lo == 4 ? 2.0f : (lo == 5 ? 3.0f : (lo == 6 ? 4.0f : 6.0f)));
-  float inv_step = lo < 4 ? 8589934592.0f : (lo < 6 ? 4294967296.0f : 2147483648.0f);
-  float fr = __fmul_rn(__fsub_rn(y, q), inv_step);       // exact, < 2^32 - 2^24
+  const uint32_t yb = __float_as_uint(y);
+  const uint32_t lo_small = (uint32_t)(y * 2.0f);
+  const uint32_t lo_big = 2u * ((yb >> 23) - 127u) + 2u + ((yb >> 22) & 1u);
+  const uint32_t lo = y < 2.0f ? lo_small : lo_big;
+  const uint32_t q2 = (uint32_t)(0x0C08060403020100ull >> (8u * lo)) & 0xFFu;   // 2 * grid[lo]
+  const uint32_t sh = (0x02110000u >> (4u * lo)) & 0xFu;                         // log2(step) + 1
+  const float inv_step = __uint_as_float((127u + 33u - sh) << 23);               // 2^32 / step
+  const float fr = __fmul_rn(__fsub_rn(y, 0.5f * (float)q2), inv_step);
   uint32_t thr = (uint32_t)ceilf(fr);
-  if (thr == 0u && lo == 0u && nonzero) thr = 1u;
-  if (lo == 7u) thr = 0u;                                  // y == 6: on the grid
+  thr = max(thr, (nonzero && lo == 0u) ? 1u : 0u);
   return lo + (u < thr ? 1u : 0u);
 }
 
@@ -73,8 +103,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
   const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    uint32_t hi0 = __umulhi(M0, c.x), lo0 = M0 * c.x;
-    uint32_t hi1 = __umulhi(M1, c.z), lo1 = M1 * c.z;
+    const uint64_t p0 = (uint64_t)M0 * c.x, p1 = (uint64_t)M1 * c.z;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
     u32x4 n;
     n.x = hi1 ^ c.y ^ k0;
     n.y = lo1;
@@ -127,10 +158,10 @@ __device__ __forceinline__ void sigmoid_silu(float a, float& sig, float& s) {
 }
 
 // ---------------------------------------------------------------- reductions
-// max over groups of 4 / 32 consecutive lanes (unsigned, all lanes active)
+// max over each group of 4 consecutive lanes (DPP quad permutes; all lanes active)
 __device__ __forceinline__ uint32_t max_quad(uint32_t v) {
-  v = max(v, (uint32_t)__shfl_xor((int)v, 1));
-  v = max(v, (uint32_t)__shfl_xor((int)v, 2));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
   return v;
 }
 

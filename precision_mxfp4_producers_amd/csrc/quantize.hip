@@ -23,10 +23,22 @@ thread_local int g_last_hip_error = 0;
 constexpr int kThreads = 256;
 constexpr int kMaxGridY = 65535;
 
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// Largest 15-bit magnitude pattern among eight bf16 values (four words).
+__device__ __forceinline__ uint32_t bf16_absmax8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  const u16x2_t a = __builtin_bit_cast(u16x2_t, w0 & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2_t, w1 & 0x7FFF7FFFu);
+  const u16x2_t c = __builtin_bit_cast(u16x2_t, w2 & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2_t, w3 & 0x7FFF7FFFu);
+  const u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return max((uint32_t)m[0], (uint32_t)m[1]);
+}
+
 // ------------------------------------------------------------------ rows
 // One lane quantizes 8 consecutive values (one 16-byte load); four lanes share
-// a 32-value block and reduce its maximum over the quad.  bf16 magnitudes are
-// ordered like their 15-bit integer patterns, so the maximum is an integer max.
+// a 32-value block and reduce its maximum over the quad (DPP).  bf16
+// magnitudes are ordered like their 15-bit integer patterns, so the maximum
+// is an integer max.  RTN goes through the hardware converter; SR draws
+// Philox words for the lane's 8 elements (two counters).
 template <bool kSR>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
@@ -37,31 +49,26 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
   for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (col_ok) v = *reinterpret_cast<const uint4*>(x + r * ldx + c8 * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t m = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
-    m = max_quad(m);
+    const uint32_t m = max_quad(bf16_absmax8(v.x, v.y, v.z, v.w));
     const int e = upward_exp(m << 16);
-    const float inv = inv_pow2(e);
-    uint32_t u[8];
+    uint32_t packed;
     if constexpr (kSR) {
       const uint64_t idx0 = (uint64_t)r * (uint64_t)cols + (uint64_t)c8 * 8u;
       const u32x4 a = sr_words(idx0 >> 2, seed, offset);
       const u32x4 b = sr_words((idx0 >> 2) + 1u, seed, offset);
-      u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w;
-      u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
-    }
-    uint32_t packed = 0;
+      const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const float inv = inv_pow2(e);
+      packed = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t bits = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-      const uint32_t mag = bits & 0x7FFFu;
-      const float y = bf16_bits_to_f32(mag) * inv;       // exact (power-of-two scale)
-      uint32_t code;
-      if constexpr (kSR) code = e2m1_sr(y, u[i], mag != 0u);
-      else code = e2m1_rtn(y);
-      packed |= (code | ((bits >> 12) & 8u)) << (4 * i);
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t bits = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        const uint32_t mag = bits & 0x7FFFu;
+        const float y = bf16_bits_to_f32(mag) * inv;     // exact (power-of-two scale)
+        packed |= (e2m1_sr(y, u[i], mag != 0u) | ((bits >> 12) & 8u)) << (4 * i);
+      }
+    } else {
+      packed = rtn8_bf16(v.x, v.y, v.z, v.w, pow2_scale(e));
     }
     if (col_ok) {
       *reinterpret_cast<uint32_t*>(codes + r * (cols >> 1) + c8 * 4) = packed;
@@ -73,8 +80,9 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 // ------------------------------------------------------------------ cols
 // One lane owns two adjacent columns and one 32-row block: it reads 32 row
 // segments of 4 bytes (64 lanes cover 256 contiguous bytes per row), optionally
-// applies the fixed-sign H32 to each column in registers, and writes each
-// column's 16 code bytes to the transposed output.
+// applies the fixed-sign H32 to each column in registers (fp32, stage order
+// of the contract), and writes each column's 16 code bytes to the transposed
+// output.
 __device__ __forceinline__ void h32_inplace(float (&f)[32]) {
 #pragma unroll
   for (int s = 1; s < 32; s <<= 1) {
@@ -92,17 +100,15 @@ __device__ __forceinline__ void h32_inplace(float (&f)[32]) {
   for (int j = 0; j < 32; ++j) f[j] = __fmul_rn(f[j], c);
 }
 
-__device__ __forceinline__ uint4 encode32_rtn(const float (&f)[32], int e) {
-  const float inv = inv_pow2(e);
-  uint32_t out[4] = {0u, 0u, 0u, 0u};
+// RTN MXFP4 of one 32-value fp32 block: upward scale of its maximum, codes.
+__device__ __forceinline__ uint4 encode32_f32(const float (&f)[32], int& e_out) {
+  float am = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t b = __float_as_uint(f[j]);
-    const float y = __uint_as_float(b & 0x7FFFFFFFu) * inv;
-    const uint32_t nib = e2m1_rtn(y) | ((b >> 28) & 8u);
-    out[j >> 3] |= nib << (4 * (j & 7));
-  }
-  return make_uint4(out[0], out[1], out[2], out[3]);
+  for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(f[j]));
+  const int e = upward_exp(__float_as_uint(am));
+  const float sc = pow2_scale(e);
+  e_out = e;
+  return make_uint4(rtn8_f32(f, sc), rtn8_f32(f + 8, sc), rtn8_f32(f + 16, sc), rtn8_f32(f + 24, sc));
 }
 
 template <bool kH32>
@@ -128,12 +134,10 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
         f[i] = bf16_bits_to_f32(b);
       }
       if constexpr (kH32) h32_inplace(f);
-      uint32_t m = 0;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(f[i]) & 0x7FFFFFFFu);
-      const int e = upward_exp(m);
+      int e;
+      const uint4 code = encode32_f32(f, e);
       const int64_t col = 2 * p + c;
-      *reinterpret_cast<uint4*>(codes_t + col * (rows >> 1) + rb * 16) = encode32_rtn(f, e);
+      *reinterpret_cast<uint4*>(codes_t + col * (rows >> 1) + rb * 16) = code;
       scales_t[col * (rows >> 5) + rb] = (uint8_t)(e + 127);
     }
   }
@@ -172,10 +176,13 @@ __global__ __launch_bounds__(kThreads) void quant_w2d32_kernel(
     v[4 * q] = d.x; v[4 * q + 1] = d.y; v[4 * q + 2] = d.z; v[4 * q + 3] = d.w;
   }
   // tile maxima (bf16 magnitude patterns), reduced over the 32 rows of the wave
-  uint32_t m[2] = {0u, 0u};
+  uint32_t m[2];
 #pragma unroll
-  for (int i = 0; i < 32; ++i)
-    m[i >> 4] = max(m[i >> 4], max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+  for (int t = 0; t < 2; ++t)
+    m[t] = max(max(bf16_absmax8(v[16 * t], v[16 * t + 1], v[16 * t + 2], v[16 * t + 3]),
+                   bf16_absmax8(v[16 * t + 4], v[16 * t + 5], v[16 * t + 6], v[16 * t + 7])),
+               max(bf16_absmax8(v[16 * t + 8], v[16 * t + 9], v[16 * t + 10], v[16 * t + 11]),
+                   bf16_absmax8(v[16 * t + 12], v[16 * t + 13], v[16 * t + 14], v[16 * t + 15])));
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -200,50 +207,44 @@ __global__ __launch_bounds__(kThreads) void quant_w2d32_kernel(
     *reinterpret_cast<uint4*>(&tile[r * kWPitch + half * 32 + q * 4]) =
         make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 
-  // row layout straight from registers
+  // row layout straight from registers (adjacent K values share a word)
   if (row_ok) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       if (!t_ok[t]) continue;
-      const float inv = inv_pow2(e[t]);
-      uint32_t out[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const uint32_t bits = (v[16 * t + (j >> 1)] >> (16 * (j & 1))) & 0xFFFFu;
-        const float y = bf16_bits_to_f32(bits & 0x7FFFu) * inv;
-        out[j >> 3] |= (e2m1_rtn(y) | ((bits >> 12) & 8u)) << (4 * (j & 7));
-      }
+      const float sc = pow2_scale(e[t]);
+      const uint32_t* q = v + 16 * t;
+      const uint4 out = make_uint4(rtn8_bf16(q[0], q[1], q[2], q[3], sc), rtn8_bf16(q[4], q[5], q[6], q[7], sc),
+                                   rtn8_bf16(q[8], q[9], q[10], q[11], sc), rtn8_bf16(q[12], q[13], q[14], q[15], sc));
       const int64_t kk = k0 + half * 64 + t * 32;
-      *reinterpret_cast<uint4*>(row_codes + (n0 + r) * (K >> 1) + (kk >> 1)) =
-          make_uint4(out[0], out[1], out[2], out[3]);
+      *reinterpret_cast<uint4*>(row_codes + (n0 + r) * (K >> 1) + (kk >> 1)) = out;
       row_scales[(n0 + r) * (K >> 5) + (kk >> 5)] = (uint8_t)(e[t] + 127);
     }
   }
   __syncthreads();
 
-  // column layout: wave q = tile-row, lane = column pair within the macro tile
+  // column layout: wave q = tile-row, lane = column pair within the macro tile;
+  // v_perm gathers (row 2j, row 2j+1) of one column into a bf16 pair
   {
     const int q = wave, pcol = lane;                     // columns 2*pcol, 2*pcol+1
     const int tc = pcol >> 4;
     if (n0 + 32 * q < N && k0 + 32 * tc < K) {
       const int et = tile_e[q][tc];
-      const float inv = inv_pow2(et);
-      uint32_t out[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+      const float sc = pow2_scale(et);
+      uint32_t d[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const uint32_t d = tile[(32 * q + i) * kWPitch + pcol];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint32_t bits = (d >> (16 * c)) & 0xFFFFu;
-          const float y = bf16_bits_to_f32(bits & 0x7FFFu) * inv;
-          out[c][i >> 3] |= (e2m1_rtn(y) | ((bits >> 12) & 8u)) << (4 * (i & 7));
-        }
-      }
+      for (int i = 0; i < 32; ++i) d[i] = tile[(32 * q + i) * kWPitch + pcol];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
+        const uint32_t sel = c ? 0x07060302u : 0x05040100u;
+        uint32_t pr[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) pr[j] = __builtin_amdgcn_perm(d[2 * j + 1], d[2 * j], sel);
+        const uint4 out = make_uint4(rtn8_bf16(pr[0], pr[1], pr[2], pr[3], sc), rtn8_bf16(pr[4], pr[5], pr[6], pr[7], sc),
+                                     rtn8_bf16(pr[8], pr[9], pr[10], pr[11], sc),
+                                     rtn8_bf16(pr[12], pr[13], pr[14], pr[15], sc));
         const int64_t kcol = k0 + 2 * pcol + c;
-        *reinterpret_cast<uint4*>(col_codes + kcol * (N >> 1) + ((n0 + 32 * q) >> 1)) =
-            make_uint4(out[c][0], out[c][1], out[c][2], out[c][3]);
+        *reinterpret_cast<uint4*>(col_codes + kcol * (N >> 1) + ((n0 + 32 * q) >> 1)) = out;
         col_scales[kcol * (N >> 5) + ((n0 >> 5) + q)] = (uint8_t)(et + 127);
       }
     }
