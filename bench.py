@@ -45,7 +45,51 @@ def parse():
     p.add_argument("--workload", default="ffn_step_8192x4096x14336")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain device copy of known size (for scaling HBM byte counters)")
     return p.parse_args()
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_fast_kernel_ffn_step_8192x4096x14336_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "precision_mxfp4_producers_amd", "csrc", "gemm.hip")
+
+
+def gemm_source_hash():
+    import hashlib
+    return hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per gemm_fast_kernel launch from the committed counter summary,
+    if it was taken on this workload with the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("gemm.hip sha256 (first 16 hex)") != gemm_source_hash() or fields.get("workload") != workload:
+        return None
+    try:
+        return float(fields["hbm bytes per launch (calibrated)"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain device copy of 1 GiB, three times: its FETCH_SIZE / WRITE_SIZE
+    counters calibrate the byte counters against a known transfer."""
+    import torch
+    n = 1 << 28                                            # 2^28 fp32 = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                      "launches": 3}), flush=True)
 
 
 class Step:
@@ -61,7 +105,7 @@ class Step:
         dev = torch.device("cuda:0")
         self.d = {k: torch.from_numpy(v.view(np.int16)).to(dev) for k, v in self.host.items()}
         self.o = {}
-        self.calls = []          # (label, kind, units, fn)
+        self.calls = []          # (label, kind, units, fn, algorithmic bytes of a GEMM)
         getattr(self, "_build_" + name.split("_")[0])()
 
     def e(self, shape, dtype):
@@ -77,14 +121,14 @@ class Step:
         mx, (R, C) = self.mx, x.shape
         out = (self.u8(R, C // 2), self.u8(R, C // 32))
         self.calls.append((label, "quant", R * C * B_SINGLE,
-                           lambda: mx.fp4_quantize_rows(x, mode, self.seed, offset, codes=out[0], scales=out[1])))
+                           lambda: mx.fp4_quantize_rows(x, mode, self.seed, offset, codes=out[0], scales=out[1]), 0))
         return out
 
     def q_cols(self, label, x):
         mx, (R, C) = self.mx, x.shape
         out = (self.u8(C, R // 2), self.u8(C, R // 32))
         self.calls.append((label, "quant", R * C * B_SINGLE,
-                           lambda: mx.fp4_quantize_cols(x, 32, self.mask, codes_t=out[0], scales_t=out[1])))
+                           lambda: mx.fp4_quantize_cols(x, 32, self.mask, codes_t=out[0], scales_t=out[1]), 0))
         return out
 
     def q_w(self, label, w, row_codes=None, row_scales=None):
@@ -93,7 +137,7 @@ class Step:
         rs = row_scales if row_scales is not None else self.u8(N, K // 32)
         out = (rc, rs, self.u8(K, N // 2), self.u8(K, N // 32))
         self.calls.append((label, "quant", N * K * B_2D32,
-                           lambda: mx.fp4_quantize_w2d32(w, 0.87, *out)))
+                           lambda: mx.fp4_quantize_w2d32(w, 0.87, *out), 0))
         return out
 
     def gemm(self, label, a, b, c=None, accumulate=False):
@@ -101,8 +145,9 @@ class Step:
         m, n, k = a[0].shape[0], b[0].shape[0], 2 * a[0].shape[1]
         if c is None:
             c = self.e((m, n), self.torch.float32)
+        alg_bytes = (m + n) * k * (0.5 + 1 / 32) + 4 * m * n * (2 if accumulate else 1)
         self.calls.append((label, "gemm", 2.0 * m * n * k,
-                           lambda: mx.fp4_gemm(a[0], a[1], b[0], b[1], c=c, accumulate=accumulate)))
+                           lambda: mx.fp4_gemm(a[0], a[1], b[0], b[1], c=c, accumulate=accumulate), alg_bytes))
         return c
 
     # -------------------------------------------------------------- workloads
@@ -138,7 +183,7 @@ class Step:
         hc = (self.u8(F, T // 2), self.u8(F, T // 32))
         self.calls.append(("swiglu_producer", "producer", 2.0 * T * 2 * F * D,
                            lambda: mx.fp4_swiglu_producer(xr[0], xr[1], w13_rc, w13_rs, self.mask, True,
-                                                          a, b, hr[0], hr[1], hc[0], hc[1])))
+                                                          a, b, hr[0], hr[1], hc[0], hc[1]), 0))
         self.gemm("W2 Fprop", hr, w2[:2])
         dyr = self.q_rows("rows(dY,SR)", dY, 1, 0)
         dyc = self.q_cols("cols(dY,H32)", dY)
@@ -146,7 +191,7 @@ class Step:
         self.gemm("W2 Wgrad", dyc, hc)
         da, db = self.e((T, F), torch.int16), self.e((T, F), torch.int16)
         self.calls.append(("swiglu_backward", "quant", T * F * B_SWIGLU_BWD,
-                           lambda: mx.fp4_swiglu_backward(dh, a, b, da, db)))
+                           lambda: mx.fp4_swiglu_backward(dh, a, b, da, db), 0))
         dar = self.q_rows("rows(dA,SR)", da, 1, 1)
         dbr = self.q_rows("rows(dB,SR)", db, 1, 2)
         dac = self.q_cols("cols(dA,H32)", da)
@@ -158,7 +203,7 @@ class Step:
         self.gemm("W3 Wgrad", dbc, xc)
 
     def run(self, events=None):
-        for i, (_, _, _, fn) in enumerate(self.calls):
+        for i, (_, _, _, fn, _) in enumerate(self.calls):
             if events is not None:
                 events[i][0].record()
             fn()
@@ -166,12 +211,12 @@ class Step:
                 events[i][1].record()
 
     def gemm_flops(self):
-        return sum(u for _, k, u, _ in self.calls if k in ("gemm", "producer"))
+        return sum(c[2] for c in self.calls if c[1] in ("gemm", "producer"))
 
 
 CPU_SAMPLE_SHAPES = {
     # reduced instances of each workload: same laws, fewer rows
-    "ffn": dict(T=64, F=1024),
+    "ffn": dict(T=128, F=4096),
     "attn": dict(T=64),
     "wgrad": dict(T=64),
     "fprop": dict(),
@@ -260,6 +305,9 @@ def main():
     import precision_mxfp4_producers_amd as mx
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
+    if args.copy_calibration:
+        copy_calibration()
+        return
     mx.load()
     torch.cuda.set_device(0)
     print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
@@ -284,7 +332,7 @@ def main():
     print(f"[bench] {args.steps} steps in {total_ms:.2f} ms", file=sys.stderr, flush=True)
 
     per = []
-    for i, (label, kind, units, _) in enumerate(step.calls):
+    for i, (label, kind, units, _, _) in enumerate(step.calls):
         ms = float(np.median([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
         entry = {"call": label, "ms": round(ms, 4)}
         if kind in ("gemm", "producer"):
@@ -300,6 +348,8 @@ def main():
     gemm_ms = sum(e["ms"] for e, c in zip(per, step.calls) if c[1] == "gemm")
     gemm_flops = sum(c[2] for c in step.calls if c[1] == "gemm")
     achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
+    n_gemm = sum(1 for c in step.calls if c[1] == "gemm")
+    gemm_alg_bytes = sum(c[4] for c in step.calls if c[1] == "gemm")
     q_bytes = sum(c[2] for c in step.calls if c[1] == "quant")
     q_ms = sum(e["ms"] for e, c in zip(per, step.calls) if c[1] == "quant")
     out = {
@@ -318,9 +368,11 @@ def main():
         "config": {"workload": args.workload, "gemm_tflop_per_step": round(flops / 1e12, 3),
                    "quantizer_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1) if q_ms > 0 else None,
                    "quantizer_frac_hbm_peak": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if q_ms > 0 else None},
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "mfma", "kernel": "gemm_fast_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MXFP4_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(args.workload),
+                     "algorithmic_bytes_per_launch": round(gemm_alg_bytes / max(1, n_gemm)),
+                     "launches_per_step": n_gemm},
         "breakdown": per,
     }
     if not args.no_cpu_baseline:
