@@ -3,7 +3,8 @@
 This module holds no arithmetic of the method: it draws float32 samples with
 numpy's PCG64 and rounds them to bf16 bit patterns.  Each workload has one
 SeedSequence; every tensor is drawn from its own spawned child stream in a fixed
-order, so a tensor's values do not depend on which other tensors are drawn.
+order, so a tensor's values do not depend on which other tensors are drawn, and
+each tensor is drawn in row chunks from further spawned streams.
 
 Workloads stand in for the Llama-3-8B training tensors of "Format-Aware Fusion
 for Fast FP4 Pretraining" (§4.1: hidden 4096, FFN 14336, 8192-token sequences),
@@ -11,6 +12,8 @@ whose data are not available.  "N(0, s)" reads s as the standard deviation.
 Outliers: a Bernoulli mask of the stated rate, drawn after the values from the
 same child stream, multiplies the selected entries by the stated factor.
 """
+
+import os
 
 import numpy as np
 
@@ -25,30 +28,48 @@ def bf16_bits(x):
     return ((b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
 
 
-def draw(rng, shape, law, std, outlier_rate=0.0, outlier_scale=1.0, chunk_rows=4096):
+CHUNK_ROWS = 512
+
+
+def _draw_chunk(ss, rows, C, law, std, outlier_rate, outlier_scale):
+    rng = np.random.Generator(np.random.PCG64(ss))
+    if law == "normal":
+        v = rng.standard_normal((rows, C), dtype=np.float32)
+    elif law == "student_t3":
+        v = (rng.standard_t(3.0, size=(rows, C)) / np.sqrt(3.0)).astype(np.float32)
+    else:
+        raise ValueError(law)
+    v *= np.float32(std)
+    if outlier_rate > 0.0:
+        v[rng.random((rows, C)) < outlier_rate] *= np.float32(outlier_scale)
+    return bf16_bits(v)
+
+
+def draw(ss, shape, law, std, outlier_rate=0.0, outlier_scale=1.0):
     """Draw a bf16 tensor [R][C] from `law` ('normal' or 'student_t3') with the
-    given standard deviation; optional Bernoulli outliers.  Drawn in row chunks
-    (same values as one draw: the generator consumes its stream sequentially)."""
+    given standard deviation and optional Bernoulli outliers.
+
+    The rows are cut into chunks of CHUNK_ROWS; chunk j draws from the j-th
+    child of `ss` (values first, then the outlier mask), so chunks are drawn in
+    parallel and any chunk can be regenerated alone."""
+    from concurrent.futures import ThreadPoolExecutor
     R, C = shape
     out = np.empty((R, C), dtype=np.uint16)
-    vals = np.empty((R, C), dtype=np.float32)
-    for r0 in range(0, R, chunk_rows):
-        r1 = min(R, r0 + chunk_rows)
-        if law == "normal":
-            v = rng.standard_normal((r1 - r0, C), dtype=np.float32)
-        elif law == "student_t3":
-            v = (rng.standard_t(3.0, size=(r1 - r0, C)) / np.sqrt(3.0)).astype(np.float32)
-        else:
-            raise ValueError(law)
-        vals[r0:r1] = v * np.float32(std)
-    if outlier_rate > 0.0:
-        for r0 in range(0, R, chunk_rows):
-            r1 = min(R, r0 + chunk_rows)
-            mask = rng.random((r1 - r0, C)) < outlier_rate
-            vals[r0:r1][mask] *= np.float32(outlier_scale)
-    for r0 in range(0, R, chunk_rows):
-        r1 = min(R, r0 + chunk_rows)
-        out[r0:r1] = bf16_bits(vals[r0:r1])
+    starts = list(range(0, R, CHUNK_ROWS))
+    children = ss.spawn(len(starts))
+
+    def one(j):
+        r0 = starts[j]
+        r1 = min(R, r0 + CHUNK_ROWS)
+        out[r0:r1] = _draw_chunk(children[j], r1 - r0, C, law, std, outlier_rate, outlier_scale)
+
+    workers = max(1, min(16, os.cpu_count() or 1, len(starts)))
+    if workers == 1:
+        for j in range(len(starts)):
+            one(j)
+    else:
+        with ThreadPoolExecutor(workers) as pool:
+            list(pool.map(one, range(len(starts))))
     return out
 
 
@@ -101,11 +122,10 @@ def workload(name, seed=None, shapes=None):
         R, C, law, std, rate, scale = spec["tensors"][nm]
         if shapes and nm in shapes:
             R, C = shapes[nm]
-        out[nm] = draw(np.random.Generator(np.random.PCG64(ss)), (R, C), law, std, rate, scale)
+        out[nm] = draw(ss, (R, C), law, std, rate, scale)
     return out
 
 
 def tensor(shape, law="normal", std=1.0, seed=0, outlier_rate=0.0, outlier_scale=1.0):
     """One standalone bf16 tensor (for tests of single calls)."""
-    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
-    return draw(rng, shape, law, std, outlier_rate, outlier_scale)
+    return draw(np.random.SeedSequence(seed), shape, law, std, outlier_rate, outlier_scale)
