@@ -268,11 +268,6 @@ static_assert(kLdsSB + 2 * BN * 8 == kSmemBytes, "fast path LDS layout");
 // s_waitcnt immediate (gfx9 encoding: vmcnt[3:0]+[15:14], expcnt[6:4], lgkmcnt[11:8])
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 14) | 0x70 | ((lgkm & 0xF) << 8); }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
-  const int64_t n = bytes < 0 ? 0 : (bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
-}
-
 struct FastPlan {
   __amdgpu_buffer_rsrc_t ra, rb, rs;   // A codes, this wave's B codes, this wave's scales
   uint32_t va, vb;                     // lane code offsets of load j = 0 (j adds 8 rows)
@@ -645,6 +640,55 @@ __device__ __forceinline__ void quantize_h_tile(const uint8_t* smem, int64_t m0,
 }
 
 // ------------------------------------------------------------------ kernels
+// Whole 256x256 C tile through LDS (free after the main loop), 128 rows per
+// pass: waves park their accumulators row-major, then each wave writes whole
+// 1 KB rows with 16-byte stores, so every store instruction covers complete
+// cache lines (a lane-per-row store pattern leaves 64 partly written lines per
+// instruction, which drains at about half the rate).
+constexpr int kCPitch = 260;                // floats per staged row (256 + 4: conflict-free rows)
+static_assert(128 * kCPitch * 4 <= kSmemBytes, "C staging fits in the stage buffers");
+
+__device__ __forceinline__ void store_c_tile_staged(uint8_t* smem, const v16f (&acc)[4][2], float* __restrict__ c,
+                                                    int64_t ldc, int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                                    int wave, int lane, int wm, int wn, int hl, bool accumulate) {
+  float* cs = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    // staged row s holds tile row (s/64)*128 + 64*pass + s%64
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int lrow = wm * 64 + ii * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float* dst = cs + lrow * kCPitch + wn * 64 + 32 * j + 4 * hl;
+        const v16f& a = acc[2 * pass + ii][j];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(dst + 8 * g) = make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+      }
+    }
+    __syncthreads();
+    const int64_t col = n0 + 4 * lane;
+#pragma unroll 4
+    for (int sr = wave; sr < 128; sr += 8) {
+      const int64_t row = m0 + (sr >> 6) * 128 + 64 * pass + (sr & 63);
+      if (row < M && col < N) {                          // N % 32 == 0: the float4 is all-in
+        float4 v = *reinterpret_cast<const float4*>(cs + sr * kCPitch + 4 * lane);
+        float* p = c + row * ldc + col;
+        if (accumulate) {
+          const float4 prev = *reinterpret_cast<const float4*>(p);
+          v.x = __fadd_rn(prev.x, v.x);
+          v.y = __fadd_rn(prev.y, v.y);
+          v.z = __fadd_rn(prev.z, v.z);
+          v.w = __fadd_rn(prev.w, v.w);
+        }
+        *reinterpret_cast<float4*>(p) = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 __global__ __launch_bounds__(kGemmThreads) void gemm_generic_kernel(
     int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, float* __restrict__ c, int64_t ldc,
@@ -683,16 +727,7 @@ __global__ __launch_bounds__(kFastThreads) void gemm_fast_kernel(
   Operand A{a_codes, a_scales, M}, B{b_codes, b_scales, N};
   v16f acc[4][2];
   main_loop_fast<false>(smem, A, B, m0, n0, 0, K, acc, wm, wn);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = m0 + wm * 128 + 32 * i + (lane & 31);
-    if (row >= M) continue;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 64 + 32 * j;
-      if (col < N) store_c_row(c + row * ldc + col, acc[i][j], hl, accumulate != 0);
-    }
-  }
+  store_c_tile_staged(smem, acc, c, ldc, M, N, m0, n0, wave, lane, wm, wn, hl, accumulate != 0);
 }
 
 // SwiGLU producer output tile: 256 tokens x 128 FFN columns.

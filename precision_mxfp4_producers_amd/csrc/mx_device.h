@@ -74,24 +74,22 @@ __device__ __forceinline__ uint32_t rtn8_f32(const float* f, float scale) {
 
 // Adjacent-bin SR code of y in [0, 6] with 32-bit draw u (software: the
 // hardware SR converter uses its random bits differently from the contract).
-// q- is the largest grid value <= y: code floor(2y) below 2, else
-// 2E + 2 + (first fraction bit) for y = 1.f * 2^E.  If y is off the grid it
-// rounds up iff u < ceil(frac * 2^32), frac = (y - q-)/(q+ - q-); the product
-// (y - q-) * 2^32/(q+ - q-) is exact in fp32 (y has at most 24 significant
-// bits, every step is a power of two).  `nonzero` tells whether the unscaled
-// input was non-zero: an input so small that y underflowed to 0 still has
-// 0 < frac * 2^32 < 1, i.e. threshold 1.  Branch-free.
+// With q- the largest grid value <= y and q+ the next one, y rounds up iff
+// u < ceil(frac * 2^32), frac = (y - q-)/(q+ - q-).  Read off the fp32 bits
+// of y (biased exponent eb, fraction f):
+//   y >= 1       q- has code 2 + 2(eb-127) + f[22]; the step is 2^(eb-128),
+//                so frac * 2^32 = f[21:0] * 2^10 (an integer: yb << 10);
+//   0.5 <= y < 1 q- = 0.5 (code 1), step 0.5: frac * 2^32 = f * 2^9 (yb << 9);
+//   y < 0.5      q- = 0, step 0.5: frac * 2^32 = y * 2^33, rounded up; an
+//                input so small that y is zero or subnormal still has
+//                0 < frac * 2^32 < 1, threshold 1 (`nonzero`).
+// y <= 6 always (upward scale), so q+ exists.  Branch-free after if-conversion.
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u, bool nonzero) {
   const uint32_t yb = __float_as_uint(y);
-  const uint32_t lo_small = (uint32_t)(y * 2.0f);
-  const uint32_t lo_big = 2u * ((yb >> 23) - 127u) + 2u + ((yb >> 22) & 1u);
-  const uint32_t lo = y < 2.0f ? lo_small : lo_big;
-  const uint32_t q2 = (uint32_t)(0x0C08060403020100ull >> (8u * lo)) & 0xFFu;   // 2 * grid[lo]
-  const uint32_t sh = (0x02110000u >> (4u * lo)) & 0xFu;                         // log2(step) + 1
-  const float inv_step = __uint_as_float((127u + 33u - sh) << 23);               // 2^32 / step
-  const float fr = __fmul_rn(__fsub_rn(y, 0.5f * (float)q2), inv_step);
-  uint32_t thr = (uint32_t)ceilf(fr);
-  thr = max(thr, (nonzero && lo == 0u) ? 1u : 0u);
+  const uint32_t eb = yb >> 23;
+  const uint32_t t_small = max((uint32_t)ceilf(y * 0x1p33f), nonzero ? 1u : 0u);
+  const uint32_t lo = eb >= 127u ? (yb >> 22) - 252u : (eb == 126u ? 1u : 0u);
+  const uint32_t thr = eb >= 127u ? (yb << 10) : (eb == 126u ? (yb << 9) : t_small);
   return lo + (u < thr ? 1u : 0u);
 }
 
@@ -156,6 +154,17 @@ __device__ __forceinline__ void sigmoid_silu(float a, float& sig, float& s) {
   sig = __fdiv_rn(1.0f, __fadd_rn(1.0f, exp_spec(-a)));
   s = __fmul_rn(a, sig);
 }
+
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zero, so out-of-range lanes need no branch (a branch around a load
+// keeps the compiler from counting outstanding loads, and it then waits for
+// all of them).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+constexpr uint32_t kOffNone = 0x80000000u;               // beyond any resource: reads zero
 
 // ---------------------------------------------------------------- reductions
 // max over each group of 4 consecutive lanes (DPP quad permutes; all lanes active)

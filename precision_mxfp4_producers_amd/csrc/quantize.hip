@@ -13,6 +13,8 @@
 // codes plus one scale byte per 32 values.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "abi_common.h"
 #include "mx_device.h"
 
@@ -22,8 +24,10 @@ thread_local int g_last_hip_error = 0;
 
 constexpr int kThreads = 256;
 constexpr int kMaxGridY = 65535;
+constexpr int64_t kTargetBlocks = 2048;                  // 8 workgroups per CU
 
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 // Largest 15-bit magnitude pattern among eight bf16 values (four words).
 __device__ __forceinline__ uint32_t bf16_absmax8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
@@ -38,7 +42,34 @@ __device__ __forceinline__ uint32_t bf16_absmax8(uint32_t w0, uint32_t w1, uint3
 // a 32-value block and reduce its maximum over the quad (DPP).  bf16
 // magnitudes are ordered like their 15-bit integer patterns, so the maximum
 // is an integer max.  RTN goes through the hardware converter; SR draws
-// Philox words for the lane's 8 elements (two counters).
+// Philox words for the lane's 8 elements (two counters).  Each pass of the
+// row loop issues the loads of kRowsPerPass rows before using any of them.
+constexpr int kRowsPerPass = 4;
+
+template <bool kSR>
+__device__ __forceinline__ uint32_t encode_row_chunk(uint4 v, int e, int64_t r, int64_t cols, int64_t c8,
+                                                     uint64_t seed, uint64_t offset) {
+  if constexpr (kSR) {
+    const uint64_t idx0 = (uint64_t)r * (uint64_t)cols + (uint64_t)c8 * 8u;
+    const u32x4 a = sr_words(idx0 >> 2, seed, offset);
+    const u32x4 b = sr_words((idx0 >> 2) + 1u, seed, offset);
+    const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const float inv = inv_pow2(e);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t bits = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const uint32_t mag = bits & 0x7FFFu;
+      const float y = bf16_bits_to_f32(mag) * inv;       // exact (power-of-two scale)
+      packed |= (e2m1_sr(y, u[i], mag != 0u) | ((bits >> 12) & 8u)) << (4 * i);
+    }
+    return packed;
+  } else {
+    return rtn8_bf16(v.x, v.y, v.z, v.w, pow2_scale(e));
+  }
+}
+
 template <bool kSR>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
@@ -46,33 +77,25 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
   const int64_t cpr = cols >> 3;                         // 8-value chunks per row
   const int64_t c8 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const bool col_ok = c8 < cpr;                          // quads are all-in or all-out
-  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (col_ok) v = *reinterpret_cast<const uint4*>(x + r * ldx + c8 * 8);
-    const uint32_t m = max_quad(bf16_absmax8(v.x, v.y, v.z, v.w));
-    const int e = upward_exp(m << 16);
-    uint32_t packed;
-    if constexpr (kSR) {
-      const uint64_t idx0 = (uint64_t)r * (uint64_t)cols + (uint64_t)c8 * 8u;
-      const u32x4 a = sr_words(idx0 >> 2, seed, offset);
-      const u32x4 b = sr_words((idx0 >> 2) + 1u, seed, offset);
-      const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      const float inv = inv_pow2(e);
-      packed = 0;
+  const int64_t rstep = gridDim.y;
+  for (int64_t r0 = blockIdx.y; r0 < rows; r0 += kRowsPerPass * rstep) {
+    uint4 v[kRowsPerPass];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t bits = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-        const uint32_t mag = bits & 0x7FFFu;
-        const float y = bf16_bits_to_f32(mag) * inv;     // exact (power-of-two scale)
-        packed |= (e2m1_sr(y, u[i], mag != 0u) | ((bits >> 12) & 8u)) << (4 * i);
-      }
-    } else {
-      packed = rtn8_bf16(v.x, v.y, v.z, v.w, pow2_scale(e));
+    for (int j = 0; j < kRowsPerPass; ++j) {
+      const int64_t r = r0 + j * rstep;
+      v[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (col_ok && r < rows) v[j] = *reinterpret_cast<const uint4*>(x + r * ldx + c8 * 8);
     }
-    if (col_ok) {
-      *reinterpret_cast<uint32_t*>(codes + r * (cols >> 1) + c8 * 4) = packed;
-      if ((c8 & 3) == 0) scales[r * (cols >> 5) + (c8 >> 2)] = (uint8_t)(e + 127);
+#pragma unroll
+    for (int j = 0; j < kRowsPerPass; ++j) {
+      const int64_t r = r0 + j * rstep;
+      const uint32_t m = max_quad(bf16_absmax8(v[j].x, v[j].y, v[j].z, v[j].w));
+      const int e = upward_exp(m << 16);
+      if (col_ok && r < rows) {
+        const uint32_t packed = encode_row_chunk<kSR>(v[j], e, r, cols, c8, seed, offset);
+        *reinterpret_cast<uint32_t*>(codes + r * (cols >> 1) + c8 * 4) = packed;
+        if ((c8 & 3) == 0) scales[r * (cols >> 5) + (c8 >> 2)] = (uint8_t)(e + 127);
+      }
     }
   }
 }
@@ -111,34 +134,90 @@ __device__ __forceinline__ uint4 encode32_f32(const float (&f)[32], int& e_out) 
   return make_uint4(rtn8_f32(f, sc), rtn8_f32(f + 8, sc), rtn8_f32(f + 16, sc), rtn8_f32(f + 24, sc));
 }
 
+// A workgroup owns kColTok tokens x kColW columns: it loads the bf16 tile
+// row-contiguously (each row segment 128 bytes) into LDS, encodes column pairs
+// from LDS (optional H32 per 32-token block), parks the codes in LDS and
+// writes every column's kColTok/2 code bytes -- one whole 128-byte line -- with
+// coalesced 16-byte stores (16-byte pieces of many lines per store
+// instruction, or pieces of one line from different workgroups, drain at a
+// fraction of the rate).
+constexpr int kColTok = 256, kColW = 64;
+constexpr int kColPitch = kColW * 2 + 4;                 // bytes per staged token row (+4: spread banks)
+constexpr int kColCodePitch = kColTok / 2 + 16;          // bytes per staged column of codes
+
 template <bool kH32>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, uint32_t sign_mask16) {
-  const int64_t pairs = cols >> 1;
-  const int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (p >= pairs) return;                                // no cross-lane work below
-  const int64_t nrb = rows >> 5;
-  for (int64_t rb = blockIdx.y; rb < nrb; rb += gridDim.y) {
-    uint32_t v[32];
-    const uint16_t* src = x + (rb * 32) * ldx + 2 * p;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kColTok * kColPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t ctile[kColW * kColCodePitch];
+  __shared__ uint8_t stile[kColW][kColTok / 32];
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * kColW, t0 = (int64_t)blockIdx.y * kColTok;
+  const int ntok = (int)min<int64_t>(kColTok, rows - t0);          // multiple of 32
+  const int ncol = (int)min<int64_t>(kColW, cols - c0);            // multiple of 32
+
+  // load: thread (row tid/8 + 32 j, 16-byte chunk tid%8); rows past the end are skipped
+  {
+    const int ch = tid & 7;
+    const bool col_ok = ch * 8 < ncol;
+    uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = *reinterpret_cast<const uint32_t*>(src + (int64_t)i * ldx);
+    for (int j = 0; j < 8; ++j) {
+      const int r = (tid >> 3) + 32 * j;
+      v[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (col_ok && r < ntok) v[j] = *reinterpret_cast<const uint4*>(x + (t0 + r) * ldx + c0 + ch * 8);
+    }
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float f[32];
+    for (int j = 0; j < 8; ++j) {
+      const int r = (tid >> 3) + 32 * j;
+      uint32_t* d = reinterpret_cast<uint32_t*>(tile + r * kColPitch + ch * 16);
+      d[0] = v[j].x; d[1] = v[j].y; d[2] = v[j].z; d[3] = v[j].w;
+    }
+  }
+  __syncthreads();
+
+  // encode: thread (column pair tid%32, token block tid/32)
+  {
+    const int cp = tid & 31, tb = tid >> 5;
+    if (2 * cp < ncol && 32 * tb < ntok) {
+      uint32_t v[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        uint32_t b = (v[i] >> (16 * c)) & 0xFFFFu;
-        if constexpr (kH32) b ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;   // d_(i mod 16)
-        f[i] = bf16_bits_to_f32(b);
+      for (int i = 0; i < 32; ++i) v[i] = *reinterpret_cast<const uint32_t*>(tile + (32 * tb + i) * kColPitch + cp * 4);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float f[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          uint32_t bb = (v[i] >> (16 * c)) & 0xFFFFu;
+          if constexpr (kH32) bb ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;   // d_(i mod 16)
+          f[i] = bf16_bits_to_f32(bb);
+        }
+        if constexpr (kH32) h32_inplace(f);
+        int e;
+        const uint4 code = encode32_f32(f, e);
+        *reinterpret_cast<uint4*>(ctile + (2 * cp + c) * kColCodePitch + tb * 16) = code;
+        stile[2 * cp + c][tb] = (uint8_t)(e + 127);
       }
-      if constexpr (kH32) h32_inplace(f);
-      int e;
-      const uint4 code = encode32_f32(f, e);
-      const int64_t col = 2 * p + c;
-      *reinterpret_cast<uint4*>(codes_t + col * (rows >> 1) + rb * 16) = code;
-      scales_t[col * (rows >> 5) + rb] = (uint8_t)(e + 127);
+    }
+  }
+  __syncthreads();
+
+  // store: 8 threads per column write its ntok/2 code bytes (one line when
+  // ntok == 256); then one thread per column writes its scale bytes
+  {
+    const int piece = tid & 7;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int col = (tid >> 3) + 32 * k;
+      if (col < ncol && piece * 32 < ntok) {
+        const uint4 d = *reinterpret_cast<const uint4*>(ctile + col * kColCodePitch + piece * 16);
+        *reinterpret_cast<uint4*>(codes_t + (c0 + col) * (rows >> 1) + (t0 >> 1) + piece * 16) = d;
+      }
+    }
+    if (tid < ncol) {
+      uint8_t* dst = scales_t + (c0 + tid) * (rows >> 5) + (t0 >> 5);
+      for (int tb = 0; tb < ntok / 32; ++tb) dst[tb] = stile[tid][tb];
     }
   }
 }
@@ -153,28 +232,34 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 // value and exponent, so both layouts hold the same nibble).
 constexpr int kWPitch = 68;                              // dwords per LDS row (64 + 4 pad)
 
-__global__ __launch_bounds__(kThreads) void quant_w2d32_kernel(
-    const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ldw,
-    uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
-    uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales, float finer_ratio) {
-  __shared__ uint32_t tile[128 * kWPitch];
-  __shared__ int tile_e[4][4];
+// Loads of lane (r, half) for macro tile (n0, k0): 64 values of row n0 + r,
+// through the strip's buffer resource (rows >= N and columns >= K read zero).
+__device__ __forceinline__ void w2d32_load(__amdgpu_buffer_rsrc_t rs, int64_t N, int64_t K, int64_t ldw,
+                                           int64_t n0, int64_t k0, uint32_t (&v)[32]) {
+  const int tid = threadIdx.x, r = tid >> 1, half = tid & 1;
+  const bool row_ok = n0 + r < N;
+  const uint32_t base = (uint32_t)(r * ldw + k0 + half * 64) * 2u;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const bool ok = row_ok && k0 + 32 * (2 * half + (q >> 2)) < K;
+    const v4i d = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? base + 16u * q : kOffNone, 0, 0));
+    v[4 * q] = d[0]; v[4 * q + 1] = d[1]; v[4 * q + 2] = d[2]; v[4 * q + 3] = d[3];
+  }
+}
+
+// Encode one macro tile whose values this lane holds in v: tile exponents,
+// row layout from registers, column layout through LDS.  Leaves LDS free for
+// the next tile (ends with a barrier).
+__device__ __forceinline__ void w2d32_tile(const uint32_t (&v)[32], int64_t N, int64_t K, int64_t n0, int64_t k0,
+                                           uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
+                                           uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales,
+                                           float finer_ratio, uint32_t* tile, int (*tile_e)[4]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t n0 = (int64_t)blockIdx.y * 128, k0 = (int64_t)blockIdx.x * 128;
   const int r = tid >> 1, half = tid & 1;
   const bool row_ok = n0 + 32 * wave < N;                // uniform per wave
   bool t_ok[2];
   t_ok[0] = k0 + 32 * (2 * half) < K;
   t_ok[1] = k0 + 32 * (2 * half + 1) < K;
-
-  uint32_t v[32];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    uint4 d = make_uint4(0u, 0u, 0u, 0u);
-    if (row_ok && t_ok[q >> 2])
-      d = *reinterpret_cast<const uint4*>(w + (n0 + r) * ldw + k0 + half * 64 + q * 8);
-    v[4 * q] = d.x; v[4 * q + 1] = d.y; v[4 * q + 2] = d.z; v[4 * q + 3] = d.w;
-  }
   // tile maxima (bf16 magnitude patterns), reduced over the 32 rows of the wave
   uint32_t m[2];
 #pragma unroll
@@ -249,6 +334,46 @@ __global__ __launch_bounds__(kThreads) void quant_w2d32_kernel(
       }
     }
   }
+  __syncthreads();
+}
+
+// A 256-lane workgroup owns 128-row strips of 128x128 weight macro tiles
+// (4x4 tiles of 32x32) and walks them along K with stride gridDim.x; the
+// loads of the next macro tile are in flight while the current one is
+// encoded.  Lane (r = tid/2, half = tid&1) holds 64 values of row r: two
+// tiles.  Wave w holds exactly tile-row w, so each tile maximum is a wave
+// reduction over the lanes with equal `half`.  Row codes are written from
+// registers; the bf16 tile is staged in LDS once and re-read by columns to
+// write the column layout with the same tile exponent (the encoding is a pure
+// function of value and exponent, so both layouts hold the same nibble).
+__global__ __launch_bounds__(kThreads) void quant_w2d32_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ldw,
+    uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
+    uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales, float finer_ratio) {
+  __shared__ uint32_t tile[128 * kWPitch];
+  __shared__ int tile_e[4][4];
+  const int64_t n0 = (int64_t)blockIdx.y * 128;
+  const int64_t gk = (K + 127) / 128;
+  int64_t kt = blockIdx.x;
+  if (kt >= gk) return;                                  // uniform over the workgroup
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w + n0 * ldw, (std::min<int64_t>(128, N - n0) - 1) * ldw * 2 + K * 2);
+  // ping-pong register buffers (a copy between them would wait for the loads)
+  uint32_t v0[32], v1[32];
+  w2d32_load(rs, N, K, ldw, n0, kt * 128, v0);
+  for (;;) {
+    // next macro tile of this strip; on the last pass the current one again
+    // (a cached re-read keeps the loads unconditional)
+    int64_t kn = kt + gridDim.x < gk ? kt + gridDim.x : kt;
+    w2d32_load(rs, N, K, ldw, n0, kn * 128, v1);
+    w2d32_tile(v0, N, K, n0, kt * 128, row_codes, row_scales, col_codes, col_scales, finer_ratio, tile, tile_e);
+    kt += gridDim.x;
+    if (kt >= gk) break;
+    kn = kt + gridDim.x < gk ? kt + gridDim.x : kt;
+    w2d32_load(rs, N, K, ldw, n0, kn * 128, v0);
+    w2d32_tile(v1, N, K, n0, kt * 128, row_codes, row_scales, col_codes, col_scales, finer_ratio, tile, tile_e);
+    kt += gridDim.x;
+    if (kt >= gk) break;
+  }
 }
 
 }  // namespace mx
@@ -264,7 +389,12 @@ fp4_status fp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
   if (rows <= 0 || !mult32(cols) || ldx < cols) return FP4_ESHAPE;
   if (!aligned16(x) || !aligned16(codes) || (ldx % 8) != 0) return FP4_EALIGN;
   const int64_t cpr = cols >> 3;
-  dim3 grid((unsigned)((cpr + kThreads - 1) / kThreads), (unsigned)(rows < kMaxGridY ? rows : kMaxGridY));
+  const int64_t gx = (cpr + kThreads - 1) / kThreads;
+  // about kTargetBlocks workgroups, each taking whole passes of kRowsPerPass rows
+  int64_t gy = std::max<int64_t>(1, kTargetBlocks / gx);
+  gy = std::min<int64_t>(gy, (rows + kRowsPerPass - 1) / kRowsPerPass);
+  gy = std::min<int64_t>(gy, kMaxGridY);
+  dim3 grid((unsigned)gx, (unsigned)gy);
   hipStream_t s = as_stream(stream);
   if (mode == FP4_SR)
     hipLaunchKernelGGL(quant_rows_kernel<true>, grid, dim3(kThreads), 0, s, x, rows, cols, ldx, codes,
@@ -281,8 +411,9 @@ fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int6
   if (!x || !codes_t || !scales_t || (hadamard != 0 && hadamard != 32)) return FP4_EINVAL;
   if (!mult32(rows) || !mult32(cols) || ldx < cols) return FP4_ESHAPE;
   if (!aligned16(x) || !aligned16(codes_t) || (ldx % 8) != 0) return FP4_EALIGN;
-  const int64_t pairs = cols >> 1, nrb = rows >> 5;
-  dim3 grid((unsigned)((pairs + kThreads - 1) / kThreads), (unsigned)(nrb < kMaxGridY ? nrb : kMaxGridY));
+  const int64_t gx = (cols + kColW - 1) / kColW, gy = (rows + kColTok - 1) / kColTok;
+  if (gy > kMaxGridY) return FP4_ESHAPE;
+  dim3 grid((unsigned)gx, (unsigned)gy);
   hipStream_t s = as_stream(stream);
   if (hadamard == 32)
     hipLaunchKernelGGL(quant_cols_kernel<true>, grid, dim3(kThreads), 0, s, x, rows, cols, ldx, codes_t,
@@ -301,8 +432,11 @@ fp4_status fp4_quantize_w2d32(const uint16_t* w, int64_t n, int64_t k, int64_t l
   if (!mult32(n) || !mult32(k) || ldw < k) return FP4_ESHAPE;
   if (!aligned16(w) || !aligned16(row_codes) || !aligned16(col_codes) || (ldw % 8) != 0)
     return FP4_EALIGN;
-  const int64_t gx = (k + 127) / 128, gy = (n + 127) / 128;
-  if (gy > kMaxGridY) return FP4_ESHAPE;
+  const int64_t gk = (k + 127) / 128, gy = (n + 127) / 128;
+  if (gy > kMaxGridY || ldw >= ((int64_t)1 << 22)) return FP4_ESHAPE;   // 128-row strips stay < 2 GiB
+  // about kTargetBlocks / 2 workgroups (LDS allows 4 per CU), each walking
+  // several macro tiles along K
+  const int64_t gx = std::min<int64_t>(gk, std::max<int64_t>(1, (kTargetBlocks / 2) / gy));
   hipLaunchKernelGGL(quant_w2d32_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0,
                      as_stream(stream), w, n, k, ldw, row_codes, row_scales, col_codes, col_scales,
                      finer_ratio);
