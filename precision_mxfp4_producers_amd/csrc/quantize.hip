@@ -223,156 +223,136 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 }
 
 // ------------------------------------------------------------------ 2D32
-// A 256-lane workgroup owns a 128x128 weight macro tile (4x4 tiles of 32x32).
-// Lane (r = tid/2, half = tid&1) loads 64 values of row r: two tiles.  Wave w
-// holds exactly tile-row w, so each tile maximum is a wave reduction over the
-// lanes with equal `half`.  Row codes are written from registers; the bf16
-// tile is staged in LDS once and re-read by columns to write the column
-// layout with the same tile exponent (the encoding is a pure function of
-// value and exponent, so both layouts hold the same nibble).
-constexpr int kWPitch = 68;                              // dwords per LDS row (64 + 4 pad)
+// A 256-lane workgroup walks consecutive 128x128 weight macro tiles (4x4 tiles
+// of 32x32) along K; the loads of the next macro tile are in flight while the
+// current one is encoded.  Wave w holds tile-row w: lane l loads rows
+// 4q + l/16 (q = 0..7) of it, 8 values at column chunk l%16, so each load
+// covers four whole 256-byte row segments and each lane's values lie in
+// tile l%16/4.  A tile maximum is a reduction over the lane's rows, its quad
+// and lane bits 4-5.  Row codes go out from registers as 64-byte runs per row;
+// the bf16 tile is staged in LDS, re-read by columns with the same tile
+// exponent (the encoding is a pure function of value and exponent, so both
+// layouts hold the same nibble), and the column codes are staged again so
+// that four lanes write each column's 64 bytes together.
+constexpr int kWPitch = 68;                              // dwords per staged bf16 row (64 + 4 pad)
+constexpr int kWCodePitch = 80;                          // bytes per staged column of codes (64 + 16 pad)
 
-// Loads of lane (r, half) for macro tile (n0, k0): 64 values of row n0 + r,
-// through the strip's buffer resource (rows >= N and columns >= K read zero).
+// Loads of macro tile (n0, k0) through the strip's buffer resource (rows >= N
+// and columns >= K read zero).
 __device__ __forceinline__ void w2d32_load(__amdgpu_buffer_rsrc_t rs, int64_t N, int64_t K, int64_t ldw,
                                            int64_t n0, int64_t k0, uint32_t (&v)[32]) {
-  const int tid = threadIdx.x, r = tid >> 1, half = tid & 1;
-  const bool row_ok = n0 + r < N;
-  const uint32_t base = (uint32_t)(r * ldw + k0 + half * 64) * 2u;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int64_t col = k0 + (l & 15) * 8;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const bool ok = row_ok && k0 + 32 * (2 * half + (q >> 2)) < K;
-    const v4i d = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? base + 16u * q : kOffNone, 0, 0));
+    const int row = 32 * w + 4 * q + (l >> 4);
+    const bool ok = n0 + row < N && col < K;
+    const v4i d = __builtin_bit_cast(
+        v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? (uint32_t)(row * ldw + col) * 2u : kOffNone, 0, 0));
     v[4 * q] = d[0]; v[4 * q + 1] = d[1]; v[4 * q + 2] = d[2]; v[4 * q + 3] = d[3];
   }
 }
 
-// Encode one macro tile whose values this lane holds in v: tile exponents,
-// row layout from registers, column layout through LDS.  Leaves LDS free for
-// the next tile (ends with a barrier).
 __device__ __forceinline__ void w2d32_tile(const uint32_t (&v)[32], int64_t N, int64_t K, int64_t n0, int64_t k0,
                                            uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
                                            uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales,
-                                           float finer_ratio, uint32_t* tile, int (*tile_e)[4]) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r = tid >> 1, half = tid & 1;
-  const bool row_ok = n0 + 32 * wave < N;                // uniform per wave
-  bool t_ok[2];
-  t_ok[0] = k0 + 32 * (2 * half) < K;
-  t_ok[1] = k0 + 32 * (2 * half + 1) < K;
-  // tile maxima (bf16 magnitude patterns), reduced over the 32 rows of the wave
-  uint32_t m[2];
+                                           float finer_ratio, uint32_t* tile, uint8_t* ccodes, int (*tile_e)[4]) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int t = (l & 15) >> 2;                           // this lane's tile within the tile-row
+  const int64_t col = k0 + (l & 15) * 8;
+  const bool tile_ok = n0 + 32 * w < N && k0 + 32 * t < K;
+  // tile maximum (bf16 magnitude patterns): own 8 rows, quad, lane bits 4-5
+  uint32_t m = 0;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-    m[t] = max(max(bf16_absmax8(v[16 * t], v[16 * t + 1], v[16 * t + 2], v[16 * t + 3]),
-                   bf16_absmax8(v[16 * t + 4], v[16 * t + 5], v[16 * t + 6], v[16 * t + 7])),
-               max(bf16_absmax8(v[16 * t + 8], v[16 * t + 9], v[16 * t + 10], v[16 * t + 11]),
-                   bf16_absmax8(v[16 * t + 12], v[16 * t + 13], v[16 * t + 14], v[16 * t + 15])));
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-#pragma unroll
-    for (int s = 2; s < 64; s <<= 1) m[t] = max(m[t], (uint32_t)__shfl_xor((int)m[t], s));
-  }
-  int e[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const uint32_t ab = m[t] << 16;
-    const int e_up = upward_exp(ab);
-    const float lhs = __uint_as_float(ab) * inv_pow2(e_up);      // exact, in (3, 6]
-    const bool finer = ((double)lhs < 6.0 * (double)finer_ratio) && e_up > -127;
-    e[t] = finer ? e_up - 1 : e_up;
-  }
-  if (lane < 2) {                                        // lane 0: tiles 0,1; lane 1: tiles 2,3
-    tile_e[wave][2 * lane] = e[0];
-    tile_e[wave][2 * lane + 1] = e[1];
-  }
+  for (int q = 0; q < 8; ++q) m = max(m, bf16_absmax8(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]));
+  m = max_quad(m);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+  const uint32_t ab = m << 16;
+  const int e_up = upward_exp(ab);
+  const float lhs = __uint_as_float(ab) * inv_pow2(e_up);          // exact, in (3, 6]
+  const bool finer = ((double)lhs < 6.0 * (double)finer_ratio) && e_up > -127;
+  const int e = finer ? e_up - 1 : e_up;
+  if (l < 16 && (l & 3) == 0) tile_e[w][t] = e;
   // stage the bf16 values for the column pass
 #pragma unroll
   for (int q = 0; q < 8; ++q)
-    *reinterpret_cast<uint4*>(&tile[r * kWPitch + half * 32 + q * 4]) =
+    *reinterpret_cast<uint4*>(&tile[(32 * w + 4 * q + (l >> 4)) * kWPitch + (l & 15) * 4]) =
         make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-
-  // row layout straight from registers (adjacent K values share a word)
-  if (row_ok) {
+  // row layout from registers: 16 lanes write 64 contiguous bytes of a row
+  if (tile_ok) {
+    const float sc = pow2_scale(e);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (!t_ok[t]) continue;
-      const float sc = pow2_scale(e[t]);
-      const uint32_t* q = v + 16 * t;
-      const uint4 out = make_uint4(rtn8_bf16(q[0], q[1], q[2], q[3], sc), rtn8_bf16(q[4], q[5], q[6], q[7], sc),
-                                   rtn8_bf16(q[8], q[9], q[10], q[11], sc), rtn8_bf16(q[12], q[13], q[14], q[15], sc));
-      const int64_t kk = k0 + half * 64 + t * 32;
-      *reinterpret_cast<uint4*>(row_codes + (n0 + r) * (K >> 1) + (kk >> 1)) = out;
-      row_scales[(n0 + r) * (K >> 5) + (kk >> 5)] = (uint8_t)(e[t] + 127);
+    for (int q = 0; q < 8; ++q) {
+      const int64_t row = n0 + 32 * w + 4 * q + (l >> 4);
+      *reinterpret_cast<uint32_t*>(row_codes + row * (K >> 1) + (col >> 1)) =
+          rtn8_bf16(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], sc);
+      if ((l & 3) == 0) row_scales[row * (K >> 5) + (col >> 5)] = (uint8_t)(e + 127);
     }
   }
   __syncthreads();
 
-  // column layout: wave q = tile-row, lane = column pair within the macro tile;
-  // v_perm gathers (row 2j, row 2j+1) of one column into a bf16 pair
+  // column pass: wave q = tile-row, lane = column pair; codes staged per column
   {
-    const int q = wave, pcol = lane;                     // columns 2*pcol, 2*pcol+1
+    const int qr = w, pcol = l;                          // columns 2*pcol, 2*pcol+1
     const int tc = pcol >> 4;
-    if (n0 + 32 * q < N && k0 + 32 * tc < K) {
-      const int et = tile_e[q][tc];
-      const float sc = pow2_scale(et);
-      uint32_t d[32];
+    const int et = tile_e[qr][tc];
+    const float sc = pow2_scale(et);
+    uint32_t d[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) d[i] = tile[(32 * q + i) * kWPitch + pcol];
+    for (int i = 0; i < 32; ++i) d[i] = tile[(32 * qr + i) * kWPitch + pcol];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint32_t sel = c ? 0x07060302u : 0x05040100u;
-        uint32_t pr[16];
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t sel = c ? 0x07060302u : 0x05040100u;
+      uint32_t pr[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) pr[j] = __builtin_amdgcn_perm(d[2 * j + 1], d[2 * j], sel);
-        const uint4 out = make_uint4(rtn8_bf16(pr[0], pr[1], pr[2], pr[3], sc), rtn8_bf16(pr[4], pr[5], pr[6], pr[7], sc),
-                                     rtn8_bf16(pr[8], pr[9], pr[10], pr[11], sc),
-                                     rtn8_bf16(pr[12], pr[13], pr[14], pr[15], sc));
-        const int64_t kcol = k0 + 2 * pcol + c;
-        *reinterpret_cast<uint4*>(col_codes + kcol * (N >> 1) + ((n0 + 32 * q) >> 1)) = out;
-        col_scales[kcol * (N >> 5) + ((n0 >> 5) + q)] = (uint8_t)(et + 127);
-      }
+      for (int j = 0; j < 16; ++j) pr[j] = __builtin_amdgcn_perm(d[2 * j + 1], d[2 * j], sel);
+      *reinterpret_cast<uint4*>(ccodes + (2 * pcol + c) * kWCodePitch + qr * 16) =
+          make_uint4(rtn8_bf16(pr[0], pr[1], pr[2], pr[3], sc), rtn8_bf16(pr[4], pr[5], pr[6], pr[7], sc),
+                     rtn8_bf16(pr[8], pr[9], pr[10], pr[11], sc), rtn8_bf16(pr[12], pr[13], pr[14], pr[15], sc));
+    }
+  }
+  __syncthreads();
+  // column codes out: piece p = (column p/4, tile-row p%4), four lanes per column
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int p = tid + 256 * k, kc = p >> 2, qr = p & 3;
+    if (k0 + kc < K && n0 + 32 * qr < N) {
+      *reinterpret_cast<uint4*>(col_codes + (k0 + kc) * (N >> 1) + (n0 >> 1) + qr * 16) =
+          *reinterpret_cast<const uint4*>(ccodes + kc * kWCodePitch + qr * 16);
+      col_scales[(k0 + kc) * (N >> 5) + (n0 >> 5) + qr] = (uint8_t)(tile_e[qr][kc >> 5] + 127);
     }
   }
   __syncthreads();
 }
 
-// A 256-lane workgroup owns 128-row strips of 128x128 weight macro tiles
-// (4x4 tiles of 32x32) and walks them along K with stride gridDim.x; the
-// loads of the next macro tile are in flight while the current one is
-// encoded.  Lane (r = tid/2, half = tid&1) holds 64 values of row r: two
-// tiles.  Wave w holds exactly tile-row w, so each tile maximum is a wave
-// reduction over the lanes with equal `half`.  Row codes are written from
-// registers; the bf16 tile is staged in LDS once and re-read by columns to
-// write the column layout with the same tile exponent (the encoding is a pure
-// function of value and exponent, so both layouts hold the same nibble).
 __global__ __launch_bounds__(kThreads) void quant_w2d32_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ldw,
     uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
-    uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales, float finer_ratio) {
-  __shared__ uint32_t tile[128 * kWPitch];
+    uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales, float finer_ratio, int per) {
+  __shared__ __attribute__((aligned(16))) uint32_t tile[128 * kWPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t ccodes[128 * kWCodePitch];
   __shared__ int tile_e[4][4];
   const int64_t n0 = (int64_t)blockIdx.y * 128;
   const int64_t gk = (K + 127) / 128;
-  int64_t kt = blockIdx.x;
-  if (kt >= gk) return;                                  // uniform over the workgroup
+  int64_t kt = (int64_t)blockIdx.x * per;
+  const int64_t kt_end = min(gk, kt + per);
+  if (kt >= kt_end) return;                              // uniform over the workgroup
   const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w + n0 * ldw, (std::min<int64_t>(128, N - n0) - 1) * ldw * 2 + K * 2);
   // ping-pong register buffers (a copy between them would wait for the loads)
   uint32_t v0[32], v1[32];
   w2d32_load(rs, N, K, ldw, n0, kt * 128, v0);
   for (;;) {
-    // next macro tile of this strip; on the last pass the current one again
+    // next macro tile of this run; on the last pass the current one again
     // (a cached re-read keeps the loads unconditional)
-    int64_t kn = kt + gridDim.x < gk ? kt + gridDim.x : kt;
+    int64_t kn = kt + 1 < kt_end ? kt + 1 : kt;
     w2d32_load(rs, N, K, ldw, n0, kn * 128, v1);
-    w2d32_tile(v0, N, K, n0, kt * 128, row_codes, row_scales, col_codes, col_scales, finer_ratio, tile, tile_e);
-    kt += gridDim.x;
-    if (kt >= gk) break;
-    kn = kt + gridDim.x < gk ? kt + gridDim.x : kt;
+    w2d32_tile(v0, N, K, n0, kt * 128, row_codes, row_scales, col_codes, col_scales, finer_ratio, tile, ccodes, tile_e);
+    if (++kt >= kt_end) break;
+    kn = kt + 1 < kt_end ? kt + 1 : kt;
     w2d32_load(rs, N, K, ldw, n0, kn * 128, v0);
-    w2d32_tile(v1, N, K, n0, kt * 128, row_codes, row_scales, col_codes, col_scales, finer_ratio, tile, tile_e);
-    kt += gridDim.x;
-    if (kt >= gk) break;
+    w2d32_tile(v1, N, K, n0, kt * 128, row_codes, row_scales, col_codes, col_scales, finer_ratio, tile, ccodes, tile_e);
+    if (++kt >= kt_end) break;
   }
 }
 
@@ -434,12 +414,14 @@ fp4_status fp4_quantize_w2d32(const uint16_t* w, int64_t n, int64_t k, int64_t l
     return FP4_EALIGN;
   const int64_t gk = (k + 127) / 128, gy = (n + 127) / 128;
   if (gy > kMaxGridY || ldw >= ((int64_t)1 << 22)) return FP4_ESHAPE;   // 128-row strips stay < 2 GiB
-  // about kTargetBlocks / 2 workgroups (LDS allows 4 per CU), each walking
-  // several macro tiles along K
-  const int64_t gx = std::min<int64_t>(gk, std::max<int64_t>(1, (kTargetBlocks / 2) / gy));
+  // about 768 workgroups (3 per CU), each walking a run of consecutive macro
+  // tiles along K
+  const int64_t want_x = std::max<int64_t>(1, 768 / gy);
+  const int per = (int)((gk + want_x - 1) / want_x);
+  const int64_t gx = (gk + per - 1) / per;
   hipLaunchKernelGGL(quant_w2d32_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0,
                      as_stream(stream), w, n, k, ldw, row_codes, row_scales, col_codes, col_scales,
-                     finer_ratio);
+                     finer_ratio, per);
   return launch_status();
 }
 
