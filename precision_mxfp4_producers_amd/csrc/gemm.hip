@@ -49,7 +49,7 @@ constexpr int kFastThreads = 512;           // fast path
 constexpr int kStageBytes = BM * BKB + BN * BKB + BM * 8 + BN * 8;    // 69632
 constexpr int kSmemBytes = 2 * kStageBytes;                            // 139264
 constexpr int kHPitch = 272;                // bytes per row of the staged h tile (256 + 16)
-static_assert(256 * kHPitch <= kSmemBytes, "h tile fits in the stage buffers");
+static_assert(2 * 256 * kHPitch <= kSmemBytes, "h and a/b tiles fit in the stage buffers");
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
@@ -689,6 +689,130 @@ __device__ __forceinline__ void store_c_tile_staged(uint8_t* smem, const v16f (&
   }
 }
 
+// SwiGLU producer epilogue for the 8-wave tile (256 tokens x 128 FFN columns;
+// wave (wm, wn) holds a in sub-tile 0 and b in sub-tile 1 for FFN columns
+// wn*32 ..).  LDS (free after the main loop) holds two staged bf16 tiles of
+// 256 rows x kHPitch bytes: h in the first, a then b in the second.  Within a
+// row, dword d sits at d ^ hswz(row) so that the column-pair reads of the H32
+// pass (8 lanes per column pair, one per token block) hit distinct banks; the
+// XOR moves whole 8-dword groups, so 16-byte chunks stay contiguous.
+//   pass 1  a, b, h in bf16 (a and b are the rounded GEMM outputs)
+//   pass 2  a out with whole-row stores; h row codes (4 lanes per row: 64
+//           contiguous bytes); h column codes with H32 (8 lanes per column:
+//           one whole 128-byte line)
+//   pass 3  b through the same buffer as a
+__device__ __forceinline__ int hswz(int row) { return ((row >> 5) & 7) << 3; }
+
+__device__ __forceinline__ void swiglu_epilogue_staged(
+    uint8_t* smem, const v16f (&acc)[4][2], int64_t T, int64_t Fdim, int64_t m0, int64_t n0, int wave, int lane,
+    int wm, int wn, int hl, uint16_t* __restrict__ a_out, uint16_t* __restrict__ b_out,
+    uint8_t* __restrict__ h_codes, uint8_t* __restrict__ h_scales, uint8_t* __restrict__ ht_codes,
+    uint8_t* __restrict__ ht_scales, uint32_t sign_mask16) {
+  uint8_t* hs = smem;
+  uint8_t* as = smem + 256 * kHPitch;
+  const int tid = threadIdx.x;
+  uint32_t bpk[4][4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lr = wm * 128 + 32 * i + (lane & 31);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dw = (wn * 32 + 8 * g + 4 * hl) >> 1;     // first dword of the lane's 4 columns
+      uint32_t ab[2], bb[2], hb[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        ab[u] = bf16_pack2_rne(acc[i][0][4 * g + 2 * u], acc[i][0][4 * g + 2 * u + 1]);
+        bb[u] = bf16_pack2_rne(acc[i][1][4 * g + 2 * u], acc[i][1][4 * g + 2 * u + 1]);
+        float sg0, sl0, sg1, sl1;
+        sigmoid_silu(__uint_as_float(ab[u] << 16), sg0, sl0);
+        sigmoid_silu(__uint_as_float(ab[u] & 0xFFFF0000u), sg1, sl1);
+        hb[u] = bf16_pack2_rne(__fmul_rn(sl0, __uint_as_float(bb[u] << 16)),
+                               __fmul_rn(sl1, __uint_as_float(bb[u] & 0xFFFF0000u)));
+      }
+      const int off = lr * kHPitch + 4 * (dw ^ hswz(lr));
+      *reinterpret_cast<uint2*>(hs + off) = make_uint2(hb[0], hb[1]);
+      *reinterpret_cast<uint2*>(as + off) = make_uint2(ab[0], ab[1]);
+      bpk[i][g][0] = bb[0];
+      bpk[i][g][1] = bb[1];
+    }
+  }
+  __syncthreads();
+  // a out: 16 lanes per row (256 bytes), 32 rows per pass of the workgroup
+  const int ch = tid & 15;
+#pragma unroll 4
+  for (int p = 0; p < 8; ++p) {
+    const int r = 32 * p + (tid >> 4);
+    const int64_t row = m0 + r, col = n0 + 8 * ch;
+    if (row < T && col < Fdim)
+      *reinterpret_cast<uint4*>(a_out + row * Fdim + col) =
+          *reinterpret_cast<const uint4*>(as + r * kHPitch + 4 * ((4 * ch) ^ hswz(r)));
+  }
+  // h row codes: thread (row b/4, block b%4)
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int b = tid + 512 * k, lr = b >> 2, blk = b & 3;
+    const int64_t row = m0 + lr, col0 = n0 + 32 * blk;
+    uint32_t wv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 d = *reinterpret_cast<const uint4*>(hs + lr * kHPitch + 4 * ((16 * blk + 4 * q) ^ hswz(lr)));
+      wv[4 * q] = d.x; wv[4 * q + 1] = d.y; wv[4 * q + 2] = d.z; wv[4 * q + 3] = d.w;
+    }
+    int e;
+    const uint4 code = encode_block_bf16(wv, e);
+    if (row < T && col0 < Fdim) {
+      *reinterpret_cast<uint4*>(h_codes + row * (Fdim >> 1) + (col0 >> 1)) = code;
+      h_scales[row * (Fdim >> 5) + (col0 >> 5)] = (uint8_t)(e + 127);
+    }
+  }
+  // h column codes with H32: thread (column pair tid/8, token block tid%8)
+  if (ht_codes != nullptr) {
+    const int cp = tid >> 3, tb = tid & 7;
+    const int64_t r0 = m0 + 32 * tb;
+    uint32_t v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = *reinterpret_cast<const uint32_t*>(hs + (32 * tb + i) * kHPitch + 4 * (cp ^ (tb << 3)));
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int64_t col = n0 + 2 * cp + c;
+      float fv[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        uint32_t bits = (v[i] >> (16 * c)) & 0xFFFFu;
+        bits ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;
+        fv[i] = bf16_bits_to_f32(bits);
+      }
+      h32_block(fv);
+      int e;
+      const uint4 code = encode_block_rtn(fv, e);
+      if (r0 < T && col < Fdim) {
+        *reinterpret_cast<uint4*>(ht_codes + col * (T >> 1) + (r0 >> 1)) = code;
+        ht_scales[col * (T >> 5) + (r0 >> 5)] = (uint8_t)(e + 127);
+      }
+    }
+  }
+  __syncthreads();
+  // b through the a buffer
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lr = wm * 128 + 32 * i + (lane & 31);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dw = (wn * 32 + 8 * g + 4 * hl) >> 1;
+      *reinterpret_cast<uint2*>(as + lr * kHPitch + 4 * (dw ^ hswz(lr))) = make_uint2(bpk[i][g][0], bpk[i][g][1]);
+    }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int p = 0; p < 8; ++p) {
+    const int r = 32 * p + (tid >> 4);
+    const int64_t row = m0 + r, col = n0 + 8 * ch;
+    if (row < T && col < Fdim)
+      *reinterpret_cast<uint4*>(b_out + row * Fdim + col) =
+          *reinterpret_cast<const uint4*>(as + r * kHPitch + 4 * ((4 * ch) ^ hswz(r)));
+  }
+}
+
 __global__ __launch_bounds__(kGemmThreads) void gemm_generic_kernel(
     int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, float* __restrict__ c, int64_t ldc,
@@ -778,21 +902,8 @@ __global__ __launch_bounds__(kFastThreads) void swiglu_fast_kernel(
   Operand A{x_codes, x_scales, T}, B{w_codes, w_scales, 2 * Fdim};
   v16f acc[4][2];
   main_loop_fast<true>(smem, A, B, m0, n0, Fdim, D, acc, wm, wn);
-  // wave (wm, wn): a in sub-tile 0 and b in sub-tile 1, FFN columns wn*32 ..
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int lr = wm * 128 + 32 * i + (lane & 31);
-    const int64_t row = m0 + lr;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int lc = wn * 32 + 8 * g + 4 * hl;
-      const int64_t col = n0 + lc;
-      swiglu_quad(acc[i][0], acc[i][1], g, smem + lr * kHPitch + lc * 2, a_out + row * Fdim + col,
-                  b_out + row * Fdim + col, row < T && col < Fdim);
-    }
-  }
-  __syncthreads();
-  quantize_h_tile<kFastThreads>(smem, m0, n0, T, Fdim, h_codes, h_scales, ht_codes, ht_scales, sign_mask16);
+  swiglu_epilogue_staged(smem, acc, T, Fdim, m0, n0, wave, lane, wm, wn, hl, a_out, b_out, h_codes, h_scales,
+                         ht_codes, ht_scales, sign_mask16);
 }
 
 }  // namespace mx

@@ -15,6 +15,20 @@ namespace mx {
 // ---------------------------------------------------------------- bf16 / fp32
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (x low), round to nearest even, NaN -> 0x7FC0.
+// gfx950's v_cvt_pk_bf16_f32 rounds to nearest even on every non-NaN fp32
+// pattern (checked against the integer rounding on all 2^32 inputs); NaNs keep
+// a payload there, so they are replaced by the canonical quiet NaN.
+__device__ __forceinline__ uint32_t bf16_pack2_rne(float x, float y) {
+  const bf16x2_t v = {(__bf16)x, (__bf16)y};
+  uint32_t r = __builtin_bit_cast(uint32_t, v);
+  r = (x != x) ? ((r & 0xFFFF0000u) | 0x7FC0u) : r;
+  r = (y != y) ? ((r & 0x0000FFFFu) | 0x7FC00000u) : r;
+  return r;
+}
+
 // fp32 -> bf16 bits, round to nearest even; NaN -> 0x7FC0.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   uint32_t b = __float_as_uint(x);
@@ -44,7 +58,6 @@ __device__ __forceinline__ float inv_pow2(int e) { return __uint_as_float((uint3
 // results were checked against the rounding contract on every bf16 pattern at
 // every exponent in [-127, 126] and on 4M random fp32 inputs; the GPU parity
 // tests compare every producer with the CPU reference.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // 2^e as fp32 for e in [-127, 126] (2^-127 is the subnormal 0x00400000).
 __device__ __forceinline__ float pow2_scale(int e) {
