@@ -35,6 +35,7 @@ METRIC = "MXFP4 quantize+GEMM TFLOP/s (Fprop/Dgrad/Wgrad) and quantizer GB/s, % 
 B_SINGLE = 2 + 0.5 + 1 / 32          # bf16 in, one orientation of codes + scales
 B_2D32 = 2 + 2 * (0.5 + 1 / 32)      # bf16 in, two layouts
 B_SWIGLU_BWD = 4 + 2 + 2 + 2 + 2     # dH fp32, a, b in; dA, dB out
+B_BWD_PRODUCER = 4 + 2 + 2 + 4 * (0.5 + 1 / 32)   # dH, a, b in; dA, dB as row SR + column H32 MXFP4
 
 
 def parse():
@@ -45,6 +46,8 @@ def parse():
     p.add_argument("--workload", default="ffn_step_8192x4096x14336")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--unfused-backward", action="store_true",
+                   help="FFN step: SwiGLU backward, SR rows and H32 cols of dA/dB as five separate calls")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of known size (for scaling HBM byte counters)")
     return p.parse_args()
@@ -95,7 +98,8 @@ def copy_calibration():
 class Step:
     """Holds device inputs/outputs and enqueues one step as a list of named calls."""
 
-    def __init__(self, name, seed, mx, torch):
+    def __init__(self, name, seed, mx, torch, fused_backward=True):
+        self.fused_backward = fused_backward
         import synthetic
         self.mx, self.torch = mx, torch
         self.name = name
@@ -189,13 +193,20 @@ class Step:
         dyc = self.q_cols("cols(dY,H32)", dY)
         dh = self.gemm("W2 Dgrad", dyr, w2[2:])
         self.gemm("W2 Wgrad", dyc, hc)
-        da, db = self.e((T, F), torch.int16), self.e((T, F), torch.int16)
-        self.calls.append(("swiglu_backward", "quant", T * F * B_SWIGLU_BWD,
-                           lambda: mx.fp4_swiglu_backward(dh, a, b, da, db), 0))
-        dar = self.q_rows("rows(dA,SR)", da, 1, 1)
-        dbr = self.q_rows("rows(dB,SR)", db, 1, 2)
-        dac = self.q_cols("cols(dA,H32)", da)
-        dbc = self.q_cols("cols(dB,H32)", db)
+        if self.fused_backward:
+            shapes = [(T, F // 2), (T, F // 32)] * 2 + [(F, T // 2), (F, T // 32)] * 2
+            outs = [self.u8(*shp) for shp in shapes]
+            dar, dbr, dac, dbc = (outs[0], outs[1]), (outs[2], outs[3]), (outs[4], outs[5]), (outs[6], outs[7])
+            self.calls.append(("swiglu_bwd_producer", "quant", T * F * B_BWD_PRODUCER,
+                               lambda: mx.fp4_swiglu_backward_producer(dh, a, b, self.seed, 1, 2, self.mask, outs), 0))
+        else:
+            da, db = self.e((T, F), torch.int16), self.e((T, F), torch.int16)
+            self.calls.append(("swiglu_backward", "quant", T * F * B_SWIGLU_BWD,
+                               lambda: mx.fp4_swiglu_backward(dh, a, b, da, db), 0))
+            dar = self.q_rows("rows(dA,SR)", da, 1, 1)
+            dbr = self.q_rows("rows(dB,SR)", db, 1, 2)
+            dac = self.q_cols("cols(dA,H32)", da)
+            dbc = self.q_cols("cols(dB,H32)", db)
         xc = self.q_cols("cols(X,H32)", X)
         dx = self.gemm("W1 Dgrad", dar, w1[2:])
         self.gemm("W3 Dgrad (+=)", dbr, w3[2:], c=dx, accumulate=True)
@@ -311,7 +322,7 @@ def main():
     mx.load()
     torch.cuda.set_device(0)
     print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
-    step = Step(args.workload, args.seed, mx, torch)
+    step = Step(args.workload, args.seed, mx, torch, fused_backward=not args.unfused_backward)
     ncalls = len(step.calls)
     print(f"[bench] warmup {args.warmup} steps, {ncalls} calls per step", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -366,6 +377,7 @@ def main():
         "dtype": "e2m1/e8m0 operands, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": args.workload, "gemm_tflop_per_step": round(flops / 1e12, 3),
+                   "swiglu_backward": "unfused" if args.unfused_backward else "fused producer",
                    "quantizer_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1) if q_ms > 0 else None,
                    "quantizer_frac_hbm_peak": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if q_ms > 0 else None},
         "roofline": {"bound": "mfma", "kernel": "gemm_fast_kernel", "achieved": round(achieved, 1),

@@ -165,6 +165,34 @@ fp4_status fp4_swiglu_backward(int64_t t, int64_t f, const float* dh, int64_t ld
                                uint16_t* da_bf16, uint16_t* db_bf16, void* stream);
 
 /*
+ * Fused SwiGLU backward producer (§3.1-§3.2: the producer completes every
+ * representation its consumers read; §2.3 Eq. 5-6 and §2.5: the W1/W3 Dgrad
+ * reads dA, dB row-facing with SR, the W1/W3 Wgrad reads them column-facing
+ * with the fixed-sign H32).  Bit-identical to
+ *   fp4_swiglu_backward(dh, a, b) -> dA, dB, then
+ *   fp4_quantize_rows(dA, FP4_SR, seed, offset_a) -> da_codes, da_scales
+ *   fp4_quantize_rows(dB, FP4_SR, seed, offset_b) -> db_codes, db_scales
+ *   fp4_quantize_cols(dA, 32, sign_mask16)        -> dat_codes, dat_scales
+ *   fp4_quantize_cols(dB, 32, sign_mask16)        -> dbt_codes, dbt_scales
+ * without writing the bf16 dA, dB.  SR draws are indexed by the element's
+ * row-major index in the [t][f] tensor, as in fp4_quantize_rows.
+ *   dh [t][lddh] fp32; a_bf16, b_bf16 [t][f]
+ *   da_codes, db_codes [t][f/2]; da_scales, db_scales [t][f/32]
+ *   dat_codes, dbt_codes [f][t/2]; dat_scales, dbt_scales [f][t/32]
+ * Errors: FP4_EINVAL null pointer; FP4_ESHAPE t or f not a multiple of 32,
+ * lddh < f; FP4_EALIGN dh, a, b or a code buffer not 16-byte aligned, or lddh
+ * not a multiple of 4.
+ */
+fp4_status fp4_swiglu_backward_producer(int64_t t, int64_t f, const float* dh, int64_t lddh,
+                                        const uint16_t* a_bf16, const uint16_t* b_bf16,
+                                        uint64_t seed, uint64_t offset_a, uint64_t offset_b,
+                                        uint32_t sign_mask16,
+                                        uint8_t* da_codes, uint8_t* da_scales,
+                                        uint8_t* db_codes, uint8_t* db_scales,
+                                        uint8_t* dat_codes, uint8_t* dat_scales,
+                                        uint8_t* dbt_codes, uint8_t* dbt_scales, void* stream);
+
+/*
  * Fixed 16-entry sign vector for H32 as a bit mask (bit j set => d_j = -1):
  * the low 16 bits of word 0 of Philox4x32-10 at counter (0,0,0,0) under key
  * (lo32(seed), hi32(seed)).  Host-only, no device work.

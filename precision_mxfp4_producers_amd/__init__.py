@@ -31,6 +31,7 @@ _SIGS = {
     "fp4_gemm": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _int, _vp],
     "fp4_swiglu_producer": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u32, _vp],
     "fp4_swiglu_backward": [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp],
+    "fp4_swiglu_backward_producer": [_i64, _i64, _vp, _i64, _vp, _vp, _u64, _u64, _u64, _u32] + [_vp] * 9,
     "fp4_sign_mask_from_seed": [_u64],
     "fp4_last_hip_error": [],
     "fp4_abi_version": [],
@@ -185,6 +186,28 @@ def fp4_swiglu_backward(dh, a, b, da=None, db=None):
     db = _out(db, (t, f), torch.int16, a.device, "db") if db is not None else torch.empty((t, f), dtype=torch.int16, device=a.device)
     _check(load().fp4_swiglu_backward(t, f, _p(dh), dh.stride(0), _p(a), _p(b), _p(da), _p(db), _stream()))
     return da, db
+
+
+def fp4_swiglu_backward_producer(dh, a, b, seed, offset_a, offset_b, sign_mask16, out=None):
+    """dA, dB of the SwiGLU backward emitted directly as MXFP4: returns
+    ((da_codes, da_scales), (db_codes, db_scales), (dat_codes, dat_scales),
+    (dbt_codes, dbt_scales)) -- row-facing SR and column-facing H32."""
+    _dev(dh, "dh")
+    t, f = a.shape
+    if dh.dtype != torch.float32 or dh.dim() != 2 or dh.stride(1) != 1 or tuple(dh.shape) != (t, f):
+        raise Fp4Error("dh must be fp32 [t][f] with unit column stride")
+    for x, nm in ((a, "a"), (b, "b")):
+        if x.dtype not in (torch.int16, torch.bfloat16) or not x.is_contiguous() or tuple(x.shape) != (t, f):
+            raise Fp4Error(f"{nm} must be a contiguous bf16 [t][f] tensor")
+    dev = a.device
+    shapes = [(t, f // 2), (t, f // 32), (t, f // 2), (t, f // 32),
+              (f, t // 2), (f, t // 32), (f, t // 2), (f, t // 32)]
+    names = ["da_codes", "da_scales", "db_codes", "db_scales", "dat_codes", "dat_scales", "dbt_codes", "dbt_scales"]
+    out = list(out) if out is not None else [None] * 8
+    bufs = [_out(o, shp, torch.uint8, dev, nm) for o, shp, nm in zip(out, shapes, names)]
+    _check(load().fp4_swiglu_backward_producer(t, f, _p(dh), dh.stride(0), _p(a), _p(b), int(seed), int(offset_a),
+                                               int(offset_b), int(sign_mask16), *[_p(x) for x in bufs], _stream()))
+    return (bufs[0], bufs[1]), (bufs[2], bufs[3]), (bufs[4], bufs[5]), (bufs[6], bufs[7])
 
 
 def fp4_sign_mask_from_seed(seed):

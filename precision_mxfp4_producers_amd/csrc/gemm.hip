@@ -548,34 +548,6 @@ __device__ __forceinline__ void swiglu_quad(const v16f& acc_a, const v16f& acc_b
   }
 }
 
-__device__ __forceinline__ void h32_block(float (&f)[32]) {
-#pragma unroll
-  for (int s = 1; s < 32; s <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if ((j & s) == 0) {
-        const float lo = f[j], hi = f[j + s];
-        f[j] = __fadd_rn(lo, hi);
-        f[j + s] = __fsub_rn(lo, hi);
-      }
-    }
-  }
-  const float cn = 0x1.6a09e6p-3f;                       // RN_fp32(2^-2.5)
-#pragma unroll
-  for (int j = 0; j < 32; ++j) f[j] = __fmul_rn(f[j], cn);
-}
-
-// RTN MXFP4 of one 32-value fp32 block: upward scale of its maximum, codes.
-__device__ __forceinline__ uint4 encode_block_rtn(const float (&f)[32], int& e_out) {
-  float am = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(f[j]));
-  const int e = upward_exp(__float_as_uint(am));
-  const float sc = pow2_scale(e);
-  e_out = e;
-  return make_uint4(rtn8_f32(f, sc), rtn8_f32(f + 8, sc), rtn8_f32(f + 16, sc), rtn8_f32(f + 24, sc));
-}
-
 // RTN MXFP4 of one 32-value bf16 block given as 16 packed words.
 __device__ __forceinline__ uint4 encode_block_bf16(const uint32_t (&w)[16], int& e_out) {
   uint32_t m = 0;
@@ -630,9 +602,9 @@ __device__ __forceinline__ void quantize_h_tile(const uint8_t* smem, int64_t m0,
         bits ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;
         fv[i] = bf16_bits_to_f32(bits);
       }
-      h32_block(fv);
+      h32_fp32(fv);
       int e;
-      const uint4 code = encode_block_rtn(fv, e);
+      const uint4 code = encode32_rtn(fv, e);
       *reinterpret_cast<uint4*>(ht_codes + col * (T >> 1) + (r0 >> 1)) = code;
       ht_scales[col * (T >> 5) + (r0 >> 5)] = (uint8_t)(e + 127);
     }
@@ -782,9 +754,9 @@ __device__ __forceinline__ void swiglu_epilogue_staged(
         bits ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;
         fv[i] = bf16_bits_to_f32(bits);
       }
-      h32_block(fv);
+      h32_fp32(fv);
       int e;
-      const uint4 code = encode_block_rtn(fv, e);
+      const uint4 code = encode32_rtn(fv, e);
       if (r0 < T && col < Fdim) {
         *reinterpret_cast<uint4*>(ht_codes + col * (T >> 1) + (r0 >> 1)) = code;
         ht_scales[col * (T >> 5) + (r0 >> 5)] = (uint8_t)(e + 127);

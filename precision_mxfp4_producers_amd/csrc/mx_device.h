@@ -106,6 +106,47 @@ __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u, bool nonzero) {
   return lo + (u < thr ? 1u : 0u);
 }
 
+// ---------------------------------------------------------------- H32
+// Fixed-sign 32-point Hadamard of one block (signs already applied): fp32
+// butterflies (lo, hi) <- (lo + hi, lo - hi) with strides 1, 2, 4, 8, 16, then
+// times RN_fp32(2^-2.5); output in natural (Sylvester) order.
+__device__ __forceinline__ void h32_fp32(float (&f)[32]) {
+#pragma unroll
+  for (int s = 1; s < 32; s <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if ((j & s) == 0) {
+        const float lo = f[j], hi = f[j + s];
+        f[j] = __fadd_rn(lo, hi);
+        f[j + s] = __fsub_rn(lo, hi);
+      }
+    }
+  }
+  const float c = 0x1.6a09e6p-3f;                        // RN_fp32(2^-2.5)
+#pragma unroll
+  for (int j = 0; j < 32; ++j) f[j] = __fmul_rn(f[j], c);
+}
+
+// RTN MXFP4 of one 32-value fp32 block: upward scale of its maximum, codes.
+__device__ __forceinline__ uint4 encode32_rtn(const float (&f)[32], int& e_out) {
+  float am = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(f[j]));
+  const int e = upward_exp(__float_as_uint(am));
+  const float sc = pow2_scale(e);
+  e_out = e;
+  return make_uint4(rtn8_f32(f, sc), rtn8_f32(f + 8, sc), rtn8_f32(f + 16, sc), rtn8_f32(f + 24, sc));
+}
+
+// Largest 15-bit magnitude pattern among eight bf16 values (four words).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_absmax8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  const u16x2_t a = __builtin_bit_cast(u16x2_t, w0 & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2_t, w1 & 0x7FFF7FFFu);
+  const u16x2_t c = __builtin_bit_cast(u16x2_t, w2 & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2_t, w3 & 0x7FFF7FFFu);
+  const u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return max((uint32_t)m[0], (uint32_t)m[1]);
+}
+
 // ---------------------------------------------------------------- Philox
 struct u32x4 { uint32_t x, y, z, w; };
 

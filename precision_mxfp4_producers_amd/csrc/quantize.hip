@@ -26,16 +26,7 @@ constexpr int kThreads = 256;
 constexpr int kMaxGridY = 65535;
 constexpr int64_t kTargetBlocks = 2048;                  // 8 workgroups per CU
 
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
-
-// Largest 15-bit magnitude pattern among eight bf16 values (four words).
-__device__ __forceinline__ uint32_t bf16_absmax8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
-  const u16x2_t a = __builtin_bit_cast(u16x2_t, w0 & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2_t, w1 & 0x7FFF7FFFu);
-  const u16x2_t c = __builtin_bit_cast(u16x2_t, w2 & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2_t, w3 & 0x7FFF7FFFu);
-  const u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
-  return max((uint32_t)m[0], (uint32_t)m[1]);
-}
 
 // ------------------------------------------------------------------ rows
 // One lane quantizes 8 consecutive values (one 16-byte load); four lanes share
@@ -101,39 +92,6 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 }
 
 // ------------------------------------------------------------------ cols
-// One lane owns two adjacent columns and one 32-row block: it reads 32 row
-// segments of 4 bytes (64 lanes cover 256 contiguous bytes per row), optionally
-// applies the fixed-sign H32 to each column in registers (fp32, stage order
-// of the contract), and writes each column's 16 code bytes to the transposed
-// output.
-__device__ __forceinline__ void h32_inplace(float (&f)[32]) {
-#pragma unroll
-  for (int s = 1; s < 32; s <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if ((j & s) == 0) {
-        const float lo = f[j], hi = f[j + s];
-        f[j] = __fadd_rn(lo, hi);
-        f[j + s] = __fsub_rn(lo, hi);
-      }
-    }
-  }
-  const float c = 0x1.6a09e6p-3f;                        // RN_fp32(2^-2.5)
-#pragma unroll
-  for (int j = 0; j < 32; ++j) f[j] = __fmul_rn(f[j], c);
-}
-
-// RTN MXFP4 of one 32-value fp32 block: upward scale of its maximum, codes.
-__device__ __forceinline__ uint4 encode32_f32(const float (&f)[32], int& e_out) {
-  float am = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(f[j]));
-  const int e = upward_exp(__float_as_uint(am));
-  const float sc = pow2_scale(e);
-  e_out = e;
-  return make_uint4(rtn8_f32(f, sc), rtn8_f32(f + 8, sc), rtn8_f32(f + 16, sc), rtn8_f32(f + 24, sc));
-}
-
 // A workgroup owns kColTok tokens x kColW columns: it loads the bf16 tile
 // row-contiguously (each row segment 128 bytes) into LDS, encodes column pairs
 // from LDS (optional H32 per 32-token block), parks the codes in LDS and
@@ -193,9 +151,9 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
           if constexpr (kH32) bb ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;   // d_(i mod 16)
           f[i] = bf16_bits_to_f32(bb);
         }
-        if constexpr (kH32) h32_inplace(f);
+        if constexpr (kH32) h32_fp32(f);
         int e;
-        const uint4 code = encode32_f32(f, e);
+        const uint4 code = encode32_rtn(f, e);
         *reinterpret_cast<uint4*>(ctile + (2 * cp + c) * kColCodePitch + tb * 16) = code;
         stile[2 * cp + c][tb] = (uint8_t)(e + 127);
       }

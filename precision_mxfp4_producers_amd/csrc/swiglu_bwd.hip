@@ -5,6 +5,12 @@
 //   dA = bf16(((dH*b)*sig) * (1 + a*(1 - sig))),  dB = bf16(dH*s)
 // with single fp32 roundings in this order and no FMA.  HBM-bound: 12 bytes
 // per element (4 read dH, 2+2 read a/b, 2+2 written dA/dB).
+//
+// The fused backward producer applies the same arithmetic and emits dA and dB
+// directly in the two representations their consumers read (§2.3, §2.5, §3.1:
+// the producer completes every layout the next contractions need): row-facing
+// with Philox SR for the W1/W3 Dgrad and column-facing with the fixed-sign H32
+// for the W1/W3 Wgrad.  The bf16 dA, dB never leave the chip.
 #include <hip/hip_runtime.h>
 
 #include "abi_common.h"
@@ -49,6 +55,174 @@ __global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_kernel(
   }
 }
 
+
+// ------------------------------------------------------------ fused producer
+// A workgroup owns kFbCols FFN columns x kFbTok tokens, walked in chunks of
+// kFbChunk tokens:
+//   1. dA, dB of the chunk in bf16 into LDS (thread: 8 columns x 4 rows);
+//   2. row-facing SR of every 32-column block (thread: one block of one row;
+//      four threads cover a row's 64 code bytes), draws indexed by the
+//      element's row-major index in the full [t][f] tensor;
+//   3. column-facing H32 of every 32-token block (thread: one column pair),
+//      codes parked in LDS per column;
+// and finally each column's kFbTok/2 code bytes -- a whole 128-byte line --
+// go out with coalesced stores.
+constexpr int kFbCols = 128, kFbTok = 256, kFbChunk = 64;
+constexpr int kFbPitch = 272;                            // bytes per staged bf16 row (256 + 16)
+constexpr int kFbCodePitch = kFbTok / 2 + 16;            // bytes per staged column of codes
+
+struct FbOut {
+  uint8_t* codes;                                        // row-facing [t][f/2]
+  uint8_t* scales;                                       // [t][f/32]
+  uint8_t* codes_t;                                      // column-facing [f][t/2]
+  uint8_t* scales_t;                                     // [f][t/32]
+  uint64_t offset;                                       // SR counter offset
+};
+
+__global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_producer_kernel(
+    int64_t T, int64_t Fdim, const float* __restrict__ dh, int64_t lddh, const uint16_t* __restrict__ a,
+    const uint16_t* __restrict__ b, FbOut oa, FbOut ob, uint64_t seed, uint32_t sign_mask16) {
+  __shared__ __attribute__((aligned(16))) uint8_t gs[2][kFbChunk * kFbPitch];          // dA, dB chunk
+  __shared__ __attribute__((aligned(16))) uint8_t cs[2][kFbCols * kFbCodePitch];       // column codes
+  __shared__ uint8_t ss[2][kFbCols][kFbTok / 32];                                      // column scales
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * kFbCols, t0 = (int64_t)blockIdx.y * kFbTok;
+  const int ncol = (int)min<int64_t>(kFbCols, Fdim - c0);          // multiple of 32
+  const int ntok = (int)min<int64_t>(kFbTok, T - t0);              // multiple of 32
+
+  for (int ck = 0; ck * kFbChunk < ntok; ++ck) {
+    const int nrow = min(kFbChunk, ntok - ck * kFbChunk);           // 32 or 64
+    const int64_t r0 = t0 + ck * kFbChunk;
+    // 1. dA, dB
+    {
+      const int cc = tid & 15, rg = tid >> 4;
+      const bool col_ok = cc * 8 < ncol;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = rg + 16 * k;
+        uint32_t oa4[4] = {0u, 0u, 0u, 0u}, ob4[4] = {0u, 0u, 0u, 0u};
+        if (col_ok && r < nrow) {
+          const float* dp = dh + (r0 + r) * lddh + c0 + cc * 8;
+          const float4 d0 = *reinterpret_cast<const float4*>(dp);
+          const float4 d1 = *reinterpret_cast<const float4*>(dp + 4);
+          const uint4 av = *reinterpret_cast<const uint4*>(a + (r0 + r) * Fdim + c0 + cc * 8);
+          const uint4 bv = *reinterpret_cast<const uint4*>(b + (r0 + r) * Fdim + c0 + cc * 8);
+          const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+          const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
+          const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            float dav[2], dbv[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const float af = bf16_bits_to_f32((aw[i >> 1] >> (16 * u)) & 0xFFFFu);
+              const float bf = bf16_bits_to_f32((bw[i >> 1] >> (16 * u)) & 0xFFFFu);
+              float sig, sl;
+              sigmoid_silu(af, sig, sl);
+              const float g = __fadd_rn(1.0f, __fmul_rn(af, __fsub_rn(1.0f, sig)));
+              dav[u] = __fmul_rn(__fmul_rn(__fmul_rn(dv[i + u], bf), sig), g);
+              dbv[u] = __fmul_rn(dv[i + u], sl);
+            }
+            oa4[i >> 1] = bf16_pack2_rne(dav[0], dav[1]);
+            ob4[i >> 1] = bf16_pack2_rne(dbv[0], dbv[1]);
+          }
+        }
+        *reinterpret_cast<uint4*>(gs[0] + r * kFbPitch + cc * 16) = make_uint4(oa4[0], oa4[1], oa4[2], oa4[3]);
+        *reinterpret_cast<uint4*>(gs[1] + r * kFbPitch + cc * 16) = make_uint4(ob4[0], ob4[1], ob4[2], ob4[3]);
+      }
+    }
+    __syncthreads();
+    // 2. row-facing SR: thread (row tid/4, block tid%4) of each tensor
+    {
+      const int r = tid >> 2, blk = tid & 3;
+      const int64_t row = r0 + r, col0 = c0 + 32 * blk;
+      const bool ok = r < nrow && 32 * blk < ncol;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const FbOut& o = k ? ob : oa;
+        uint32_t w[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 d = *reinterpret_cast<const uint4*>(gs[k] + r * kFbPitch + blk * 64 + q * 16);
+          w[4 * q] = d.x; w[4 * q + 1] = d.y; w[4 * q + 2] = d.z; w[4 * q + 3] = d.w;
+        }
+        uint32_t m = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) m = max(m, bf16_absmax8(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]));
+        const int e = upward_exp(m << 16);
+        const float inv = inv_pow2(e);
+        const uint64_t blk0 = ((uint64_t)row * (uint64_t)Fdim + (uint64_t)col0) >> 2;   // first Philox counter
+        uint32_t packed[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {                    // 8 elements per output word
+          const u32x4 u0 = sr_words(blk0 + 2 * q, seed, o.offset);
+          const u32x4 u1 = sr_words(blk0 + 2 * q + 1, seed, o.offset);
+          const uint32_t u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+          uint32_t pk = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t bits = (w[4 * q + (j >> 1)] >> (16 * (j & 1))) & 0xFFFFu;
+            const uint32_t mag = bits & 0x7FFFu;
+            const float y = bf16_bits_to_f32(mag) * inv;
+            pk |= (e2m1_sr(y, u[j], mag != 0u) | ((bits >> 12) & 8u)) << (4 * j);
+          }
+          packed[q] = pk;
+        }
+        if (ok) {
+          *reinterpret_cast<uint4*>(o.codes + row * (Fdim >> 1) + (col0 >> 1)) =
+              make_uint4(packed[0], packed[1], packed[2], packed[3]);
+          o.scales[row * (Fdim >> 5) + (col0 >> 5)] = (uint8_t)(e + 127);
+        }
+      }
+    }
+    // 3. column-facing H32: thread (tensor tid/128, token block (tid/64)%2, column pair tid%64)
+    {
+      const int k = tid >> 7, tb = (tid >> 6) & 1, cp = tid & 63;
+      if (32 * tb < nrow && 2 * cp < ncol) {
+        uint32_t v[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = *reinterpret_cast<const uint32_t*>(gs[k] + (32 * tb + i) * kFbPitch + cp * 4);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          float f[32];
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            uint32_t bb = (v[i] >> (16 * c)) & 0xFFFFu;
+            bb ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;   // d_(i mod 16)
+            f[i] = bf16_bits_to_f32(bb);
+          }
+          h32_fp32(f);
+          int e;
+          const uint4 code = encode32_rtn(f, e);
+          const int tblk = ck * (kFbChunk / 32) + tb;   // token block within the workgroup
+          *reinterpret_cast<uint4*>(cs[k] + (2 * cp + c) * kFbCodePitch + tblk * 16) = code;
+          ss[k][2 * cp + c][tblk] = (uint8_t)(e + 127);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // 4. column codes out: piece p = (tensor, column, 16-byte piece); 8 threads per column
+#pragma unroll
+  for (int pass = 0; pass < 8; ++pass) {
+    const int p = tid + kBwdThreads * pass;
+    const int k = p >> 10, col = (p >> 3) & 127, q = p & 7;
+    if (col < ncol && 32 * q < ntok) {
+      const FbOut& o = k ? ob : oa;
+      *reinterpret_cast<uint4*>(o.codes_t + (c0 + col) * (T >> 1) + (t0 >> 1) + 16 * q) =
+          *reinterpret_cast<const uint4*>(cs[k] + col * kFbCodePitch + 16 * q);
+    }
+  }
+  {
+    const int k = tid >> 7, col = tid & 127;
+    if (col < ncol) {
+      const FbOut& o = k ? ob : oa;
+      uint8_t* dst = o.scales_t + (c0 + col) * (T >> 5) + (t0 >> 5);
+      for (int tb = 0; tb < ntok / 32; ++tb) dst[tb] = ss[k][col][tb];
+    }
+  }
+}
+
 }  // namespace mx
 
 using namespace mx;
@@ -65,5 +239,26 @@ extern "C" fp4_status fp4_swiglu_backward(int64_t t, int64_t f, const float* dh,
   dim3 grid((unsigned)((cpr + kBwdThreads - 1) / kBwdThreads), (unsigned)(t < kMaxGridY ? t : kMaxGridY));
   hipLaunchKernelGGL(swiglu_bwd_kernel, grid, dim3(kBwdThreads), 0, as_stream(stream), t, f, dh, lddh, a_bf16,
                      b_bf16, da_bf16, db_bf16);
+  return launch_status();
+}
+
+extern "C" fp4_status fp4_swiglu_backward_producer(
+    int64_t t, int64_t f, const float* dh, int64_t lddh, const uint16_t* a_bf16, const uint16_t* b_bf16,
+    uint64_t seed, uint64_t offset_a, uint64_t offset_b, uint32_t sign_mask16,
+    uint8_t* da_codes, uint8_t* da_scales, uint8_t* db_codes, uint8_t* db_scales,
+    uint8_t* dat_codes, uint8_t* dat_scales, uint8_t* dbt_codes, uint8_t* dbt_scales, void* stream) {
+  if (!dh || !a_bf16 || !b_bf16 || !da_codes || !da_scales || !db_codes || !db_scales || !dat_codes ||
+      !dat_scales || !dbt_codes || !dbt_scales)
+    return FP4_EINVAL;
+  if (!mult32(t) || !mult32(f) || lddh < f) return FP4_ESHAPE;
+  if (!aligned16(dh) || !aligned16(a_bf16) || !aligned16(b_bf16) || !aligned16(da_codes) ||
+      !aligned16(db_codes) || !aligned16(dat_codes) || !aligned16(dbt_codes) || (lddh % 4) != 0)
+    return FP4_EALIGN;
+  const int64_t gx = (f + kFbCols - 1) / kFbCols, gy = (t + kFbTok - 1) / kFbTok;
+  if (gy > kMaxGridY) return FP4_ESHAPE;
+  const FbOut oa{da_codes, da_scales, dat_codes, dat_scales, offset_a};
+  const FbOut ob{db_codes, db_scales, dbt_codes, dbt_scales, offset_b};
+  hipLaunchKernelGGL(swiglu_bwd_producer_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kBwdThreads), 0,
+                     as_stream(stream), t, f, dh, lddh, a_bf16, b_bf16, oa, ob, seed, sign_mask16 & 0xFFFFu);
   return launch_status();
 }

@@ -71,3 +71,11 @@ def test_argument_errors_are_reported_without_gpu_work():
     assert lib.fp4_swiglu_producer(32, 32, 32, v(4096), v(4096), v(4096), v(4096), v(4096), v(4096),
                                    v(4096), v(4096), v(4096), None, 0, None) == 1
     assert lib.fp4_swiglu_backward(32, 32, v(4096), 16, v(4096), v(4096), v(4096), v(4096), None) == 2
+    u64 = ctypes.c_uint64
+    bufs = [v(4096)] * 8
+    assert lib.fp4_swiglu_backward_producer(32, 48, v(4096), 48, v(4096), v(4096), u64(0), u64(0), u64(1),
+                                            0, *bufs, None) == 2
+    assert lib.fp4_swiglu_backward_producer(32, 32, v(4096), 32, v(4096), None, u64(0), u64(0), u64(1),
+                                            0, *bufs, None) == 1
+    assert lib.fp4_swiglu_backward_producer(32, 32, v(4100), 32, v(4096), v(4096), u64(0), u64(0), u64(1),
+                                            0, *bufs, None) == 3

@@ -231,6 +231,12 @@ def test_ffn_step(gpu_lib, name):
     check_cols(dac, np.ascontiguousarray(host16(cols_of(da, fc))), fc, mask, "cols(dA,H32)")
     check_cols(dbc, np.ascontiguousarray(host16(cols_of(db, fc))), fc, mask, "cols(dB,H32)")
 
+    # fused backward producer: the same bytes as the unfused calls, everywhere
+    fused = gpu_lib.fp4_swiglu_backward_producer(dh, a, b, seed, 1, 2, mask)
+    for got, want, nm in zip(fused, (dar, dbr, dac, dbc), ("dA rows", "dB rows", "dA cols", "dB cols")):
+        assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1]), "fused " + nm
+    del fused
+
     # the seven contractions
     check_gemm(y, (hrc, hrs), w2[:2], rng, "W2 Fprop")
     check_gemm(dh, dyr, w2[2:], rng, "W2 Dgrad")

@@ -219,6 +219,35 @@ def test_swiglu_backward(gpu_lib, tf):
     assert np.array_equal(host16(db), want_db)
 
 
+@pytest.mark.parametrize("tf", [(256, 256), (288, 160), (64, 96), (32, 32), (320, 416), (512, 128)])
+def test_swiglu_backward_producer(gpu_lib, tf):
+    """Fused backward producer == SwiGLU backward, then SR rows and H32 cols
+    of dA and dB (oracle composition and the unfused GPU calls)."""
+    t, f = tf
+    a = synthetic.tensor((t, f), std=1.3, seed=40)
+    b = synthetic.tensor((t, f), std=1.3, seed=41)
+    a[0, :8] = np.array([0x0000, 0x8000, 0x4300, 0xC300, 0x42C8, 0xC2C8, 0x7F7F, 0xFF7F], dtype=np.uint16)
+    rng = np.random.default_rng(42)
+    dh = (rng.standard_normal((t, f)) * 1e-3).astype(np.float32)
+    dh[1, :32] = 0.0
+    seed, oa, ob, mask = 2 ** 35 + 11, 5, 2 ** 33 + 9, P.sign_mask_from_seed(7)
+    dhd, ad, bd = torch.from_numpy(dh).cuda(), dev16(a), dev16(b)
+    (dar, dbr, dac, dbc) = gpu_lib.fp4_swiglu_backward_producer(dhd, ad, bd, seed, oa, ob, mask)
+    da, db = S.swiglu_backward(dh, a, b)
+    for got, want, nm in ((dar, Q.quantize_rows(da, Q.SR, seed, oa), "dA rows"),
+                          (dbr, Q.quantize_rows(db, Q.SR, seed, ob), "dB rows"),
+                          (dac, Q.quantize_cols(da, 32, mask), "dA cols"),
+                          (dbc, Q.quantize_cols(db, 32, mask), "dB cols")):
+        assert_same(got[0], want[0], nm + " codes")
+        assert_same(got[1], want[1], nm + " scales")
+    # same bytes as the unfused calls
+    dag, dbg = gpu_lib.fp4_swiglu_backward(dhd, ad, bd)
+    ref = (gpu_lib.fp4_quantize_rows(dag, gpu_lib.FP4_SR, seed, oa), gpu_lib.fp4_quantize_rows(dbg, gpu_lib.FP4_SR, seed, ob),
+           gpu_lib.fp4_quantize_cols(dag, 32, mask), gpu_lib.fp4_quantize_cols(dbg, 32, mask))
+    for got, want in zip((dar, dbr, dac, dbc), ref):
+        assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1])
+
+
 def test_run_twice_bitwise_deterministic(gpu_lib):
     x = synthetic.tensor((512, 1024), std=1.0, seed=27)
     w = synthetic.tensor((768, 1024), std=0.02, seed=28)
