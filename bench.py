@@ -227,7 +227,7 @@ class Step:
 
 CPU_SAMPLE_SHAPES = {
     # reduced instances of each workload: same laws, fewer rows
-    "ffn": dict(T=128, F=4096),
+    "ffn": dict(T=256, F=6144),
     "attn": dict(T=64),
     "wgrad": dict(T=64),
     "fprop": dict(),
