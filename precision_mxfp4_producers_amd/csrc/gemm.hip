@@ -260,8 +260,13 @@ __device__ __forceinline__ void main_loop_generic(uint8_t* buf0, uint8_t* buf1, 
 // Step it+1 is loaded global -> VGPRs during step it-1 (raw buffer loads),
 // written to its stage during sub-steps 1-2 of step it, and the loads of step
 // it+2 go out right after those writes: each load has about one and a half
-// steps to land.  (Direct global->LDS transfers measured at half this path's
-// throughput on gfx950.)
+// steps to land.  Alternatives measured on one MI355X, in the FFN step: direct
+// global -> LDS transfers (buffer_load ... lds) in this 8-wave loop, about 2%
+// slower per step (3% faster alone on random codes); four waves of 128 x 128
+// (a third less LDS reading, one wave per SIMD), 4-8% slower.  The MFMA pipe
+// is about half busy here; the LDS writes (by either route) and the per-step
+// barrier account for most of the rest: without the writes the same loop
+// takes 217 instead of 307 us on 8192 x 4096 x 14336.
 constexpr int kLdsA = 0, kLdsB = 2 * BM * BKB, kLdsSA = 4 * BM * BKB, kLdsSB = kLdsSA + 2 * BM * 8;
 static_assert(kLdsSB + 2 * BN * 8 == kSmemBytes, "fast path LDS layout");
 
