@@ -29,15 +29,23 @@
  *   - "scales" hold one E8M0 byte per 32 values: value 2^(byte-127).  Bytes
  *     lie in [0, 253]; 0xFF is never written.
  *   - Row-major everywhere; ld* are leading dimensions in ELEMENTS.
- *   - Every blocked dimension must be a positive multiple of 32.  Pointers
- *     must be 16-byte aligned and ld* multiples of 8 (bf16) / 4 (fp32).
+ *   - Every blocked dimension must be a multiple of 32 (the rows of
+ *     fp4_quantize_rows may be any count).  Pointers must be 16-byte aligned
+ *     and ld* multiples of 8 (bf16) / 4 (fp32).
+ *   - Empty calls are valid: a call whose output has no elements returns
+ *     FP4_OK without touching the GPU, and its pointers may be NULL.  An empty
+ *     reduction writes its definition: fp4_gemm with k = 0 sets C to 0 (leaves
+ *     it unchanged when accumulating); fp4_swiglu_producer with d = 0 writes
+ *     a = b = h = +0 and quantizes that h as usual (the H32 view of a zero
+ *     block holds the signed zeros the fixed signs produce).
  *   - Outputs must not alias inputs or each other.
  *   - Inputs must be finite; Inf/NaN inputs give unspecified codes.
  *   - Each call validates its arguments on the host, enqueues its kernels on
  *     `stream` (a hipStream_t; NULL = default stream) and returns without
  *     synchronising.  Results are valid once the stream has reached them.
- *   - Errors: FP4_EINVAL (null pointer or bad enum), FP4_ESHAPE (dimension
- *     not a positive multiple of 32, or ld smaller than the row length),
+ *   - Errors: FP4_EINVAL (null pointer or bad enum), FP4_ESHAPE (negative
+ *     dimension, dimension not a multiple of 32, or ld smaller than the row
+ *     length),
  *     FP4_EALIGN (alignment), FP4_EHIP (launch failed; fp4_last_hip_error()
  *     returns the hipError_t value).  Kernels report no data-dependent errors.
  *     On any error nothing has been enqueued (except after FP4_EHIP, where
@@ -179,8 +187,8 @@ fp4_status fp4_swiglu_backward(int64_t t, int64_t f, const float* dh, int64_t ld
  *   dh [t][lddh] fp32; a_bf16, b_bf16 [t][f]
  *   da_codes, db_codes [t][f/2]; da_scales, db_scales [t][f/32]
  *   dat_codes, dbt_codes [f][t/2]; dat_scales, dbt_scales [f][t/32]
- * Errors: FP4_EINVAL null pointer; FP4_ESHAPE t or f not a multiple of 32,
- * lddh < f; FP4_EALIGN dh, a, b or a code buffer not 16-byte aligned, or lddh
+ * Errors: FP4_EINVAL null pointer; FP4_ESHAPE t or f negative or not a
+ * multiple of 32, lddh < f; FP4_EALIGN dh, a, b or a code buffer not 16-byte aligned, or lddh
  * not a multiple of 4.
  */
 fp4_status fp4_swiglu_backward_producer(int64_t t, int64_t f, const float* dh, int64_t lddh,

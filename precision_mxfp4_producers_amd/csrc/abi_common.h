@@ -12,6 +12,7 @@ extern thread_local int g_last_hip_error;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool mult32(int64_t v) { return v > 0 && (v % 32) == 0; }
+inline bool mult32z(int64_t v) { return v >= 0 && (v % 32) == 0; }   // zero allowed (empty)
 
 inline fp4_status launch_status() {
   hipError_t e = hipGetLastError();

@@ -33,6 +33,8 @@
 // logical chunk hit 16 distinct bank groups.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "abi_common.h"
 #include "mx_device.h"
 
@@ -883,6 +885,14 @@ __global__ __launch_bounds__(kFastThreads) void swiglu_fast_kernel(
                          ht_codes, ht_scales, sign_mask16);
 }
 
+// A contraction with K = 0 (every sum empty) writes zeros; a plain kernel
+// rather than a memset so that the call stays capturable in graphs.
+__global__ __launch_bounds__(256) void fill_rows_f32_kernel(float* __restrict__ c, int64_t m, int64_t n, int64_t ldc) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= n) return;
+  for (int64_t r = blockIdx.y; r < m; r += gridDim.y) c[r * ldc + col] = 0.0f;
+}
+
 }  // namespace mx
 
 using namespace mx;
@@ -892,9 +902,18 @@ extern "C" {
 fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                     const uint8_t* b_codes, const uint8_t* b_scales, float* c, int64_t ldc, int accumulate,
                     void* stream) {
-  if (!a_codes || !a_scales || !b_codes || !b_scales || !c || (accumulate != 0 && accumulate != 1))
-    return FP4_EINVAL;
-  if (!mult32(m) || !mult32(n) || !mult32(k) || ldc < n) return FP4_ESHAPE;
+  if (accumulate != 0 && accumulate != 1) return FP4_EINVAL;
+  if (!mult32z(m) || !mult32z(n) || !mult32z(k) || ldc < n) return FP4_ESHAPE;
+  if (m == 0 || n == 0) return FP4_OK;                    // empty C
+  if (!c) return FP4_EINVAL;
+  if (k == 0) {                                           // empty sums: C = 0, or C unchanged when accumulating
+    if (accumulate) return FP4_OK;
+    const int64_t gy = std::min<int64_t>(m, 65535);
+    hipLaunchKernelGGL(fill_rows_f32_kernel, dim3((unsigned)((n + 255) / 256), (unsigned)gy), dim3(256), 0,
+                       as_stream(stream), c, m, n, ldc);
+    return launch_status();
+  }
+  if (!a_codes || !a_scales || !b_codes || !b_scales) return FP4_EINVAL;
   if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned16(a_scales) || !aligned16(b_scales) ||
       !aligned16(c) || (ldc % 4) != 0)
     return FP4_EALIGN;
@@ -915,10 +934,15 @@ fp4_status fp4_swiglu_producer(int64_t t, int64_t f, int64_t d, const uint8_t* x
                                const uint8_t* w13_codes, const uint8_t* w13_scales, uint16_t* a_bf16,
                                uint16_t* b_bf16, uint8_t* h_codes, uint8_t* h_scales, uint8_t* ht_codes,
                                uint8_t* ht_scales, uint32_t sign_mask16, void* stream) {
-  if (!x_codes || !x_scales || !w13_codes || !w13_scales || !a_bf16 || !b_bf16 || !h_codes || !h_scales)
-    return FP4_EINVAL;
   if ((ht_codes == nullptr) != (ht_scales == nullptr)) return FP4_EINVAL;
-  if (!mult32(t) || !mult32(f) || !mult32(d)) return FP4_ESHAPE;
+  if (!mult32z(t) || !mult32z(f) || !mult32z(d)) return FP4_ESHAPE;
+  if (t == 0 || f == 0) return FP4_OK;                    // empty outputs
+  if (!a_bf16 || !b_bf16 || !h_codes || !h_scales) return FP4_EINVAL;
+  // d = 0 (empty sums) runs the ordinary kernel: its operand loads go through
+  // empty buffer resources and read zero, and the epilogue then produces the
+  // definition (a = b = +0, h = +0; the H32 signs still decide the sign of
+  // each transformed zero)
+  if (d > 0 && (!x_codes || !x_scales || !w13_codes || !w13_scales)) return FP4_EINVAL;
   if (!aligned16(x_codes) || !aligned16(w13_codes) || !aligned16(h_codes) || !aligned16(x_scales) ||
       !aligned16(w13_scales) || !aligned16(a_bf16) || !aligned16(b_bf16) || (ht_codes && !aligned16(ht_codes)))
     return FP4_EALIGN;

@@ -323,8 +323,10 @@ extern "C" {
 fp4_status fp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* codes, uint8_t* scales, int mode, uint64_t seed,
                              uint64_t offset, void* stream) {
-  if (!x || !codes || !scales || (mode != FP4_RTN && mode != FP4_SR)) return FP4_EINVAL;
-  if (rows <= 0 || !mult32(cols) || ldx < cols) return FP4_ESHAPE;
+  if (mode != FP4_RTN && mode != FP4_SR) return FP4_EINVAL;
+  if (rows < 0 || !mult32z(cols) || ldx < cols) return FP4_ESHAPE;
+  if (rows == 0 || cols == 0) return FP4_OK;             // empty: nothing to write
+  if (!x || !codes || !scales) return FP4_EINVAL;
   if (!aligned16(x) || !aligned16(codes) || (ldx % 8) != 0) return FP4_EALIGN;
   const int64_t cpr = cols >> 3;
   const int64_t gx = (cpr + kThreads - 1) / kThreads;
@@ -346,8 +348,10 @@ fp4_status fp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
 fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* codes_t, uint8_t* scales_t, int hadamard,
                              uint32_t sign_mask16, void* stream) {
-  if (!x || !codes_t || !scales_t || (hadamard != 0 && hadamard != 32)) return FP4_EINVAL;
-  if (!mult32(rows) || !mult32(cols) || ldx < cols) return FP4_ESHAPE;
+  if (hadamard != 0 && hadamard != 32) return FP4_EINVAL;
+  if (!mult32z(rows) || !mult32z(cols) || ldx < cols) return FP4_ESHAPE;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (!x || !codes_t || !scales_t) return FP4_EINVAL;
   if (!aligned16(x) || !aligned16(codes_t) || (ldx % 8) != 0) return FP4_EALIGN;
   const int64_t gx = (cols + kColW - 1) / kColW, gy = (rows + kColTok - 1) / kColTok;
   if (gy > kMaxGridY) return FP4_ESHAPE;
@@ -365,9 +369,10 @@ fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int6
 fp4_status fp4_quantize_w2d32(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
                               uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
                               uint8_t* col_scales, float finer_ratio, void* stream) {
-  if (!w || !row_codes || !row_scales || !col_codes || !col_scales) return FP4_EINVAL;
   if (!(finer_ratio >= 0.0f && finer_ratio <= 1.0f)) return FP4_EINVAL;
-  if (!mult32(n) || !mult32(k) || ldw < k) return FP4_ESHAPE;
+  if (!mult32z(n) || !mult32z(k) || ldw < k) return FP4_ESHAPE;
+  if (n == 0 || k == 0) return FP4_OK;
+  if (!w || !row_codes || !row_scales || !col_codes || !col_scales) return FP4_EINVAL;
   if (!aligned16(w) || !aligned16(row_codes) || !aligned16(col_codes) || (ldw % 8) != 0)
     return FP4_EALIGN;
   const int64_t gk = (k + 127) / 128, gy = (n + 127) / 128;

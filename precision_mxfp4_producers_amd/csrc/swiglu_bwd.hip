@@ -230,8 +230,9 @@ using namespace mx;
 extern "C" fp4_status fp4_swiglu_backward(int64_t t, int64_t f, const float* dh, int64_t lddh,
                                           const uint16_t* a_bf16, const uint16_t* b_bf16, uint16_t* da_bf16,
                                           uint16_t* db_bf16, void* stream) {
+  if (!mult32z(t) || !mult32z(f) || lddh < f) return FP4_ESHAPE;
+  if (t == 0 || f == 0) return FP4_OK;
   if (!dh || !a_bf16 || !b_bf16 || !da_bf16 || !db_bf16) return FP4_EINVAL;
-  if (!mult32(t) || !mult32(f) || lddh < f) return FP4_ESHAPE;
   if (!aligned16(dh) || !aligned16(a_bf16) || !aligned16(b_bf16) || !aligned16(da_bf16) || !aligned16(db_bf16) ||
       (lddh % 4) != 0)
     return FP4_EALIGN;
@@ -247,10 +248,11 @@ extern "C" fp4_status fp4_swiglu_backward_producer(
     uint64_t seed, uint64_t offset_a, uint64_t offset_b, uint32_t sign_mask16,
     uint8_t* da_codes, uint8_t* da_scales, uint8_t* db_codes, uint8_t* db_scales,
     uint8_t* dat_codes, uint8_t* dat_scales, uint8_t* dbt_codes, uint8_t* dbt_scales, void* stream) {
+  if (!mult32z(t) || !mult32z(f) || lddh < f) return FP4_ESHAPE;
+  if (t == 0 || f == 0) return FP4_OK;
   if (!dh || !a_bf16 || !b_bf16 || !da_codes || !da_scales || !db_codes || !db_scales || !dat_codes ||
       !dat_scales || !dbt_codes || !dbt_scales)
     return FP4_EINVAL;
-  if (!mult32(t) || !mult32(f) || lddh < f) return FP4_ESHAPE;
   if (!aligned16(dh) || !aligned16(a_bf16) || !aligned16(b_bf16) || !aligned16(da_codes) ||
       !aligned16(db_codes) || !aligned16(dat_codes) || !aligned16(dbt_codes) || (lddh % 4) != 0)
     return FP4_EALIGN;

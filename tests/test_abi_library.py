@@ -79,3 +79,25 @@ def test_argument_errors_are_reported_without_gpu_work():
                                             0, *bufs, None) == 1
     assert lib.fp4_swiglu_backward_producer(32, 32, v(4100), 32, v(4096), v(4096), u64(0), u64(0), u64(1),
                                             0, *bufs, None) == 3
+
+
+def test_empty_calls_are_noops_without_gpu_work():
+    """An output with no elements: FP4_OK, NULL pointers allowed, no device call."""
+    import precision_mxfp4_producers_amd as mx
+    lib = mx.load(LIB)
+    u64 = ctypes.c_uint64
+    assert lib.fp4_quantize_rows(None, 0, 64, 64, None, None, 1, 0, 0, None) == 0
+    assert lib.fp4_quantize_rows(None, 5, 0, 0, None, None, 0, 0, 0, None) == 0
+    assert lib.fp4_quantize_cols(None, 0, 64, 64, None, None, 32, 0, None) == 0
+    assert lib.fp4_quantize_cols(None, 64, 0, 0, None, None, 0, 0, None) == 0
+    assert lib.fp4_quantize_w2d32(None, 0, 64, 64, None, None, None, None, ctypes.c_float(0.87), None) == 0
+    assert lib.fp4_gemm(0, 64, 64, None, None, None, None, None, 64, 0, None) == 0
+    assert lib.fp4_gemm(64, 0, 64, None, None, None, None, None, 0, 1, None) == 0
+    assert lib.fp4_swiglu_producer(0, 64, 64, None, None, None, None, None, None, None, None, None, None, 0, None) == 0
+    assert lib.fp4_swiglu_backward(0, 64, None, 64, None, None, None, None, None) == 0
+    assert lib.fp4_swiglu_backward_producer(64, 0, None, 0, None, None, u64(0), u64(0), u64(1), 0,
+                                            *([None] * 8), None) == 0
+    # negative sizes and bad enums are still rejected
+    assert lib.fp4_quantize_rows(None, -1, 64, 64, None, None, 0, 0, 0, None) == 2
+    assert lib.fp4_quantize_rows(None, 0, 64, 64, None, None, 5, 0, 0, None) == 1
+    assert lib.fp4_gemm(-32, 64, 64, None, None, None, None, None, 64, 0, None) == 2

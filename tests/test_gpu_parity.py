@@ -248,6 +248,55 @@ def test_swiglu_backward_producer(gpu_lib, tf):
         assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1])
 
 
+def test_empty_tensors(gpu_lib):
+    """Empty inputs give empty outputs (no launch)."""
+    x = torch.empty((0, 64), dtype=torch.int16, device="cuda")
+    codes, scales = gpu_lib.fp4_quantize_rows(x, gpu_lib.FP4_SR, 1, 2)
+    assert tuple(codes.shape) == (0, 32) and tuple(scales.shape) == (0, 2)
+    ct, st = gpu_lib.fp4_quantize_cols(torch.empty((0, 64), dtype=torch.int16, device="cuda"), 32, 5)
+    assert tuple(ct.shape) == (64, 0) and tuple(st.shape) == (64, 0)
+    a = torch.empty((0, 32), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((0, 2), dtype=torch.uint8, device="cuda")
+    c = gpu_lib.fp4_gemm(a, sa, a, sa)
+    assert tuple(c.shape) == (0, 0)
+    torch.cuda.synchronize()
+
+
+def test_gemm_k0_is_an_empty_sum(gpu_lib):
+    """K = 0: every element of C is the empty sum 0; accumulating leaves C."""
+    m, n = 96, 160
+    a = torch.empty((m, 0), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((m, 0), dtype=torch.uint8, device="cuda")
+    b = torch.empty((n, 0), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((n, 0), dtype=torch.uint8, device="cuda")
+    c = torch.full((m, n), 7.5, dtype=torch.float32, device="cuda")
+    gpu_lib.fp4_gemm(a, sa, b, sb, c=c, accumulate=True)
+    assert torch.all(c == 7.5)
+    gpu_lib.fp4_gemm(a, sa, b, sb, c=c)
+    ref, e = G.gemm_ref(np.zeros((m, 0), np.uint8), np.zeros((m, 0), np.uint8),
+                        np.zeros((n, 0), np.uint8), np.zeros((n, 0), np.uint8))
+    assert np.array_equal(host(c).astype(np.float64), ref) and not np.any(e)
+
+
+def test_swiglu_producer_d0(gpu_lib):
+    """d = 0: a = b = 0, h = SiLU(0) * 0 = 0, quantized as all-zero blocks."""
+    t, f = 64, 96
+    x = torch.empty((t, 0), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((t, 0), dtype=torch.uint8, device="cuda")
+    w = torch.empty((2 * f, 0), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((2 * f, 0), dtype=torch.uint8, device="cuda")
+    outs = [torch.full(shp, 0x55, dtype=dt, device="cuda") for shp, dt in
+            (((t, f), torch.int16), ((t, f), torch.int16), ((t, f // 2), torch.uint8), ((t, f // 32), torch.uint8),
+             ((f, t // 2), torch.uint8), ((f, t // 32), torch.uint8))]
+    gpu_lib.fp4_swiglu_producer(x, xs, w, ws, P.sign_mask_from_seed(0), True, *outs)
+    zero = np.zeros((t, f), dtype=np.uint16)
+    h = S.swiglu_h(zero, zero)
+    want = Q.quantize_rows(h) + Q.quantize_cols(h, 32, P.sign_mask_from_seed(0))
+    assert np.array_equal(host16(outs[0]), zero) and np.array_equal(host16(outs[1]), zero)
+    for got, wv in zip(outs[2:], want):
+        assert_same(got, wv, "d=0 output")
+
+
 def test_run_twice_bitwise_deterministic(gpu_lib):
     x = synthetic.tensor((512, 1024), std=1.0, seed=27)
     w = synthetic.tensor((768, 1024), std=0.02, seed=28)
