@@ -18,6 +18,7 @@ cpu_baseline times the CPU oracle on a bounded sample of the same step.
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -48,6 +49,8 @@ def parse():
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--unfused-backward", action="store_true",
                    help="FFN step: SwiGLU backward, SR rows and H32 cols of dA/dB as five separate calls")
+    p.add_argument("--quality", action="store_true",
+                   help="numerical quality of the MXFP4 contractions against fp32 on the bf16 inputs, with ablations")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of known size (for scaling HBM byte counters)")
     return p.parse_args()
@@ -306,6 +309,60 @@ def cpu_baseline(step):
             "host_cpus": os.cpu_count()}
 
 
+
+QUALITY_CASES = {
+    # attention-projection laws at full size: X with 0.1% x20 outliers
+    "attn_proj_8192x4096x4096": None,
+    # heavy-tailed laws of the large FFN workload (Student-t3 X, W ~ N(0,0.015),
+    # dY ~ N(0,1e-4) with 1% x50 outliers) on one 8192 x 4096 x 4096 layer
+    "ffn_large_32768x8192x28672": {"X": (8192, 4096), "W1": (4096, 4096), "dY": (8192, 4096)},
+}
+
+
+def quality_report(mx, torch):
+    """Relative L2 error, cosine and bias of each MXFP4 contraction against the
+    fp32 contraction of the same bf16 tensors, with the method's ablations:
+    2D32 weights vs 1x32 blocks, finer 2D32 scale on/off, SR vs RTN for Dgrad,
+    H32 vs none for Wgrad."""
+    import synthetic
+    out = []
+    for name, shapes in QUALITY_CASES.items():
+        h = synthetic.workload(name, shapes=shapes)
+        seed = synthetic.WORKLOADS[name]["seed"]
+        mask = mx.fp4_sign_mask_from_seed(seed)
+        dev = lambda k: torch.from_numpy(h[k].view(np.int16)).cuda()
+        X, dY = dev("X"), dev("dY")
+        W = dev("W" if "W" in h else "W1")
+        f32 = lambda t: t.view(torch.bfloat16).float()
+        refs = {"Fprop": f32(X) @ f32(W).T, "Dgrad": f32(dY) @ f32(W), "Wgrad": f32(dY).T.contiguous() @ f32(X)}
+
+        def score(kind, variant, c):
+            r = refs[kind].double()
+            d = c.double() - r
+            rl2 = (d.norm() / r.norm()).item()
+            out.append({"workload": name, "contraction": kind, "variant": variant, "rel_l2": round(rl2, 6),
+                        "snr_db": round(-20 * math.log10(rl2), 2),
+                        "cosine": round((c.double() * r).sum().item() / (c.double().norm() * r.norm()).item(), 7),
+                        "bias": round((d.mean() / r.pow(2).mean().sqrt()).item(), 7)})
+
+        xr = mx.fp4_quantize_rows(X)
+        for ratio, tag in ((0.87, "2D32, finer rule 0.87"), (0.0, "2D32, finer rule off")):
+            wq = mx.fp4_quantize_w2d32(W, ratio)
+            score("Fprop", tag, mx.fp4_gemm(xr[0], xr[1], wq[0], wq[1]))
+            if ratio:
+                for mode, mtag in ((mx.FP4_SR, "SR"), (mx.FP4_RTN, "RTN")):
+                    dyr = mx.fp4_quantize_rows(dY, mode, seed, 0)
+                    score("Dgrad", f"dY {mtag}, W 2D32 columns", mx.fp4_gemm(dyr[0], dyr[1], wq[2], wq[3]))
+        wr = mx.fp4_quantize_rows(W)
+        score("Fprop", "1x32 weight blocks", mx.fp4_gemm(xr[0], xr[1], wr[0], wr[1]))
+        for had, tag in ((32, "paired fixed-sign H32"), (0, "no Hadamard")):
+            dyc = mx.fp4_quantize_cols(dY, had, mask)
+            xc = mx.fp4_quantize_cols(X, had, mask)
+            score("Wgrad", tag, mx.fp4_gemm(dyc[0], dyc[1], xc[0], xc[1]))
+        del refs
+        torch.cuda.empty_cache()
+    return out
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -321,6 +378,9 @@ def main():
         return
     mx.load()
     torch.cuda.set_device(0)
+    if args.quality:
+        print(json.dumps({"quality": quality_report(mx, torch)}), flush=True)
+        return
     print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
     step = Step(args.workload, args.seed, mx, torch, fused_backward=not args.unfused_backward)
     ncalls = len(step.calls)
