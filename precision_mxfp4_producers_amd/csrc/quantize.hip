@@ -24,7 +24,7 @@ thread_local int g_last_hip_error = 0;
 
 constexpr int kThreads = 256;
 constexpr int kMaxGridY = 65535;
-constexpr int64_t kTargetBlocks = 2048;                  // 8 workgroups per CU
+constexpr int64_t kTargetBlocks = 8192;                  // 32 workgroups per CU
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -35,7 +35,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // is an integer max.  RTN goes through the hardware converter; SR draws
 // Philox words for the lane's 8 elements (two counters).  Each pass of the
 // row loop issues the loads of kRowsPerPass rows before using any of them.
-constexpr int kRowsPerPass = 4;
+constexpr int kRowsPerPass = 2;
 
 template <bool kSR>
 __device__ __forceinline__ uint32_t encode_row_chunk(uint4 v, int e, int64_t r, int64_t cols, int64_t c8,
@@ -93,15 +93,24 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 
 // ------------------------------------------------------------------ cols
 // A workgroup owns kColTok tokens x kColW columns: it loads the bf16 tile
-// row-contiguously (each row segment 128 bytes) into LDS, encodes column pairs
-// from LDS (optional H32 per 32-token block), parks the codes in LDS and
-// writes every column's kColTok/2 code bytes -- one whole 128-byte line -- with
-// coalesced 16-byte stores (16-byte pieces of many lines per store
-// instruction, or pieces of one line from different workgroups, drain at a
-// fraction of the rate).
-constexpr int kColTok = 256, kColW = 64;
+// row-contiguously into LDS, encodes column pairs from LDS (optional H32 per
+// 32-token block), parks the codes in LDS and writes each column's kColTok/2
+// code bytes as one contiguous run with coalesced 16-byte stores (16-byte
+// pieces of many lines per store instruction drain at a fraction of the rate).
+// 128 x 128 measured best among 128-512 tokens x 32-128 columns on one MI355X
+// (it trades whole 128-byte code lines for more workgroups per CU).
+#ifndef MX_COL_TOK
+#define MX_COL_TOK 128
+#endif
+#ifndef MX_COL_W
+#define MX_COL_W 128
+#endif
+constexpr int kColTok = MX_COL_TOK, kColW = MX_COL_W;
+constexpr int kColChunks = kColW / 8;                    // 16-byte chunks per token row
+constexpr int kColRowsPerLoad = kThreads / kColChunks;   // token rows one load instruction round covers
 constexpr int kColPitch = kColW * 2 + 4;                 // bytes per staged token row (+4: spread banks)
 constexpr int kColCodePitch = kColTok / 2 + 16;          // bytes per staged column of codes
+static_assert(kColTok % kColRowsPerLoad == 0 && kColTok % 32 == 0 && kColW % 32 == 0, "column tile shape");
 
 template <bool kH32>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
@@ -115,41 +124,42 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
   const int ntok = (int)min<int64_t>(kColTok, rows - t0);          // multiple of 32
   const int ncol = (int)min<int64_t>(kColW, cols - c0);            // multiple of 32
 
-  // load: thread (row tid/8 + 32 j, 16-byte chunk tid%8); rows past the end are skipped
+  // load: thread (row tid/kColChunks + kColRowsPerLoad j, 16-byte chunk tid%kColChunks)
   {
-    const int ch = tid & 7;
+    constexpr int kJ = kColTok / kColRowsPerLoad;
+    const int ch = tid % kColChunks;
     const bool col_ok = ch * 8 < ncol;
-    uint4 v[8];
+    uint4 v[kJ];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = (tid >> 3) + 32 * j;
+    for (int j = 0; j < kJ; ++j) {
+      const int r = tid / kColChunks + kColRowsPerLoad * j;
       v[j] = make_uint4(0u, 0u, 0u, 0u);
       if (col_ok && r < ntok) v[j] = *reinterpret_cast<const uint4*>(x + (t0 + r) * ldx + c0 + ch * 8);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = (tid >> 3) + 32 * j;
+    for (int j = 0; j < kJ; ++j) {
+      const int r = tid / kColChunks + kColRowsPerLoad * j;
       uint32_t* d = reinterpret_cast<uint32_t*>(tile + r * kColPitch + ch * 16);
       d[0] = v[j].x; d[1] = v[j].y; d[2] = v[j].z; d[3] = v[j].w;
     }
   }
   __syncthreads();
 
-  // encode: thread (column pair tid%32, token block tid/32)
-  {
-    const int cp = tid & 31, tb = tid >> 5;
+  // encode: item (column pair i % (kColW/2), token block i / (kColW/2))
+  for (int i = tid; i < (kColW / 2) * (kColTok / 32); i += kThreads) {
+    const int cp = i % (kColW / 2), tb = i / (kColW / 2);
     if (2 * cp < ncol && 32 * tb < ntok) {
       uint32_t v[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = *reinterpret_cast<const uint32_t*>(tile + (32 * tb + i) * kColPitch + cp * 4);
+      for (int k = 0; k < 32; ++k) v[k] = *reinterpret_cast<const uint32_t*>(tile + (32 * tb + k) * kColPitch + cp * 4);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         float f[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          uint32_t bb = (v[i] >> (16 * c)) & 0xFFFFu;
-          if constexpr (kH32) bb ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;   // d_(i mod 16)
-          f[i] = bf16_bits_to_f32(bb);
+        for (int k = 0; k < 32; ++k) {
+          uint32_t bb = (v[k] >> (16 * c)) & 0xFFFFu;
+          if constexpr (kH32) bb ^= ((sign_mask16 >> (k & 15)) & 1u) << 15;   // d_(k mod 16)
+          f[k] = bf16_bits_to_f32(bb);
         }
         if constexpr (kH32) h32_fp32(f);
         int e;
@@ -161,22 +171,20 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
   }
   __syncthreads();
 
-  // store: 8 threads per column write its ntok/2 code bytes (one line when
-  // ntok == 256); then one thread per column writes its scale bytes
-  {
-    const int piece = tid & 7;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int col = (tid >> 3) + 32 * k;
-      if (col < ncol && piece * 32 < ntok) {
-        const uint4 d = *reinterpret_cast<const uint4*>(ctile + col * kColCodePitch + piece * 16);
-        *reinterpret_cast<uint4*>(codes_t + (c0 + col) * (rows >> 1) + (t0 >> 1) + piece * 16) = d;
-      }
+  // store: consecutive threads cover one column's kColTok/2 code bytes (one
+  // whole 128-byte line when kColTok == 256); then one thread per column
+  // writes its scale bytes
+  constexpr int kPieces = kColTok / 32;                  // 16-byte pieces per column
+  for (int i = tid; i < kColW * kPieces; i += kThreads) {
+    const int col = i / kPieces, piece = i % kPieces;
+    if (col < ncol && piece * 32 < ntok) {
+      const uint4 d = *reinterpret_cast<const uint4*>(ctile + col * kColCodePitch + piece * 16);
+      *reinterpret_cast<uint4*>(codes_t + (c0 + col) * (rows >> 1) + (t0 >> 1) + piece * 16) = d;
     }
-    if (tid < ncol) {
-      uint8_t* dst = scales_t + (c0 + tid) * (rows >> 5) + (t0 >> 5);
-      for (int tb = 0; tb < ntok / 32; ++tb) dst[tb] = stile[tid][tb];
-    }
+  }
+  for (int col = tid; col < ncol; col += kThreads) {
+    uint8_t* dst = scales_t + (c0 + col) * (rows >> 5) + (t0 >> 5);
+    for (int tb = 0; tb < ntok / 32; ++tb) dst[tb] = stile[col][tb];
   }
 }
 
@@ -377,9 +385,9 @@ fp4_status fp4_quantize_w2d32(const uint16_t* w, int64_t n, int64_t k, int64_t l
     return FP4_EALIGN;
   const int64_t gk = (k + 127) / 128, gy = (n + 127) / 128;
   if (gy > kMaxGridY || ldw >= ((int64_t)1 << 22)) return FP4_ESHAPE;   // 128-row strips stay < 2 GiB
-  // about 768 workgroups (3 per CU), each walking a run of consecutive macro
-  // tiles along K
-  const int64_t want_x = std::max<int64_t>(1, 768 / gy);
+  // about 512 workgroups (2 per CU, each long-running), each walking a run of
+  // consecutive macro tiles along K
+  const int64_t want_x = std::max<int64_t>(1, 512 / gy);
   const int per = (int)((gk + want_x - 1) / want_x);
   const int64_t gx = (gk + per - 1) / per;
   hipLaunchKernelGGL(quant_w2d32_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0,
