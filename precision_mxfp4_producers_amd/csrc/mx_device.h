@@ -95,14 +95,16 @@ __device__ __forceinline__ uint32_t rtn8_f32(const float* f, float scale) {
 //   0.5 <= y < 1 q- = 0.5 (code 1), step 0.5: frac * 2^32 = f * 2^9 (yb << 9);
 //   y < 0.5      q- = 0, step 0.5: frac * 2^32 = y * 2^33, rounded up; an
 //                input so small that y is zero or subnormal still has
-//                0 < frac * 2^32 < 1, threshold 1 (`nonzero`).
+//                0 < frac * 2^32 < 1, threshold 1 (`nonzero`: 1 for a
+//                non-zero input, else 0).
 // y <= 6 always (upward scale), so q+ exists.  Branch-free after if-conversion.
-__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u, bool nonzero) {
+__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u, uint32_t nonzero) {   // nonzero: 0 or 1
   const uint32_t yb = __float_as_uint(y);
-  const uint32_t eb = yb >> 23;
-  const uint32_t t_small = max((uint32_t)ceilf(y * 0x1p33f), nonzero ? 1u : 0u);
-  const uint32_t lo = eb >= 127u ? (yb >> 22) - 252u : (eb == 126u ? 1u : 0u);
-  const uint32_t thr = eb >= 127u ? (yb << 10) : (eb == 126u ? (yb << 9) : t_small);
+  const bool big = yb >= 0x3F800000u;                    // y >= 1
+  const bool small = yb < 0x3F000000u;                   // y < 0.5
+  const uint32_t t_small = max((uint32_t)ceilf(y * 0x1p33f), nonzero);
+  const uint32_t thr = small ? t_small : (yb << (big ? 10u : 9u));
+  const uint32_t lo = small ? 0u : (big ? (yb >> 22) - 252u : 1u);
   return lo + (u < thr ? 1u : 0u);
 }
 

@@ -53,7 +53,7 @@ __device__ __forceinline__ uint32_t encode_row_chunk(uint4 v, int e, int64_t r, 
       const uint32_t bits = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
       const uint32_t mag = bits & 0x7FFFu;
       const float y = bf16_bits_to_f32(mag) * inv;       // exact (power-of-two scale)
-      packed |= (e2m1_sr(y, u[i], mag != 0u) | ((bits >> 12) & 8u)) << (4 * i);
+      packed |= (e2m1_sr(y, u[i], min(mag, 1u)) | ((bits >> 12) & 8u)) << (4 * i);
     }
     return packed;
   } else {

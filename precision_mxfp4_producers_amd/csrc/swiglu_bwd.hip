@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_producer_kernel(
             const uint32_t bits = (w[4 * q + (j >> 1)] >> (16 * (j & 1))) & 0xFFFFu;
             const uint32_t mag = bits & 0x7FFFu;
             const float y = bf16_bits_to_f32(mag) * inv;
-            pk |= (e2m1_sr(y, u[j], mag != 0u) | ((bits >> 12) & 8u)) << (4 * j);
+            pk |= (e2m1_sr(y, u[j], min(mag, 1u)) | ((bits >> 12) & 8u)) << (4 * j);
           }
           packed[q] = pk;
         }
