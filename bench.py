@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--unfused-backward", action="store_true",
                    help="FFN step: SwiGLU backward, SR rows and H32 cols of dA/dB as five separate calls")
+    p.add_argument("--eager", action="store_true",
+                   help="time the step as eager launches instead of one captured HIP graph")
     p.add_argument("--quality", action="store_true",
                    help="numerical quality of the MXFP4 contractions against fp32 on the bf16 inputs, with ablations")
     p.add_argument("--copy-calibration", action="store_true",
@@ -389,6 +391,7 @@ def main():
         step.run()
     torch.cuda.synchronize()
 
+    # per-call times: eager steps with HIP events around every call
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(ncalls)]
           for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -399,8 +402,27 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
+    print(f"[bench] {args.steps} eager steps in {total_ms:.2f} ms", file=sys.stderr, flush=True)
+    mode = "eager"
+    if not args.eager:
+        # the step as one captured HIP graph (every call writes preallocated
+        # buffers; no memsets): removes the launch gaps between the calls
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step.run()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            graph.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(stop)
+        mode = "hip graph"
+        print(f"[bench] {args.steps} graph replays in {total_ms:.2f} ms", file=sys.stderr, flush=True)
     ms_per_step = total_ms / args.steps
-    print(f"[bench] {args.steps} steps in {total_ms:.2f} ms", file=sys.stderr, flush=True)
 
     per = []
     for i, (label, kind, units, _, _) in enumerate(step.calls):
@@ -438,6 +460,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "gemm_tflop_per_step": round(flops / 1e12, 3),
                    "swiglu_backward": "unfused" if args.unfused_backward else "fused producer",
+                   "launch": mode,
                    "quantizer_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1) if q_ms > 0 else None,
                    "quantizer_frac_hbm_peak": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if q_ms > 0 else None},
         "roofline": {"bound": "mfma", "kernel": "gemm_fast_kernel", "achieved": round(achieved, 1),
