@@ -115,7 +115,11 @@ class Step:
         self.d = {k: torch.from_numpy(v.view(np.int16)).to(dev) for k, v in self.host.items()}
         self.o = {}
         self.calls = []          # (label, kind, units, fn, algorithmic bytes of a GEMM)
+        self.charge = {}         # contraction label -> producer calls charged to it (each charged once)
         getattr(self, "_build_" + name.split("_")[0])()
+        charged = sorted(q for v in self.charge.values() for q in v)
+        producers = sorted(c[0] for c in self.calls if c[1] == "quant")
+        assert charged == producers, f"every producer call is charged to exactly one contraction: {charged} {producers}"
 
     def e(self, shape, dtype):
         key = len(self.o)
@@ -164,6 +168,7 @@ class Step:
         xr = self.q_rows("rows(X)", self.d["X"])
         wr = self.q_rows("rows(W)", self.d["W"])
         self.gemm("Fprop", xr, wr)
+        self.charge = {"Fprop": ["rows(X)", "rows(W)"]}
 
     def _build_attn(self):                       # attn_proj: Fprop + Dgrad
         xr = self.q_rows("rows(X)", self.d["X"])
@@ -171,11 +176,13 @@ class Step:
         dyr = self.q_rows("rows(dY,SR)", self.d["dY"], 1, 0)
         self.gemm("Fprop", xr, wq[:2])
         self.gemm("Dgrad", dyr, wq[2:])
+        self.charge = {"Fprop": ["rows(X)", "w2d32(W)"], "Dgrad": ["rows(dY,SR)"]}
 
     def _build_wgrad(self):                      # wgrad_h32: paired H32 Wgrad
         dyc = self.q_cols("cols(dY,H32)", self.d["dY"])
         xc = self.q_cols("cols(X,H32)", self.d["X"])
         self.gemm("Wgrad", dyc, xc)
+        self.charge = {"Wgrad": ["cols(dY,H32)", "cols(X,H32)"]}
 
     def _build_ffn(self):                        # full SwiGLU FFN step
         torch, mx = self.torch, self.mx
@@ -217,6 +224,16 @@ class Step:
         self.gemm("W3 Dgrad (+=)", dbr, w3[2:], c=dx, accumulate=True)
         self.gemm("W1 Wgrad", dac, xc)
         self.gemm("W3 Wgrad", dbc, xc)
+        # each producer is charged to the first contraction that reads it
+        self.charge = {"swiglu_producer": ["rows(X)", "w2d32(W1)", "w2d32(W3)"], "W2 Fprop": ["w2d32(W2)"],
+                       "W2 Dgrad": ["rows(dY,SR)"], "W2 Wgrad": ["cols(dY,H32)"], "W1 Wgrad": ["cols(X,H32)"]}
+        if self.fused_backward:
+            self.charge["W1 Dgrad"] = ["swiglu_bwd_producer"]
+        else:
+            self.charge["W1 Dgrad"] = ["swiglu_backward", "rows(dA,SR)"]
+            self.charge["W3 Dgrad (+=)"] = ["rows(dB,SR)"]
+            self.charge["W1 Wgrad"] += ["cols(dA,H32)"]
+            self.charge["W3 Wgrad"] = ["cols(dB,H32)"]
 
     def run(self, events=None):
         for i, (_, _, _, fn, _) in enumerate(self.calls):
@@ -436,6 +453,17 @@ def main():
             entry["frac_hbm_peak"] = round(units / ms / 1e6 / PEAK_HBM_GBPS, 4)
         per.append(entry)
 
+    # quantize+GEMM TFLOP/s per contraction: 2MNK over the contraction's time
+    # plus that of the producer calls charged to it
+    ms_of = {e["call"]: e["ms"] for e in per}
+    contractions = []
+    for label, kind, units, _, _ in step.calls:
+        if kind not in ("gemm", "producer"):
+            continue
+        prod_ms = sum(ms_of[p] for p in step.charge.get(label, []))
+        contractions.append({"contraction": label, "tflop": round(units / 1e12, 4), "gemm_ms": ms_of[label],
+                             "producers": step.charge.get(label, []), "producer_ms": round(prod_ms, 4),
+                             "quantize_gemm_tflops": round(units / ((ms_of[label] + prod_ms) * 1e-3) / 1e12, 1)})
     flops = step.gemm_flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_ms = sum(e["ms"] for e, c in zip(per, step.calls) if c[1] == "gemm")
@@ -469,6 +497,7 @@ def main():
                      "algorithmic_bytes_per_launch": round(gemm_alg_bytes / max(1, n_gemm)),
                      "launches_per_step": n_gemm},
         "breakdown": per,
+        "contractions": contractions,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
