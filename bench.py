@@ -1,13 +1,16 @@
 """Benchmark of the MXFP4 producer + block-scaled E2M1 GEMM hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--eager] [--unfused-backward] [--quality] [--copy-calibration]
 
 A step is one pass of the whole hot path over one batch of synthetic input.
 The default workload is the full Llama-3-8B SwiGLU FFN step (T 8192, D 4096,
 F 14336): forward (row quantize X, 2D32 W1/W3/W2, fused SwiGLU producer emitting
 h row- and column-facing, W2 Fprop) and backward (row-SR and column-H32 dY, W2
-Dgrad and Wgrad, SwiGLU backward, row-SR and column-H32 dA/dB, column-H32 X,
-W1/W3 Dgrad with accumulation, W1/W3 Wgrad): nine contractions, 8.66 TFLOP.
+Dgrad and Wgrad, the fused SwiGLU backward producer emitting dA/dB row-SR and
+column-H32, column-H32 X, W1/W3 Dgrad with accumulation, W1/W3 Wgrad stacked
+into one launch): nine contractions, 8.66 TFLOP, timed as one captured HIP
+graph (per-call times come from eager steps with events around every call).
 
 Prints one JSON line.  `value` = GEMM FLOPs of the step / step time (the
 "quantize+GEMM TFLOP/s": producer time is inside the step).  Timing uses HIP
@@ -137,9 +140,9 @@ class Step:
                            lambda: mx.fp4_quantize_rows(x, mode, self.seed, offset, codes=out[0], scales=out[1]), 0))
         return out
 
-    def q_cols(self, label, x):
+    def q_cols(self, label, x, out=None):
         mx, (R, C) = self.mx, x.shape
-        out = (self.u8(C, R // 2), self.u8(C, R // 32))
+        out = out if out is not None else (self.u8(C, R // 2), self.u8(C, R // 32))
         self.calls.append((label, "quant", R * C * B_SINGLE,
                            lambda: mx.fp4_quantize_cols(x, 32, self.mask, codes_t=out[0], scales_t=out[1]), 0))
         return out
@@ -205,10 +208,16 @@ class Step:
         dyc = self.q_cols("cols(dY,H32)", dY)
         dh = self.gemm("W2 Dgrad", dyr, w2[2:])
         self.gemm("W2 Wgrad", dyc, hc)
+        # column-facing dA and dB land in one stacked [2F][T/2] buffer, so that
+        # the W1 and W3 Wgrads (same B operand, X column-facing) run as one
+        # contraction with M = 2F: 2x896 256x256 tiles (3.5 rounds of 256 CUs
+        # each) become 1792 (7 full rounds)
+        dabc = (self.u8(2 * F, T // 2), self.u8(2 * F, T // 32))
+        dac, dbc = (dabc[0][:F], dabc[1][:F]), (dabc[0][F:], dabc[1][F:])
         if self.fused_backward:
-            shapes = [(T, F // 2), (T, F // 32)] * 2 + [(F, T // 2), (F, T // 32)] * 2
-            outs = [self.u8(*shp) for shp in shapes]
-            dar, dbr, dac, dbc = (outs[0], outs[1]), (outs[2], outs[3]), (outs[4], outs[5]), (outs[6], outs[7])
+            shapes = [(T, F // 2), (T, F // 32)] * 2
+            outs = [self.u8(*shp) for shp in shapes] + [dac[0], dac[1], dbc[0], dbc[1]]
+            dar, dbr = (outs[0], outs[1]), (outs[2], outs[3])
             self.calls.append(("swiglu_bwd_producer", "quant", T * F * B_BWD_PRODUCER,
                                lambda: mx.fp4_swiglu_backward_producer(dh, a, b, self.seed, 1, 2, self.mask, outs), 0))
         else:
@@ -217,23 +226,21 @@ class Step:
                                lambda: mx.fp4_swiglu_backward(dh, a, b, da, db), 0))
             dar = self.q_rows("rows(dA,SR)", da, 1, 1)
             dbr = self.q_rows("rows(dB,SR)", db, 1, 2)
-            dac = self.q_cols("cols(dA,H32)", da)
-            dbc = self.q_cols("cols(dB,H32)", db)
+            self.q_cols("cols(dA,H32)", da, out=dac)
+            self.q_cols("cols(dB,H32)", db, out=dbc)
         xc = self.q_cols("cols(X,H32)", X)
         dx = self.gemm("W1 Dgrad", dar, w1[2:])
         self.gemm("W3 Dgrad (+=)", dbr, w3[2:], c=dx, accumulate=True)
-        self.gemm("W1 Wgrad", dac, xc)
-        self.gemm("W3 Wgrad", dbc, xc)
+        self.gemm("W1|W3 Wgrad", dabc, xc)
         # each producer is charged to the first contraction that reads it
         self.charge = {"swiglu_producer": ["rows(X)", "w2d32(W1)", "w2d32(W3)"], "W2 Fprop": ["w2d32(W2)"],
-                       "W2 Dgrad": ["rows(dY,SR)"], "W2 Wgrad": ["cols(dY,H32)"], "W1 Wgrad": ["cols(X,H32)"]}
+                       "W2 Dgrad": ["rows(dY,SR)"], "W2 Wgrad": ["cols(dY,H32)"], "W1|W3 Wgrad": ["cols(X,H32)"]}
         if self.fused_backward:
             self.charge["W1 Dgrad"] = ["swiglu_bwd_producer"]
         else:
             self.charge["W1 Dgrad"] = ["swiglu_backward", "rows(dA,SR)"]
             self.charge["W3 Dgrad (+=)"] = ["rows(dB,SR)"]
-            self.charge["W1 Wgrad"] += ["cols(dA,H32)"]
-            self.charge["W3 Wgrad"] = ["cols(dB,H32)"]
+            self.charge["W1|W3 Wgrad"] += ["cols(dA,H32)", "cols(dB,H32)"]
 
     def run(self, events=None):
         for i, (_, _, _, fn, _) in enumerate(self.calls):

@@ -246,3 +246,6 @@ def test_ffn_step(gpu_lib, name):
                c_prev=lambda ms_, ns_: host(cols_of(rows_of(dx_first, ms_), ns_)))
     check_gemm(dw1, dac, xc, rng, "W1 Wgrad")
     check_gemm(dw3, dbc, xc, rng, "W3 Wgrad")
+    # the two Wgrads stacked into one contraction (M = 2F) give the same bytes
+    stacked = gpu_lib.fp4_gemm(torch.cat([dac[0], dbc[0]]), torch.cat([dac[1], dbc[1]]), xc[0], xc[1])
+    assert torch.equal(stacked[:Fw], dw1) and torch.equal(stacked[Fw:], dw3), "stacked Wgrad"
