@@ -70,9 +70,10 @@ def gemm_source_hash():
     return hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, launches):
     """HBM bytes per gemm_fast_kernel launch from the committed counter summary,
-    if it was taken on this workload with the current kernel source; else None."""
+    if it was taken on this workload, with the same launches per step and the
+    current kernel source; else None."""
     if not os.path.exists(TRAFFIC_SUMMARY):
         return None
     fields = {}
@@ -80,7 +81,8 @@ def measured_traffic(workload):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    if fields.get("gemm.hip sha256 (first 16 hex)") != gemm_source_hash() or fields.get("workload") != workload:
+    if (fields.get("gemm.hip sha256 (first 16 hex)") != gemm_source_hash() or fields.get("workload") != workload
+            or fields.get("gemm launches per step") != str(launches)):
         return None
     try:
         return float(fields["hbm bytes per launch (calibrated)"])
@@ -500,7 +502,7 @@ def main():
                    "quantizer_frac_hbm_peak": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if q_ms > 0 else None},
         "roofline": {"bound": "mfma", "kernel": "gemm_fast_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MXFP4_TFLOPS, 4),
-                     "traffic": measured_traffic(args.workload),
+                     "traffic": measured_traffic(args.workload, n_gemm),
                      "algorithmic_bytes_per_launch": round(gemm_alg_bytes / max(1, n_gemm)),
                      "launches_per_step": n_gemm},
         "breakdown": per,
