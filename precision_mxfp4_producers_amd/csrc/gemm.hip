@@ -24,10 +24,10 @@
 // Two main loops:
 //   generic  (any K multiple of 32): 4 waves of 128x128, global -> registers
 //            -> LDS with per-chunk predicates.
-//   fast     (K % 256 == 0): 8 waves of 128x64, two per SIMD so one wave's
-//            waits are covered by the other's MFMAs; raw buffer loads (rows
-//            beyond M/N read as zero), LDS writes and loads software-pipelined
-//            under the MFMAs, fragments read one sub-step ahead.
+//   fast     (K % 256 == 0): 8 waves of 128x64, two per SIMD taking turns:
+//            one issues a half step of MFMAs while the other reads its next
+//            fragments, writes staged registers to LDS and issues raw buffer
+//            loads (rows beyond M/N read as zero).
 // Both stage tiles through the same LDS layout family: 128-byte rows whose
 // 16-byte chunks are XOR-swizzled so that 16 consecutive rows read at one
 // logical chunk hit 16 distinct bank groups.
@@ -257,18 +257,46 @@ __device__ __forceinline__ void main_loop_generic(uint8_t* buf0, uint8_t* buf1, 
 
 
 // ------------------------------------------------------------------ fast main loop
-// LDS layout, stage-major per operand (the stage is an immediate offset):
+// K % 256 == 0.  LDS holds two K-256 stages, stage-major per operand:
 //   A[2] 32 KB each (256 rows x 128 B) | B[2] | SA[2] 2 KB (256 rows x 8 B) | SB[2]
-// Step it+1 is loaded global -> VGPRs during step it-1 (raw buffer loads),
-// written to its stage during sub-steps 1-2 of step it, and the loads of step
-// it+2 go out right after those writes: each load has about one and a half
-// steps to land.  Alternatives measured on one MI355X, in the FFN step: direct
-// global -> LDS transfers (buffer_load ... lds) in this 8-wave loop, about 2%
-// slower per step (3% faster alone on random codes); four waves of 128 x 128
-// (a third less LDS reading, one wave per SIMD), 4-8% slower.  The MFMA pipe
-// is about half busy here; the LDS writes (by either route) and the per-step
-// barrier account for most of the rest: without the writes the same loop
-// takes 217 instead of 307 us on 8192 x 4096 x 14336.
+// The two waves on a SIMD (w and w + 4) take turns: while one issues the 16
+// MFMAs of a half K step (two 64-deep sub-steps) back to back, the other does
+// its memory work -- reads its fragments for its next half step, writes its
+// share of a later stage from registers to LDS, and issues the global loads of
+// the stage after that.  Group 0 (waves 0-3, tile rows 0-127) computes in the
+// even phases of the global numbering, group 1 (rows 128-255) in the odd ones.
+// Per K step s (phases 4s .. 4s+3) and wave, its share of a stage is an A part
+// (4 code loads) and a B part (4 code loads + its scale rows):
+//   phase  group 0                               group 1
+//   4s     half 0 of s                           frags half 0 of s; write A of s+1; load A of s+2
+//   4s+1   frags half 1 of s; write B of s+1;    half 0 of s
+//          load B of s+2
+//   4s+2   half 1 of s                           frags half 1 of s; write B of s+1; load B of s+2
+//   4s+3   frags half 0 of s+1; write A of s+2;  half 1 of s
+//          load A of s+3
+// One workgroup barrier per K step, at the end of phase 4s+2, covers every
+// LDS hazard: stage s+1 is written in phases 4s-1 .. 4s+2 and first read in
+// 4s+3; stage s (the buffer that A of s+2 overwrites in 4s+3) is last read in
+// 4s+2; stage s-1 (the buffer of s+1) is last read in 4s-2, before the
+// previous barrier.  The barrier also pulls the groups back into opposite
+// phases once per step.  A part is loaded four phases before it is written;
+// loads past the last step are clamped to it and land in a buffer nobody reads
+// again.
+//
+// Measured alternatives (one MI355X, 8192 x 4096 x 14336, random codes):
+//   - the same schedule with a barrier at every phase end: 293 us; every
+//     other phase: 283 us; once per step (this loop): 273 us;
+//   - all eight waves interleaving fragment reads, LDS writes and MFMAs in
+//     one instruction stream with a barrier per step: 300-324 us;
+//   - direct global -> LDS transfers (buffer_load ... lds) into four K-128
+//     stages, which frees the staging registers and the LDS write
+//     instructions: 365 us (the transfers run at about half the rate of
+//     register-staged loads);
+//   - four waves of 128 x 128 (one per SIMD): 4-8% slower than the
+//     interleaved eight-wave loop.
+// Ablations of this loop: without the global loads 251 us, without the LDS
+// writes 225 us, with all-zero operands (less power, higher clock) 209 us; the
+// MFMA pipe itself sustains about 5.6 PFLOP/s on random FP4 data.
 constexpr int kLdsA = 0, kLdsB = 2 * BM * BKB, kLdsSA = 4 * BM * BKB, kLdsSB = kLdsSA + 2 * BM * 8;
 static_assert(kLdsSB + 2 * BN * 8 == kSmemBytes, "fast path LDS layout");
 
@@ -282,11 +310,6 @@ struct FastPlan {
   uint32_t ldb8;                       // 8 code rows (bytes)
   uint32_t wa0, wa1;                   // lane LDS offsets (even / odd j) of its code chunk
   uint32_t ws;                         // lane LDS offset of its scale row (stage 0)
-};
-
-struct Staged8 {
-  v4i a[4], b[4];
-  uint2 s;
 };
 
 // Wave w loads code rows 32w..32w+31 of both tiles (load j: rows 32w + 8j +
@@ -337,83 +360,12 @@ __device__ __forceinline__ void make_fast_plan(FastPlan& p, const Operand& A, co
   p.wa1 = (uint32_t)(row0 * BKB + ((c ^ (l >> 3) ^ 1) * 16));
 }
 
-// Loads of K step `kit` into registers (the caller clamps kit to the last step,
-// which keeps the loop branch-free: a re-loaded last step is never read).
-__device__ __forceinline__ void load_step8(const FastPlan& p, int kit, Staged8& st) {
-  const uint32_t so = (uint32_t)kit * BKB, sso = (uint32_t)kit * 8u;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    st.a[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(p.ra, p.va + (uint32_t)j * p.ldb8, so, 0));
-    st.b[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(p.rb, p.vb + (uint32_t)j * p.ldb8, so, 0));
-  }
-  st.s = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(p.rs, p.vs, sso, 0));
-}
-
-// Write half H (loads 2H, 2H+1; H = 1 adds the scale row) into stage `stg`.
-template <int H>
-__device__ __forceinline__ void write_half8(uint8_t* smem, const FastPlan& p, uint32_t stg, const Staged8& st) {
-#pragma unroll
-  for (int j = 2 * H; j < 2 * H + 2; ++j) {
-    const uint32_t off = ((j & 1) ? p.wa1 : p.wa0) + (uint32_t)j * 1024u + stg * (BM * BKB);
-    *reinterpret_cast<v4i*>(smem + kLdsA + off) = st.a[j];
-    *reinterpret_cast<v4i*>(smem + kLdsB + off) = st.b[j];
-  }
-  if constexpr (H == 1) *reinterpret_cast<uint2*>(smem + p.ws + stg * (BM * 8)) = st.s;
-}
-
 struct Frags8 {
   v4i a[4], b[2];
 };
 
-// Lane-constant LDS offsets of this wave's fragments for sub-step s and of its
-// scale dwords (stage 0).  Wave (wm, wn) = (w / 4, w % 4) computes tokens
-// wm*128.. against B rows wn*64.. (GEMM: columns wn*64 .. +63) or against W1
-// rows wn*32.. and W3 rows 128 + wn*32.. (SwiGLU: a and b of FFN columns
-// wn*32 .. +31).
-struct FragAddr8 {
-  uint32_t a[4], b[4];
-  uint32_t sa, sb;
-};
-
 template <bool kSwiGLU>
 __device__ __forceinline__ constexpr int bsub8(int j) { return kSwiGLU ? 128 * j : 32 * j; }
-
-template <bool kSwiGLU>
-__device__ __forceinline__ void make_frag_addr8(FragAddr8& fa, int wm, int wn, int r, int h) {
-  const int g = (r & 7) ^ ((r >> 3) & 1);               // swizzle of rows r + 32k
-  const int x = (4 * h) ^ g;
-  const int arow = wm * 128 + r;
-  const int brow = (kSwiGLU ? wn * 32 : wn * 64) + r;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    fa.a[s] = (uint32_t)(kLdsA + arow * BKB + ((x ^ s) * 16));
-    fa.b[s] = (uint32_t)(kLdsB + brow * BKB + ((x ^ s) * 16));
-  }
-  fa.sa = (uint32_t)(kLdsSA + (2 * arow + h) * 4);
-  fa.sb = (uint32_t)(kLdsSB + (2 * brow + h) * 4);
-}
-
-template <bool kSwiGLU>
-__device__ __forceinline__ void read_frags8(const uint8_t* smem, const FragAddr8& fa, Frags8& fr, int s,
-                                            uint32_t stg) {
-  const uint8_t* pa = smem + (fa.a[s] + stg * (BM * BKB));
-  const uint8_t* pb = smem + (fa.b[s] + stg * (BN * BKB));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) fr.a[i] = *reinterpret_cast<const v4i*>(pa + i * 32 * BKB);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) fr.b[j] = *reinterpret_cast<const v4i*>(pb + bsub8<kSwiGLU>(j) * BKB);
-}
-
-template <bool kSwiGLU>
-__device__ __forceinline__ void read_scales8(const uint8_t* smem, const FragAddr8& fa, uint32_t (&sa)[4],
-                                             uint32_t (&sb)[2], uint32_t stg) {
-  const uint8_t* pa = smem + (fa.sa + stg * (BM * 8));
-  const uint8_t* pb = smem + (fa.sb + stg * (BN * 8));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(pa + i * 32 * 8);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(pb + bsub8<kSwiGLU>(j) * 8);
-}
 
 template <int S, int I0, int I1>
 __device__ __forceinline__ void mfma8(const Frags8& fr, const uint32_t (&sa)[4], const uint32_t (&sb)[2],
@@ -434,49 +386,131 @@ __device__ __forceinline__ void mfma8(const Frags8& fr, const uint32_t (&sa)[4],
     for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
-// One K step on stage it&1 (its sub-step 0 fragments and scales already in
-// registers; `st` holds step it+1).
+struct PartA {
+  v4i a[4];
+};
+struct PartB {
+  v4i b[4];
+  uint2 s;
+};
+
+// Load j of a part reads 8 rows further down.  The row offset stays in the
+// lane offset: the buffer range check (rows past the operand read zero) covers
+// the lane offset, not the scalar one, which carries only the K position.
+__device__ __forceinline__ void load_part_a(const FastPlan& p, int kit, PartA& x) {
+  const uint32_t so = (uint32_t)kit * BKB;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    x.a[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(p.ra, p.va + (uint32_t)j * p.ldb8, so, 0));
+}
+
+__device__ __forceinline__ void load_part_b(const FastPlan& p, int kit, PartB& x) {
+  const uint32_t so = (uint32_t)kit * BKB, sso = (uint32_t)kit * 8u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    x.b[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(p.rb, p.vb + (uint32_t)j * p.ldb8, so, 0));
+  x.s = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(p.rs, p.vs, sso, 0));
+}
+
+// Stage `stg` (0 or 1, wave-uniform) of the part: 32 KB per code stage, 2 KB
+// per scale stage.
+__device__ __forceinline__ void write_part_a(uint8_t* smem, const FastPlan& p, uint32_t stg, const PartA& x) {
+  uint8_t* b0 = smem + (p.wa0 + (stg << 15));
+  uint8_t* b1 = smem + (p.wa1 + (stg << 15));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(((j & 1) ? b1 : b0) + (kLdsA + j * 1024)) = x.a[j];
+}
+
+__device__ __forceinline__ void write_part_b(uint8_t* smem, const FastPlan& p, uint32_t stg, const PartB& x) {
+  uint8_t* b0 = smem + (p.wa0 + (stg << 15));
+  uint8_t* b1 = smem + (p.wa1 + (stg << 15));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(((j & 1) ? b1 : b0) + (kLdsB + j * 1024)) = x.b[j];
+  *reinterpret_cast<uint2*>(smem + (p.ws + (stg << 11))) = x.s;
+}
+
+// Fragment addresses without per-sub-step registers: the chunk swizzle only
+// touches address bits 4-6 and the sub-step XORs bits 4-5, so sub-step s of a
+// fragment is its sub-step 0 address XOR 16 s; stage 1 sets bit 15 (codes) or
+// bit 11 (scales), which no stage-0 address has set.
+struct PPAddr {
+  uint32_t a, b;      // sub-step 0, stage 0 byte address of this lane's first A and B fragment rows
+  uint32_t sa, sb;    // scale dwords, stage 0
+};
+
 template <bool kSwiGLU>
-__device__ __forceinline__ void fast_step(uint8_t* smem, const FastPlan& p, const FragAddr8& fa, int it, int nk,
-                                          Staged8& st, Frags8& f0, Frags8& f1, uint32_t (&sa)[4], uint32_t (&sb)[2],
-                                          v16f (&acc)[4][2]) {
-  const uint32_t cur = (uint32_t)(it & 1), nxt = cur ^ 1u;
-  read_frags8<kSwiGLU>(smem, fa, f1, 1, cur);
-  mfma8<0, 0, 4>(f0, sa, sb, acc);
-  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);    // DS read
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);    // MFMA
+__device__ __forceinline__ void make_pp_addr(PPAddr& q, int wm, int wn, int r, int h) {
+  const int g = (r & 7) ^ ((r >> 3) & 1);
+  const int x = (4 * h) ^ g;
+  const int arow = wm * 128 + r;
+  const int brow = (kSwiGLU ? wn * 32 : wn * 64) + r;
+  q.a = (uint32_t)(kLdsA + arow * BKB + x * 16);
+  q.b = (uint32_t)(kLdsB + brow * BKB + x * 16);
+  q.sa = (uint32_t)(kLdsSA + (2 * arow + h) * 4);
+  q.sb = (uint32_t)(kLdsSB + (2 * brow + h) * 4);
+}
+
+template <bool kSwiGLU, int S>
+__device__ __forceinline__ void pp_read_frags(const uint8_t* smem, const PPAddr& q, uint32_t stg, Frags8& fr) {
+  const uint8_t* pa = smem + ((q.a ^ (uint32_t)(16 * S)) | (stg << 15));
+  const uint8_t* pb = smem + ((q.b ^ (uint32_t)(16 * S)) | (stg << 15));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fr.a[i] = *reinterpret_cast<const v4i*>(pa + i * 32 * BKB);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fr.b[j] = *reinterpret_cast<const v4i*>(pb + bsub8<kSwiGLU>(j) * BKB);
+}
+
+template <bool kSwiGLU>
+__device__ __forceinline__ void pp_read_scales(const uint8_t* smem, const PPAddr& q, uint32_t stg, uint32_t (&sa)[4],
+                                               uint32_t (&sb)[2]) {
+  const uint8_t* pa = smem + (q.sa | (stg << 11));
+  const uint8_t* pb = smem + (q.sb | (stg << 11));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(pa + i * 32 * 8);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(pb + bsub8<kSwiGLU>(j) * 8);
+}
+
+// Phase ends.  pp_sync: this wave's LDS traffic has landed, then the
+// workgroup barrier; pp_next: no synchronisation, only an ordering fence
+// (MFMAs are pure, and the optimizer would otherwise move them across phases).
+__device__ __forceinline__ void pp_sync() {
   __builtin_amdgcn_sched_barrier(0);
-  read_frags8<kSwiGLU>(smem, fa, f0, 2, cur);
-  write_half8<0>(smem, p, nxt, st);
-  mfma8<1, 0, 4>(f1, sa, sb, acc);
-  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-  __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);    // DS write
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags8<kSwiGLU>(smem, fa, f1, 3, cur);
-  write_half8<1>(smem, p, nxt, st);
-  load_step8(p, min(it + 2, nk - 1), st);
-  mfma8<2, 0, 4>(f0, sa, sb, acc);
-  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-  __builtin_amdgcn_sched_group_barrier(0x200, 5, 0);
-  __builtin_amdgcn_sched_group_barrier(0x020, 9, 0);    // VMEM read
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  mfma8<3, 0, 2>(f1, sa, sb, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  // every wave has written step it+1 and finished reading step it
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  uint32_t sa_n[4], sb_n[2];
-  read_frags8<kSwiGLU>(smem, fa, f0, 0, nxt);            // harmless past the last step
-  read_scales8<kSwiGLU>(smem, fa, sa_n, sb_n, nxt);
-  mfma8<3, 2, 4>(f1, sa, sb, acc);
+}
+
+__device__ __forceinline__ void pp_next() { __builtin_amdgcn_sched_barrier(0); }
+
+template <int H, bool kSync>
+__device__ __forceinline__ void pp_compute(const Frags8& f0, const Frags8& f1, const uint32_t (&sa)[4],
+                                           const uint32_t (&sb)[2], v16f (&acc)[4][2]) {
+  mfma8<2 * H, 0, 4>(f0, sa, sb, acc);
+  mfma8<2 * H + 1, 0, 4>(f1, sa, sb, acc);
+  if constexpr (kSync) pp_sync();
+  else pp_next();
+}
+
+// Memory work of a phase: fragments of half H of stage `frs` (for H = 0 also
+// the stage's scale dwords), one part written to stage `wst`, the same part of
+// K step `lkit` loaded.
+template <bool kSwiGLU, int H, bool kPartA, bool kSync>
+__device__ __forceinline__ void pp_memory(uint8_t* smem, const FastPlan& p, const PPAddr& q, uint32_t frs,
+                                          uint32_t wst, int lkit, Frags8& f0, Frags8& f1, uint32_t (&sa)[4],
+                                          uint32_t (&sb)[2], PartA& xa, PartB& xb) {
+  pp_read_frags<kSwiGLU, 2 * H>(smem, q, frs, f0);
+  pp_read_frags<kSwiGLU, 2 * H + 1>(smem, q, frs, f1);
+  if constexpr (H == 0) pp_read_scales<kSwiGLU>(smem, q, frs, sa, sb);
+  // the part's registers are written out before they are loaded again: kept
+  // in this order, one set of staging registers per part suffices
+  if constexpr (kPartA) write_part_a(smem, p, wst, xa);
+  else write_part_b(smem, p, wst, xb);
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) sa[i] = sa_n[i];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) sb[j] = sb_n[j];
+  if constexpr (kPartA) load_part_a(p, lkit, xa);
+  else load_part_b(p, lkit, xb);
+  if constexpr (kSync) pp_sync();
+  else pp_next();
 }
 
 template <bool kSwiGLU>
@@ -489,23 +523,50 @@ __device__ __forceinline__ void main_loop_fast(uint8_t* smem, const Operand& A, 
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
   const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
-  const int nk = (int)(K / 256);
+  const int nk = (int)(K / 256), last = nk - 1;
   FastPlan p;
   make_fast_plan<kSwiGLU>(p, A, B, m0, n0, f, K);
-  FragAddr8 fa;
-  make_frag_addr8<kSwiGLU>(fa, wm, wn, r, h);
-  Staged8 st;
-  load_step8(p, 0, st);
-  write_half8<0>(smem, p, 0u, st);
-  write_half8<1>(smem, p, 0u, st);
-  load_step8(p, min(1, nk - 1), st);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-  __builtin_amdgcn_s_barrier();
+  PPAddr q;
+  make_pp_addr<kSwiGLU>(q, wm, wn, r, h);
+  PartA xa;
+  PartB xb;
   Frags8 f0, f1;
   uint32_t sa[4], sb[2];
-  read_frags8<kSwiGLU>(smem, fa, f0, 0, 0u);
-  read_scales8<kSwiGLU>(smem, fa, sa, sb, 0u);
-  for (int it = 0; it < nk; ++it) fast_step<kSwiGLU>(smem, p, fa, it, nk, st, f0, f1, sa, sb, acc);
+  // every wave: stage 0 whole, then its stage-1 parts in registers
+  load_part_a(p, 0, xa);
+  load_part_b(p, 0, xb);
+  write_part_a(smem, p, 0u, xa);
+  write_part_b(smem, p, 0u, xb);
+  __builtin_amdgcn_sched_barrier(0);
+  load_part_a(p, min(1, last), xa);
+  load_part_b(p, min(1, last), xb);
+  if (__builtin_amdgcn_readfirstlane(wm) == 0) {
+    // group 0 writes its A part of stage 1 now (its phase 4s-1 for s = 0),
+    // loads A of stage 2, and reads its first fragments after the barrier
+    write_part_a(smem, p, 1u, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    load_part_a(p, min(2, last), xa);
+    pp_sync();
+    pp_read_frags<kSwiGLU, 0>(smem, q, 0u, f0);
+    pp_read_frags<kSwiGLU, 1>(smem, q, 0u, f1);
+    pp_read_scales<kSwiGLU>(smem, q, 0u, sa, sb);
+    for (int s = 0; s < nk; ++s) {
+      const uint32_t cur = (uint32_t)(s & 1), nxt = cur ^ 1u;
+      pp_compute<0, false>(f0, f1, sa, sb, acc);
+      pp_memory<kSwiGLU, 1, false, false>(smem, p, q, cur, nxt, min(s + 2, last), f0, f1, sa, sb, xa, xb);
+      pp_compute<1, true>(f0, f1, sa, sb, acc);
+      pp_memory<kSwiGLU, 0, true, false>(smem, p, q, nxt, cur, min(s + 3, last), f0, f1, sa, sb, xa, xb);
+    }
+  } else {
+    pp_sync();
+    for (int s = 0; s < nk; ++s) {
+      const uint32_t cur = (uint32_t)(s & 1), nxt = cur ^ 1u;
+      pp_memory<kSwiGLU, 0, true, false>(smem, p, q, cur, nxt, min(s + 2, last), f0, f1, sa, sb, xa, xb);
+      pp_compute<0, false>(f0, f1, sa, sb, acc);
+      pp_memory<kSwiGLU, 1, false, true>(smem, p, q, cur, nxt, min(s + 2, last), f0, f1, sa, sb, xa, xb);
+      pp_compute<1, false>(f0, f1, sa, sb, acc);
+    }
+  }
   __syncthreads();
 }
 
