@@ -8,8 +8,8 @@ The default workload is the full Llama-3-8B SwiGLU FFN step (T 8192, D 4096,
 F 14336): forward (row quantize X, 2D32 W1/W3/W2, fused SwiGLU producer emitting
 h row- and column-facing, W2 Fprop) and backward (row-SR and column-H32 dY, W2
 Dgrad and Wgrad, the fused SwiGLU backward producer emitting dA/dB row-SR and
-column-H32, column-H32 X, W1/W3 Dgrad with accumulation, W1/W3 Wgrad stacked
-into one launch): nine contractions, 8.66 TFLOP, timed as one captured HIP
+column-H32, column-H32 X, W1/W3 Dgrad as one accumulation over K = 2F, W1/W3
+Wgrad stacked into one launch): nine contractions, 8.66 TFLOP, timed as one captured HIP
 graph (per-call times come from eager steps with events around every call).
 
 Prints one JSON line.  `value` = GEMM FLOPs of the step / step time (the
@@ -168,6 +168,16 @@ class Step:
                            lambda: mx.fp4_gemm(a[0], a[1], b[0], b[1], c=c, accumulate=accumulate), alg_bytes))
         return c
 
+    def gemm_pair(self, label, a1, b1, a2, b2):
+        mx = self.mx
+        m, n, k = a1[0].shape[0], b1[0].shape[0], 2 * a1[0].shape[1]
+        c = self.e((m, n), self.torch.float32)
+        alg_bytes = 2 * (m + n) * k * (0.5 + 1 / 32) + 4 * m * n
+        self.calls.append((label, "gemm", 2.0 * m * n * 2 * k,
+                           lambda: mx.fp4_gemm_pair(a1[0], a1[1], b1[0], b1[1], a2[0], a2[1], b2[0], b2[1], c=c),
+                           alg_bytes))
+        return c
+
     # -------------------------------------------------------------- workloads
     def _build_fprop(self):                      # fprop_256x512x512: 1x32 blocks for X and W
         xr = self.q_rows("rows(X)", self.d["X"])
@@ -231,17 +241,16 @@ class Step:
             self.q_cols("cols(dA,H32)", da, out=dac)
             self.q_cols("cols(dB,H32)", db, out=dbc)
         xc = self.q_cols("cols(X,H32)", X)
-        dx = self.gemm("W1 Dgrad", dar, w1[2:])
-        self.gemm("W3 Dgrad (+=)", dbr, w3[2:], c=dx, accumulate=True)
+        # dX = dA W1 + dB W3: one contraction over K = 2F (no fp32 read-back of dX)
+        self.gemm_pair("W1+W3 Dgrad", dar, w1[2:], dbr, w3[2:])
         self.gemm("W1|W3 Wgrad", dabc, xc)
         # each producer is charged to the first contraction that reads it
         self.charge = {"swiglu_producer": ["rows(X)", "w2d32(W1)", "w2d32(W3)"], "W2 Fprop": ["w2d32(W2)"],
                        "W2 Dgrad": ["rows(dY,SR)"], "W2 Wgrad": ["cols(dY,H32)"], "W1|W3 Wgrad": ["cols(X,H32)"]}
         if self.fused_backward:
-            self.charge["W1 Dgrad"] = ["swiglu_bwd_producer"]
+            self.charge["W1+W3 Dgrad"] = ["swiglu_bwd_producer"]
         else:
-            self.charge["W1 Dgrad"] = ["swiglu_backward", "rows(dA,SR)"]
-            self.charge["W3 Dgrad (+=)"] = ["rows(dB,SR)"]
+            self.charge["W1+W3 Dgrad"] = ["swiglu_backward", "rows(dA,SR)", "rows(dB,SR)"]
             self.charge["W1|W3 Wgrad"] += ["cols(dA,H32)", "cols(dB,H32)"]
 
     def run(self, events=None):

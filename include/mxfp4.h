@@ -139,6 +139,24 @@ fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k,
                     float* c, int64_t ldc, int accumulate, void* stream);
 
 /*
+ * Two block-scaled products summed in one fp32 accumulation:
+ *   C[m][n] (+)= sum_k dec(A1)[m][k] dec(B1)[n][k] + sum_k dec(A2)[m][k] dec(B2)[n][k]
+ * For the gated FFN's input gradient (§3.2 with §2.3 Eq. 5): dX = dA W1 + dB W3
+ * reads the row-facing SR codes of dA and dB and the column layouts of W1 and
+ * W3, i.e. one Dgrad over the concatenated K = 2f.  All eight operands have the
+ * shapes of fp4_gemm's (same m, n, k).  When k is a multiple of 256 the sum
+ * runs over the K steps of pair 1, then pair 2, into the same accumulators;
+ * otherwise it is fp4_gemm(pair 1) followed by fp4_gemm(pair 2, accumulate).
+ * Deterministic.  Errors as fp4_gemm.
+ */
+fp4_status fp4_gemm_pair(int64_t m, int64_t n, int64_t k,
+                         const uint8_t* a1_codes, const uint8_t* a1_scales,
+                         const uint8_t* b1_codes, const uint8_t* b1_scales,
+                         const uint8_t* a2_codes, const uint8_t* a2_scales,
+                         const uint8_t* b2_codes, const uint8_t* b2_scales,
+                         float* c, int64_t ldc, int accumulate, void* stream);
+
+/*
  * Fused gated-FFN producer (§3.2): a = X W1^T and b = X W3^T computed together
  * on the block-scaled MFMA, rounded to bf16 (RNE) and saved for backward; then
  *   sig = 1/(1 + exp(-a)), s = a*sig, h = bf16(s*b)

@@ -29,6 +29,7 @@ _SIGS = {
     "fp4_quantize_cols": [_vp, _i64, _i64, _i64, _vp, _vp, _int, _u32, _vp],
     "fp4_quantize_w2d32": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.c_float, _vp],
     "fp4_gemm": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _int, _vp],
+    "fp4_gemm_pair": [_i64, _i64, _i64] + [_vp] * 9 + [_i64, _int, _vp],
     "fp4_swiglu_producer": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u32, _vp],
     "fp4_swiglu_backward": [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp],
     "fp4_swiglu_backward_producer": [_i64, _i64, _vp, _i64, _vp, _vp, _u64, _u64, _u64, _u32] + [_vp] * 9,
@@ -153,6 +154,35 @@ def fp4_gemm(a_codes, a_scales, b_codes, b_scales, c=None, accumulate=False):
             raise Fp4Error("c must be fp32 [m][n] with unit column stride")
     _check(load().fp4_gemm(m, n, k, _p(a_codes), _p(a_scales), _p(b_codes), _p(b_scales), _p(c), c.stride(0),
                            1 if accumulate else 0, _stream()))
+    return c
+
+
+def fp4_gemm_pair(a1_codes, a1_scales, b1_codes, b1_scales, a2_codes, a2_scales, b2_codes, b2_scales, c=None,
+                  accumulate=False):
+    """C (+)= A1 B1^T + A2 B2^T, one fp32 sum over both K ranges (same shapes)."""
+    ops = ((a1_codes, "a1_codes"), (a1_scales, "a1_scales"), (b1_codes, "b1_codes"), (b1_scales, "b1_scales"),
+           (a2_codes, "a2_codes"), (a2_scales, "a2_scales"), (b2_codes, "b2_codes"), (b2_scales, "b2_scales"))
+    for t, nm in ops:
+        _dev(t, nm)
+        if t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 2:
+            raise Fp4Error(f"{nm} must be a contiguous 2-D uint8 tensor")
+    m, k2 = a1_codes.shape
+    n = b1_codes.shape[0]
+    k = 2 * k2
+    for (ac, asc, bc, bsc) in ((a1_codes, a1_scales, b1_codes, b1_scales), (a2_codes, a2_scales, b2_codes, b2_scales)):
+        if (tuple(ac.shape) != (m, k2) or tuple(bc.shape) != (n, k2) or tuple(asc.shape) != (m, k // 32)
+                or tuple(bsc.shape) != (n, k // 32)):
+            raise Fp4Error("operand shapes disagree")
+    if c is None:
+        if accumulate:
+            raise Fp4Error("accumulate needs an output tensor")
+        c = torch.empty((m, n), dtype=torch.float32, device=a1_codes.device)
+    else:
+        _dev(c, "c")
+        if c.dtype != torch.float32 or c.dim() != 2 or c.stride(1) != 1 or tuple(c.shape) != (m, n):
+            raise Fp4Error("c must be fp32 [m][n] with unit column stride")
+    _check(load().fp4_gemm_pair(m, n, k, *(_p(t) for t, _ in ops), _p(c), c.stride(0), 1 if accumulate else 0,
+                                _stream()))
     return c
 
 

@@ -305,6 +305,8 @@ constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 
 
 struct FastPlan {
   __amdgpu_buffer_rsrc_t ra, rb, rs;   // A codes, this wave's B codes, this wave's scales
+  __amdgpu_buffer_rsrc_t ra2, rb2, rs2;  // the same for the second operand pair (K steps nk1 ..)
+  int nk1;                             // K steps of the first pair
   uint32_t va, vb;                     // lane code offsets of load j = 0 (j adds 8 rows)
   uint32_t vs;                         // lane scale offset
   uint32_t ldb8;                       // 8 code rows (bytes)
@@ -318,7 +320,8 @@ struct FastPlan {
 // 0..127 are W1 rows n0.. and rows 128..255 are W3 rows f+n0..
 template <bool kSwiGLU>
 __device__ __forceinline__ void make_fast_plan(FastPlan& p, const Operand& A, const Operand& B, int64_t m0,
-                                               int64_t n0, int64_t f, int64_t K) {
+                                               int64_t n0, int64_t f, int64_t K, const Operand* A2 = nullptr,
+                                               const Operand* B2 = nullptr) {
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int l = threadIdx.x & 63;
   const int64_t ldb = K >> 1, lsc = K >> 5;
@@ -358,6 +361,20 @@ __device__ __forceinline__ void make_fast_plan(FastPlan& p, const Operand& A, co
   // and (row >> 3) & 1 = j & 1
   p.wa0 = (uint32_t)(row0 * BKB + ((c ^ (l >> 3)) * 16));
   p.wa1 = (uint32_t)(row0 * BKB + ((c ^ (l >> 3) ^ 1) * 16));
+  // second pair (plain GEMM only): same shapes, so the same lane offsets
+  if constexpr (!kSwiGLU) {
+    if (A2 != nullptr && A2->codes != nullptr) {
+      p.ra2 = buffer_rsrc(A2->codes + m0 * ldb, rows_a * ldb);
+      p.rb2 = buffer_rsrc(B2->codes + n0 * ldb, rows_b * ldb);
+      p.rs2 = w < 4 ? buffer_rsrc(A2->scales + m0 * lsc, rows_a * lsc) : buffer_rsrc(B2->scales + n0 * lsc, rows_b * lsc);
+      p.nk1 = (int)(K / 256);
+      return;
+    }
+  }
+  p.ra2 = p.ra;
+  p.rb2 = p.rb;
+  p.rs2 = p.rs;
+  p.nk1 = 0x7FFFFFFF;
 }
 
 struct Frags8 {
@@ -397,19 +414,27 @@ struct PartB {
 // Load j of a part reads 8 rows further down.  The row offset stays in the
 // lane offset: the buffer range check (rows past the operand read zero) covers
 // the lane offset, not the scalar one, which carries only the K position.
+// K step `kit` of the concatenated K range: steps from nk1 on come from the
+// second operand pair (a wave-uniform choice of buffer resources).
 __device__ __forceinline__ void load_part_a(const FastPlan& p, int kit, PartA& x) {
-  const uint32_t so = (uint32_t)kit * BKB;
+  const bool second = kit >= p.nk1;
+  const __amdgpu_buffer_rsrc_t ra = second ? p.ra2 : p.ra;
+  const uint32_t so = (uint32_t)(second ? kit - p.nk1 : kit) * BKB;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    x.a[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(p.ra, p.va + (uint32_t)j * p.ldb8, so, 0));
+    x.a[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, p.va + (uint32_t)j * p.ldb8, so, 0));
 }
 
 __device__ __forceinline__ void load_part_b(const FastPlan& p, int kit, PartB& x) {
-  const uint32_t so = (uint32_t)kit * BKB, sso = (uint32_t)kit * 8u;
+  const bool second = kit >= p.nk1;
+  const __amdgpu_buffer_rsrc_t rb = second ? p.rb2 : p.rb;
+  const __amdgpu_buffer_rsrc_t rs = second ? p.rs2 : p.rs;
+  const int k1 = second ? kit - p.nk1 : kit;
+  const uint32_t so = (uint32_t)k1 * BKB, sso = (uint32_t)k1 * 8u;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    x.b[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(p.rb, p.vb + (uint32_t)j * p.ldb8, so, 0));
-  x.s = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(p.rs, p.vs, sso, 0));
+    x.b[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb, p.vb + (uint32_t)j * p.ldb8, so, 0));
+  x.s = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, p.vs, sso, 0));
 }
 
 // Stage `stg` (0 or 1, wave-uniform) of the part: 32 KB per code stage, 2 KB
@@ -513,9 +538,12 @@ __device__ __forceinline__ void pp_memory(uint8_t* smem, const FastPlan& p, cons
   else pp_next();
 }
 
+// With A2/B2 (plain GEMM only) the loop runs over K of (A, B) and then K of
+// (A2, B2) into the same accumulators: one fp32 sum over the concatenated K.
 template <bool kSwiGLU>
 __device__ __forceinline__ void main_loop_fast(uint8_t* smem, const Operand& A, const Operand& B, int64_t m0,
-                                               int64_t n0, int64_t f, int64_t K, v16f (&acc)[4][2], int wm, int wn) {
+                                               int64_t n0, int64_t f, int64_t K, v16f (&acc)[4][2], int wm, int wn,
+                                               const Operand* A2 = nullptr, const Operand* B2 = nullptr) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -523,9 +551,9 @@ __device__ __forceinline__ void main_loop_fast(uint8_t* smem, const Operand& A, 
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
   const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
-  const int nk = (int)(K / 256), last = nk - 1;
+  const int nk = (int)(K / 256) * ((A2 != nullptr && A2->codes != nullptr) ? 2 : 1), last = nk - 1;
   FastPlan p;
-  make_fast_plan<kSwiGLU>(p, A, B, m0, n0, f, K);
+  make_fast_plan<kSwiGLU>(p, A, B, m0, n0, f, K, A2, B2);
   PPAddr q;
   make_pp_addr<kSwiGLU>(q, wm, wn, r, h);
   PartA xa;
@@ -878,10 +906,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_generic_kernel(
   }
 }
 
+// a2_codes == nullptr: C (+)= A B^T.  Otherwise C (+)= A B^T + A2 B2^T as one
+// fp32 accumulation over both K ranges (each K long).
 __global__ __launch_bounds__(kFastThreads) void gemm_fast_kernel(
     int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
-    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, float* __restrict__ c, int64_t ldc,
-    int accumulate) {
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, const uint8_t* __restrict__ a2_codes,
+    const uint8_t* __restrict__ a2_scales, const uint8_t* __restrict__ b2_codes,
+    const uint8_t* __restrict__ b2_scales, float* __restrict__ c, int64_t ldc, int accumulate) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   int64_t tm, tn;
   tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
@@ -889,8 +920,9 @@ __global__ __launch_bounds__(kFastThreads) void gemm_fast_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3, hl = lane >> 5;
   Operand A{a_codes, a_scales, M}, B{b_codes, b_scales, N};
+  Operand A2{a2_codes, a2_scales, M}, B2{b2_codes, b2_scales, N};
   v16f acc[4][2];
-  main_loop_fast<false>(smem, A, B, m0, n0, 0, K, acc, wm, wn);
+  main_loop_fast<false>(smem, A, B, m0, n0, 0, K, acc, wm, wn, &A2, &B2);
   store_c_tile_staged(smem, acc, c, ldc, M, N, m0, n0, wave, lane, wm, wn, hl, accumulate != 0);
 }
 
@@ -984,11 +1016,40 @@ fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, con
   // the fast path needs K % 256 == 0 and buffer offsets below 2^31 per tile
   if ((k % 256) == 0 && 256 * (k / 2) < 0x7FFFFFFF)
     hipLaunchKernelGGL(gemm_fast_kernel, dim3((unsigned)tiles), dim3(kFastThreads), 0, s, m, n, k, a_codes, a_scales,
-                       b_codes, b_scales, c, ldc, accumulate);
+                       b_codes, b_scales, nullptr, nullptr, nullptr, nullptr, c, ldc, accumulate);
   else
     hipLaunchKernelGGL(gemm_generic_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, m, n, k, a_codes,
                        a_scales, b_codes, b_scales, c, ldc, accumulate);
   return launch_status();
+}
+
+fp4_status fp4_gemm_pair(int64_t m, int64_t n, int64_t k, const uint8_t* a1_codes, const uint8_t* a1_scales,
+                         const uint8_t* b1_codes, const uint8_t* b1_scales, const uint8_t* a2_codes,
+                         const uint8_t* a2_scales, const uint8_t* b2_codes, const uint8_t* b2_scales, float* c,
+                         int64_t ldc, int accumulate, void* stream) {
+  if (accumulate != 0 && accumulate != 1) return FP4_EINVAL;
+  if (!mult32z(m) || !mult32z(n) || !mult32z(k) || ldc < n) return FP4_ESHAPE;
+  if (m == 0 || n == 0) return FP4_OK;
+  if (k == 0) return fp4_gemm(m, n, 0, nullptr, nullptr, nullptr, nullptr, c, ldc, accumulate, stream);
+  if (!c || !a1_codes || !a1_scales || !b1_codes || !b1_scales || !a2_codes || !a2_scales || !b2_codes ||
+      !b2_scales)
+    return FP4_EINVAL;
+  if (!aligned16(a1_codes) || !aligned16(b1_codes) || !aligned16(a1_scales) || !aligned16(b1_scales) ||
+      !aligned16(a2_codes) || !aligned16(b2_codes) || !aligned16(a2_scales) || !aligned16(b2_scales) ||
+      !aligned16(c) || (ldc % 4) != 0)
+    return FP4_EALIGN;
+  const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  if (tiles > 0x7FFFFFFF) return FP4_ESHAPE;
+  if ((k % 256) == 0 && 256 * (k / 2) < 0x7FFFFFFF) {
+    hipLaunchKernelGGL(gemm_fast_kernel, dim3((unsigned)tiles), dim3(kFastThreads), 0, as_stream(stream), m, n, k,
+                       a1_codes, a1_scales, b1_codes, b1_scales, a2_codes, a2_scales, b2_codes, b2_scales, c, ldc,
+                       accumulate);
+    return launch_status();
+  }
+  // K not a multiple of 256: the second product is added to the first's result
+  const fp4_status st = fp4_gemm(m, n, k, a1_codes, a1_scales, b1_codes, b1_scales, c, ldc, accumulate, stream);
+  if (st != FP4_OK) return st;
+  return fp4_gemm(m, n, k, a2_codes, a2_scales, b2_codes, b2_scales, c, ldc, 1, stream);
 }
 
 fp4_status fp4_swiglu_producer(int64_t t, int64_t f, int64_t d, const uint8_t* x_codes, const uint8_t* x_scales,

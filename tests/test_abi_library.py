@@ -24,8 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_hot_path_calls():
     names = declared_functions()
-    for n in ("fp4_quantize_rows", "fp4_quantize_cols", "fp4_quantize_w2d32", "fp4_gemm",
-              "fp4_swiglu_producer", "fp4_swiglu_backward"):
+    for n in ("fp4_quantize_rows", "fp4_quantize_cols", "fp4_quantize_w2d32", "fp4_gemm", "fp4_gemm_pair",
+              "fp4_swiglu_producer", "fp4_swiglu_backward", "fp4_swiglu_backward_producer"):
         assert n in names
 
 
@@ -48,6 +48,7 @@ def test_host_only_calls():
     from oracle import philox as P
     lib = mx.load(LIB)
     assert lib.fp4_abi_version() >> 16 == 1
+    assert lib.fp4_abi_version() & 0xFFFF >= 1      # fp4_gemm_pair
     # the library's host sign-mask helper agrees with the oracle's generator
     for seed in (0, 1, 2 ** 40 + 7):
         assert mx.fp4_sign_mask_from_seed(seed) == P.sign_mask_from_seed(seed)
@@ -68,6 +69,11 @@ def test_argument_errors_are_reported_without_gpu_work():
                                   ctypes.c_float(0.87), None) == 2
     assert lib.fp4_gemm(32, 32, 48, v(4096), v(4096), v(4096), v(4096), v(4096), 32, 0, None) == 2
     assert lib.fp4_gemm(32, 32, 32, v(4096), v(4096), v(4096), v(4096), v(4096), 32, 2, None) == 1
+    pair = [v(4096)] * 8
+    assert lib.fp4_gemm_pair(32, 32, 48, *pair, v(4096), 32, 0, None) == 2
+    assert lib.fp4_gemm_pair(32, 32, 32, *pair, v(4096), 32, 2, None) == 1
+    assert lib.fp4_gemm_pair(32, 32, 32, *pair[:7], None, v(4096), 32, 0, None) == 1
+    assert lib.fp4_gemm_pair(32, 32, 32, *pair[:5], v(4100), *pair[6:], v(4096), 32, 0, None) == 3
     assert lib.fp4_swiglu_producer(32, 32, 32, v(4096), v(4096), v(4096), v(4096), v(4096), v(4096),
                                    v(4096), v(4096), v(4096), None, 0, None) == 1
     assert lib.fp4_swiglu_backward(32, 32, v(4096), 16, v(4096), v(4096), v(4096), v(4096), None) == 2
@@ -93,6 +99,9 @@ def test_empty_calls_are_noops_without_gpu_work():
     assert lib.fp4_quantize_w2d32(None, 0, 64, 64, None, None, None, None, ctypes.c_float(0.87), None) == 0
     assert lib.fp4_gemm(0, 64, 64, None, None, None, None, None, 64, 0, None) == 0
     assert lib.fp4_gemm(64, 0, 64, None, None, None, None, None, 0, 1, None) == 0
+    assert lib.fp4_gemm_pair(0, 64, 64, *([None] * 8), None, 64, 0, None) == 0
+    # k = 0 accumulating: C unchanged, no device work (C itself must still be given)
+    assert lib.fp4_gemm_pair(64, 64, 0, *([None] * 8), ctypes.c_void_p(4096), 64, 1, None) == 0
     assert lib.fp4_swiglu_producer(0, 64, 64, None, None, None, None, None, None, None, None, None, None, 0, None) == 0
     assert lib.fp4_swiglu_backward(0, 64, None, 64, None, None, None, None, None) == 0
     assert lib.fp4_swiglu_backward_producer(64, 0, None, 0, None, None, u64(0), u64(0), u64(1), 0,

@@ -106,6 +106,21 @@ def check_gemm(c, a, b, rng, what, c_prev=None):
                              f"first ({ms[i[0]]}, {ns[i[1]]}): got {got[i]} ref {ref[i]} E {e[i]}")
 
 
+def check_gemm_pair(c, a1, b1, a2, b2, rng, what):
+    ms = pick(a1[0].shape[0], N_GEMM_M, rng)
+    ns = pick(b1[0].shape[0], N_GEMM_N, rng)
+    r1, e1 = G.gemm_ref(host(rows_of(a1[0], ms)), host(rows_of(a1[1], ms)),
+                        host(rows_of(b1[0], ns)), host(rows_of(b1[1], ns)))
+    r2, e2 = G.gemm_ref(host(rows_of(a2[0], ms)), host(rows_of(a2[1], ms)),
+                        host(rows_of(b2[0], ns)), host(rows_of(b2[1], ns)))
+    got = host(cols_of(rows_of(c, ms), ns))
+    ok = G.within_bound(got, r1 + r2, e1 + e2)
+    if not ok.all():
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError(f"{what}: {int((~ok).sum())} sampled elements outside the bound; "
+                             f"first ({ms[i[0]]}, {ns[i[1]]}): got {got[i]} ref {(r1 + r2)[i]}")
+
+
 def test_fprop_256x512x512_full(gpu_lib):
     """Single Fprop linear, 1x32 blocks for both operands: the whole output."""
     h = synthetic.workload("fprop_256x512x512")
@@ -190,6 +205,7 @@ def test_ffn_step(gpu_lib, name):
     dx = gpu_lib.fp4_gemm(dar[0], dar[1], w1[2], w1[3])
     dx_first = dx.clone()
     gpu_lib.fp4_gemm(dbr[0], dbr[1], w3[2], w3[3], c=dx, accumulate=True)
+    dx_pair = gpu_lib.fp4_gemm_pair(dar[0], dar[1], w1[2], w1[3], dbr[0], dbr[1], w3[2], w3[3])
     dw1 = gpu_lib.fp4_gemm(dac[0], dac[1], xc[0], xc[1])
     dw3 = gpu_lib.fp4_gemm(dbc[0], dbc[1], xc[0], xc[1])
     torch.cuda.synchronize()
@@ -244,6 +260,7 @@ def test_ffn_step(gpu_lib, name):
     check_gemm(dx_first, dar, w1[2:], rng, "W1 Dgrad")
     check_gemm(dx, dbr, w3[2:], rng, "W3 Dgrad (+=)",
                c_prev=lambda ms_, ns_: host(cols_of(rows_of(dx_first, ms_), ns_)))
+    check_gemm_pair(dx_pair, dar, w1[2:], dbr, w3[2:], rng, "W1+W3 Dgrad (one accumulation)")
     check_gemm(dw1, dac, xc, rng, "W1 Wgrad")
     check_gemm(dw3, dbc, xc, rng, "W3 Wgrad")
     # the two Wgrads stacked into one contraction (M = 2F) give the same bytes

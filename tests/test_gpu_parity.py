@@ -139,6 +139,33 @@ def test_gemm(gpu_lib, mnk):
     check_gemm(c2, a, b, c_prev=prev, what="accumulate")
 
 
+@pytest.mark.parametrize("mnk", [(288, 352, 512), (256, 512, 1024), (96, 544, 256), (64, 96, 288), (32, 32, 32)])
+def test_gemm_pair(gpu_lib, mnk):
+    """C = A1 B1^T + A2 B2^T within the bound of the summed products; with K a
+    multiple of 256 it is one accumulation, byte-equal to fp4_gemm over the
+    operands concatenated along K."""
+    m, n, k = mnk
+    q = []
+    for i, (rows, std) in enumerate(((m, 1.0), (n, 0.02), (m, 1e-3), (n, 0.02))):
+        t = synthetic.tensor((rows, k), std=std, seed=40 + i, outlier_rate=0.001, outlier_scale=20.0)
+        q.append(gpu_lib.fp4_quantize_rows(dev16(t)))
+    a1, b1, a2, b2 = q
+    c = gpu_lib.fp4_gemm_pair(*a1, *b1, *a2, *b2)
+    r1, e1 = G.gemm_ref(host(a1[0]), host(a1[1]), host(b1[0]), host(b1[1]))
+    r2, e2 = G.gemm_ref(host(a2[0]), host(a2[1]), host(b2[0]), host(b2[1]))
+    ok = G.within_bound(host(c), r1 + r2, e1 + e2)
+    assert ok.all(), f"{(~ok).sum()} elements outside the bound"
+    prev = host(c).copy()
+    c2 = gpu_lib.fp4_gemm_pair(*a1, *b1, *a2, *b2, c=c, accumulate=True)
+    ok = G.within_bound(host(c2), r1 + r2, e1 + e2, c_prev=prev)
+    assert ok.all(), f"accumulate: {(~ok).sum()} elements outside the bound"
+    if k % 256 == 0:
+        cat = [torch.cat((x, y), dim=1).contiguous() for x, y in zip(a1 + b1, a2 + b2)]
+        whole = gpu_lib.fp4_gemm(*cat)
+        assert np.array_equal(host(gpu_lib.fp4_gemm_pair(*a1, *b1, *a2, *b2)).view(np.uint32),
+                              host(whole).view(np.uint32))
+
+
 def test_gemm_layout_one_hot(gpu_lib):
     # one non-zero product per output element pins the MFMA register layout
     m, n, k = 64, 96, 256
