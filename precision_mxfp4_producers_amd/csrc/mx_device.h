@@ -187,10 +187,13 @@ __device__ __forceinline__ float exp_spec(float x) {
   const float LOG2E = 0x1.715476p+0f;                      // RN(1/ln 2)
   const float LN2_HI = 0.693359375f;                       // 355/512
   const float LN2_LO = -0x1.bd0106p-13f;                   // RN(ln 2 - 355/512)
-  if (x > 89.0f) return __builtin_inff();
-  if (x < -104.0f) return 0.0f;
-  float n = rintf(__fmul_rn(x, LOG2E));
-  float r = __fsub_rn(__fsub_rn(x, __fmul_rn(n, LN2_HI)), __fmul_rn(n, LN2_LO));
+  // out-of-range inputs run the polynomial on 0 and are replaced at the end:
+  // no branch (a branch per element splits the unrolled element loops into
+  // exec-masked regions the scheduler cannot interleave)
+  const bool over = x > 89.0f, under = x < -104.0f;
+  const float xs = (over || under) ? 0.0f : x;
+  float n = rintf(__fmul_rn(xs, LOG2E));
+  float r = __fsub_rn(__fsub_rn(xs, __fmul_rn(n, LN2_HI)), __fmul_rn(n, LN2_LO));
   float p = 0x1.a01a02p-13f;                               // RN(1/7!)
   p = __fadd_rn(__fmul_rn(p, r), 0x1.6c16c2p-10f);          // RN(1/6!)
   p = __fadd_rn(__fmul_rn(p, r), 0x1.111112p-7f);           // RN(1/5!)
@@ -202,7 +205,8 @@ __device__ __forceinline__ float exp_spec(float x) {
   int ni = (int)n;
   int n1 = ni >> 1;                                        // floor(n/2)
   int n2 = ni - n1;
-  return __fmul_rn(__fmul_rn(p, pow2_i(n1)), pow2_i(n2));
+  const float e = __fmul_rn(__fmul_rn(p, pow2_i(n1)), pow2_i(n2));
+  return under ? 0.0f : (over ? __builtin_inff() : e);
 }
 
 // sig = 1/(1+exp(-a)), s = a*sig
