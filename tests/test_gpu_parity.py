@@ -166,6 +166,29 @@ def test_gemm_pair(gpu_lib, mnk):
                               host(whole).view(np.uint32))
 
 
+@pytest.mark.parametrize("k", [768, 1024])
+def test_gemm_more_tiles_than_cus(gpu_lib, k):
+    """17 x 17 tiles (ragged in both dimensions): more tiles than CUs, so each
+    workgroup of the launch computes one or two tiles in turn; plain,
+    accumulating and paired forms."""
+    m, n = 4160, 4128
+    x = synthetic.tensor((m, k), std=1.0, seed=51, outlier_rate=0.001, outlier_scale=20.0)
+    w = synthetic.tensor((n, k), std=0.02, seed=52)
+    a = gpu_lib.fp4_quantize_rows(dev16(x))
+    b = gpu_lib.fp4_quantize_rows(dev16(w))
+    c = gpu_lib.fp4_gemm(a[0], a[1], b[0], b[1])
+    check_gemm(c, a, b)
+    prev = host(c).copy()
+    c2 = gpu_lib.fp4_gemm(a[0], a[1], b[0], b[1], c=c, accumulate=True)
+    check_gemm(c2, a, b, c_prev=prev, what="accumulate")
+    x2 = synthetic.tensor((m, k), std=1e-3, seed=53)
+    a2 = gpu_lib.fp4_quantize_rows(dev16(x2))
+    cp = gpu_lib.fp4_gemm_pair(a[0], a[1], b[0], b[1], a2[0], a2[1], b[0], b[1])
+    r1, e1 = G.gemm_ref(host(a[0]), host(a[1]), host(b[0]), host(b[1]))
+    r2, e2 = G.gemm_ref(host(a2[0]), host(a2[1]), host(b[0]), host(b[1]))
+    assert G.within_bound(host(cp), r1 + r2, e1 + e2).all()
+
+
 def test_gemm_layout_one_hot(gpu_lib):
     # one non-zero product per output element pins the MFMA register layout
     m, n, k = 64, 96, 256
