@@ -6,8 +6,8 @@
 A step is one pass of the whole hot path over one batch of synthetic input.
 The default workload is the full Llama-3-8B SwiGLU FFN step (T 8192, D 4096,
 F 14336): forward (row quantize X, 2D32 W1/W3/W2, fused SwiGLU producer emitting
-h row- and column-facing, W2 Fprop) and backward (row-SR and column-H32 dY, W2
-Dgrad and Wgrad, the fused SwiGLU backward producer emitting dA/dB row-SR and
+h row- and column-facing, W2 Fprop) and backward (row-SR and column-H32 dY from
+one read, W2 Dgrad and Wgrad, the fused SwiGLU backward producer emitting dA/dB row-SR and
 column-H32, column-H32 X, W1/W3 Dgrad as one accumulation over K = 2F, W1/W3
 Wgrad stacked into one launch): nine contractions, 8.66 TFLOP, timed as one captured HIP
 graph (per-call times come from eager steps with events around every call).
@@ -38,6 +38,7 @@ METRIC = "MXFP4 quantize+GEMM TFLOP/s (Fprop/Dgrad/Wgrad) and quantizer GB/s, % 
 # Algorithmic bytes per element (what the producer must move):
 B_SINGLE = 2 + 0.5 + 1 / 32          # bf16 in, one orientation of codes + scales
 B_2D32 = 2 + 2 * (0.5 + 1 / 32)      # bf16 in, two layouts
+B_DUAL = 2 + 2 * (0.5 + 1 / 32)      # bf16 in once, row and column codes + scales
 B_SWIGLU_BWD = 4 + 2 + 2 + 2 + 2     # dH fp32, a, b in; dA, dB out
 B_BWD_PRODUCER = 4 + 2 + 2 + 4 * (0.5 + 1 / 32)   # dH, a, b in; dA, dB as row SR + column H32 MXFP4
 
@@ -51,7 +52,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--unfused-backward", action="store_true",
-                   help="FFN step: SwiGLU backward, SR rows and H32 cols of dA/dB as five separate calls")
+                   help="FFN step: separate producer calls (SR rows and H32 cols of dY as two calls; SwiGLU backward, "
+                        "SR rows and H32 cols of dA/dB as five)")
     p.add_argument("--eager", action="store_true",
                    help="time the step as eager launches instead of one captured HIP graph")
     p.add_argument("--quality", action="store_true",
@@ -149,6 +151,14 @@ class Step:
                            lambda: mx.fp4_quantize_cols(x, 32, self.mask, codes_t=out[0], scales_t=out[1]), 0))
         return out
 
+    def q_dual(self, label, x, offset=0):
+        """Row SR and column H32 of x from one read."""
+        mx, (R, C) = self.mx, x.shape
+        out = (self.u8(R, C // 2), self.u8(R, C // 32), self.u8(C, R // 2), self.u8(C, R // 32))
+        self.calls.append((label, "quant", R * C * B_DUAL,
+                           lambda: mx.fp4_quantize_dual(x, 1, self.seed, offset, 32, self.mask, *out), 0))
+        return out[:2], out[2:]
+
     def q_w(self, label, w, row_codes=None, row_scales=None):
         mx, (N, K) = self.mx, w.shape
         rc = row_codes if row_codes is not None else self.u8(N, K // 2)
@@ -216,8 +226,11 @@ class Step:
                            lambda: mx.fp4_swiglu_producer(xr[0], xr[1], w13_rc, w13_rs, self.mask, True,
                                                           a, b, hr[0], hr[1], hc[0], hc[1]), 0))
         self.gemm("W2 Fprop", hr, w2[:2])
-        dyr = self.q_rows("rows(dY,SR)", dY, 1, 0)
-        dyc = self.q_cols("cols(dY,H32)", dY)
+        if self.fused_backward:
+            dyr, dyc = self.q_dual("dual(dY: SR rows, H32 cols)", dY, 0)
+        else:
+            dyr = self.q_rows("rows(dY,SR)", dY, 1, 0)
+            dyc = self.q_cols("cols(dY,H32)", dY)
         dh = self.gemm("W2 Dgrad", dyr, w2[2:])
         self.gemm("W2 Wgrad", dyc, hc)
         # column-facing dA and dB land in one stacked [2F][T/2] buffer, so that
@@ -246,7 +259,12 @@ class Step:
         self.gemm("W1|W3 Wgrad", dabc, xc)
         # each producer is charged to the first contraction that reads it
         self.charge = {"swiglu_producer": ["rows(X)", "w2d32(W1)", "w2d32(W3)"], "W2 Fprop": ["w2d32(W2)"],
-                       "W2 Dgrad": ["rows(dY,SR)"], "W2 Wgrad": ["cols(dY,H32)"], "W1|W3 Wgrad": ["cols(X,H32)"]}
+                       "W1|W3 Wgrad": ["cols(X,H32)"]}
+        if self.fused_backward:
+            self.charge["W2 Dgrad"] = ["dual(dY: SR rows, H32 cols)"]
+        else:
+            self.charge["W2 Dgrad"] = ["rows(dY,SR)"]
+            self.charge["W2 Wgrad"] = ["cols(dY,H32)"]
         if self.fused_backward:
             self.charge["W1+W3 Dgrad"] = ["swiglu_bwd_producer"]
         else:

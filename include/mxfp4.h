@@ -107,6 +107,24 @@ fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int6
                              int hadamard, uint32_t sign_mask16, void* stream);
 
 /*
+ * Both activation-gradient views from one read (§2.3 Eq. 5-6 with §2.5: the
+ * Dgrad reads dY row-facing with SR, the Wgrad reads it column-facing with
+ * the fixed-sign H32).  Byte-identical to
+ *   fp4_quantize_rows(x, mode, seed, offset)      -> row_codes, row_scales
+ *   fp4_quantize_cols(x, hadamard, sign_mask16)   -> codes_t, scales_t
+ * on the same tensor; x is read once.  rows and cols must be multiples of 32.
+ *   x         [rows][ldx] bf16
+ *   row_codes [rows][cols/2], row_scales [rows][cols/32]
+ *   codes_t   [cols][rows/2], scales_t   [cols][rows/32]
+ * Errors as the two calls (FP4_EINVAL for a bad mode or hadamard).
+ */
+fp4_status fp4_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* row_codes, uint8_t* row_scales,
+                             int mode, uint64_t seed, uint64_t offset,
+                             uint8_t* codes_t, uint8_t* scales_t,
+                             int hadamard, uint32_t sign_mask16, void* stream);
+
+/*
  * 2D32 weight producer (§2.4, Eq. 7-8; adaptive rule of §2.2.1).  One
  * exponent per 32x32 tile: e_up from the tile maximum a_T; the finer exponent
  * e_up - 1 is taken iff (a_T/6)/2^e_up < finer_ratio (exact comparison) and

@@ -27,6 +27,7 @@ _i64, _u64, _u32, _int, _vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, 
 _SIGS = {
     "fp4_quantize_rows": [_vp, _i64, _i64, _i64, _vp, _vp, _int, _u64, _u64, _vp],
     "fp4_quantize_cols": [_vp, _i64, _i64, _i64, _vp, _vp, _int, _u32, _vp],
+    "fp4_quantize_dual": [_vp, _i64, _i64, _i64, _vp, _vp, _int, _u64, _u64, _vp, _vp, _int, _u32, _vp],
     "fp4_quantize_w2d32": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.c_float, _vp],
     "fp4_gemm": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _int, _vp],
     "fp4_gemm_pair": [_i64, _i64, _i64] + [_vp] * 9 + [_i64, _int, _vp],
@@ -120,6 +121,23 @@ def fp4_quantize_cols(x, hadamard=0, sign_mask16=0, codes_t=None, scales_t=None)
     _check(load().fp4_quantize_cols(_p(x), rows, cols, x.stride(0), _p(codes_t), _p(scales_t), int(hadamard),
                                     int(sign_mask16), _stream()))
     return codes_t, scales_t
+
+
+def fp4_quantize_dual(x, mode=FP4_RTN, seed=0, offset=0, hadamard=0, sign_mask16=0, codes=None, scales=None,
+                      codes_t=None, scales_t=None):
+    """Row-facing and column-facing MXFP4 of x from one read: returns
+    (codes, scales, codes_t, scales_t), the bytes of fp4_quantize_rows and
+    fp4_quantize_cols."""
+    x = _bf16_2d(x, "x")
+    rows, cols = x.shape
+    codes = _out(codes, (rows, cols // 2), torch.uint8, x.device, "codes")
+    scales = _out(scales, (rows, cols // 32), torch.uint8, x.device, "scales")
+    codes_t = _out(codes_t, (cols, rows // 2), torch.uint8, x.device, "codes_t")
+    scales_t = _out(scales_t, (cols, rows // 32), torch.uint8, x.device, "scales_t")
+    _check(load().fp4_quantize_dual(_p(x), rows, cols, x.stride(0), _p(codes), _p(scales), int(mode), int(seed),
+                                    int(offset), _p(codes_t), _p(scales_t), int(hadamard), int(sign_mask16),
+                                    _stream()))
+    return codes, scales, codes_t, scales_t
 
 
 def fp4_quantize_w2d32(w, finer_ratio=0.87, row_codes=None, row_scales=None, col_codes=None, col_scales=None):

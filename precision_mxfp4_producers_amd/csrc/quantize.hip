@@ -188,6 +188,137 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
   }
 }
 
+// ------------------------------------------------------------------ dual (rows + cols, one read)
+// Both views of one tensor from a single read (the dY of a linear layer: row
+// SR for Dgrad, column H32 for Wgrad).  A workgroup stages kDualTok tokens x
+// kDualW columns of bf16 in LDS, then
+//   rows: lane (row ci/32, 8-value chunk ci%32) encodes with the rows
+//         kernel's own code (quad max, SR words of the element's row-major
+//         index); a wave stores two whole 128-byte code lines;
+//   cols: as the column kernel (column pairs x 32-token blocks, optional H32),
+//         codes staged in the tile buffer once every lane has read its values,
+//         then stored as 64-byte runs per column.
+// Bytes are those of fp4_quantize_rows and fp4_quantize_cols on the same
+// tensor: the same per-block encoders run on the same values.
+constexpr int kDualTok = 128, kDualW = 256;
+constexpr int kDualThreads = 512;                        // one column item per lane
+constexpr int kDualPitch = kDualW * 2 + 4;               // bytes per staged token row
+constexpr int kDualCodePitch = kDualTok / 2 + 16;        // bytes per staged column of codes
+static_assert(kDualW * kDualCodePitch <= kDualTok * kDualPitch, "column codes fit in the tile buffer");
+
+template <bool kSR, bool kH32>
+__global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* __restrict__ row_codes,
+    uint8_t* __restrict__ row_scales, uint64_t seed, uint64_t offset, uint8_t* __restrict__ codes_t,
+    uint8_t* __restrict__ scales_t, uint32_t sign_mask16) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kDualTok * kDualPitch];
+  __shared__ uint8_t stile[kDualW][kDualTok / 32];
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * kDualW, t0 = (int64_t)blockIdx.y * kDualTok;
+  const int ntok = (int)min<int64_t>(kDualTok, rows - t0);         // multiple of 32
+  const int ncol = (int)min<int64_t>(kDualW, cols - c0);           // multiple of 32
+
+  // load: thread (row tid/32 + 16j, 16-byte chunk tid%32); rows beyond the
+  // tensor and chunks beyond its columns stage zeros (never encoded)
+  {
+    constexpr int kJ = kDualTok / (kDualThreads / 32);
+    const int ch = tid & 31;
+    const bool col_ok = ch * 8 < ncol;
+#pragma unroll 4
+    for (int j0 = 0; j0 < kJ; j0 += 4) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = (tid >> 5) + (kDualThreads / 32) * (j0 + u);
+        v[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (col_ok && r < ntok) v[u] = *reinterpret_cast<const uint4*>(x + (t0 + r) * ldx + c0 + ch * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = (tid >> 5) + (kDualThreads / 32) * (j0 + u);
+        uint32_t* d = reinterpret_cast<uint32_t*>(tile + r * kDualPitch + ch * 16);
+        d[0] = v[u].x; d[1] = v[u].y; d[2] = v[u].z; d[3] = v[u].w;
+      }
+    }
+  }
+  __syncthreads();
+
+  // rows: 128 rows x 32 chunks; a quad covers one 32-value block
+  {
+    const int64_t cpr = cols >> 3;
+#pragma unroll 2
+    for (int ci = tid; ci < kDualTok * 32; ci += kDualThreads) {
+      const int r = ci >> 5, ch = ci & 31;
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + r * kDualPitch + ch * 16);
+      const uint32_t m = max_quad(bf16_absmax8(v.x, v.y, v.z, v.w));
+      const int e = upward_exp(m << 16);
+      if (r < ntok && ch * 8 < ncol) {
+        const int64_t gr = t0 + r, c8 = (c0 >> 3) + ch;
+        (void)cpr;
+        const uint32_t packed = encode_row_chunk<kSR>(v, e, gr, cols, c8, seed, offset);
+        *reinterpret_cast<uint32_t*>(row_codes + gr * (cols >> 1) + c8 * 4) = packed;
+        if ((ch & 3) == 0) row_scales[gr * (cols >> 5) + (c8 >> 2)] = (uint8_t)(e + 127);
+      }
+    }
+  }
+
+  // cols: items (column pair, token block); all lanes read before any code
+  // overwrites the tile
+  constexpr int kItems = (kDualW / 2) * (kDualTok / 32);
+  static_assert(kItems == kDualThreads, "one column item per lane");
+  uint4 code[1][2];
+  int ex[1][2];
+  bool live[1];
+#pragma unroll
+  for (int u = 0; u < 1; ++u) {
+    const int i = tid + u * kDualThreads;
+    const int cp = i % (kDualW / 2), tb = i / (kDualW / 2);
+    live[u] = 2 * cp < ncol && 32 * tb < ntok;
+    uint32_t v[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) v[k] = *reinterpret_cast<const uint32_t*>(tile + (32 * tb + k) * kDualPitch + cp * 4);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float f[32];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        uint32_t bb = (v[k] >> (16 * c)) & 0xFFFFu;
+        if constexpr (kH32) bb ^= ((sign_mask16 >> (k & 15)) & 1u) << 15;   // d_(k mod 16)
+        f[k] = bf16_bits_to_f32(bb);
+      }
+      if constexpr (kH32) h32_fp32(f);
+      code[u][c] = encode32_rtn(f, ex[u][c]);
+    }
+  }
+  __syncthreads();
+  uint8_t* ctile = tile;
+#pragma unroll
+  for (int u = 0; u < 1; ++u) {
+    const int i = tid + u * kDualThreads;
+    const int cp = i % (kDualW / 2), tb = i / (kDualW / 2);
+    if (live[u]) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        *reinterpret_cast<uint4*>(ctile + (2 * cp + c) * kDualCodePitch + tb * 16) = code[u][c];
+        stile[2 * cp + c][tb] = (uint8_t)(ex[u][c] + 127);
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int kPieces = kDualTok / 32;                 // 16-byte pieces per column
+  for (int i = tid; i < kDualW * kPieces; i += kDualThreads) {
+    const int col = i / kPieces, piece = i % kPieces;
+    if (col < ncol && piece * 32 < ntok) {
+      const uint4 d = *reinterpret_cast<const uint4*>(ctile + col * kDualCodePitch + piece * 16);
+      *reinterpret_cast<uint4*>(codes_t + (c0 + col) * (rows >> 1) + (t0 >> 1) + piece * 16) = d;
+    }
+  }
+  for (int col = tid; col < ncol; col += kDualThreads) {
+    uint8_t* dst = scales_t + (c0 + col) * (rows >> 5) + (t0 >> 5);
+    for (int tb = 0; tb < ntok / 32; ++tb) dst[tb] = stile[col][tb];
+  }
+}
+
 // ------------------------------------------------------------------ 2D32
 // A 256-lane workgroup walks consecutive 128x128 weight macro tiles (4x4 tiles
 // of 32x32) along K; the loads of the next macro tile are in flight while the
@@ -374,6 +505,36 @@ fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int6
   return launch_status();
 }
 
+fp4_status fp4_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* row_codes, uint8_t* row_scales, int mode, uint64_t seed, uint64_t offset,
+                             uint8_t* codes_t, uint8_t* scales_t, int hadamard, uint32_t sign_mask16,
+                             void* stream) {
+  if (mode != FP4_RTN && mode != FP4_SR) return FP4_EINVAL;
+  if (hadamard != 0 && hadamard != 32) return FP4_EINVAL;
+  if (!mult32z(rows) || !mult32z(cols) || ldx < cols) return FP4_ESHAPE;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (!x || !row_codes || !row_scales || !codes_t || !scales_t) return FP4_EINVAL;
+  if (!aligned16(x) || !aligned16(row_codes) || !aligned16(codes_t) || (ldx % 8) != 0) return FP4_EALIGN;
+  const int64_t gx = (cols + kDualW - 1) / kDualW, gy = (rows + kDualTok - 1) / kDualTok;
+  if (gy > kMaxGridY) return FP4_ESHAPE;
+  dim3 grid((unsigned)gx, (unsigned)gy);
+  hipStream_t s = as_stream(stream);
+  const uint32_t m16 = hadamard == 32 ? (sign_mask16 & 0xFFFFu) : 0u;
+  if (mode == FP4_SR && hadamard == 32)
+    hipLaunchKernelGGL((quant_dual_kernel<true, true>), grid, dim3(kDualThreads), 0, s, x, rows, cols, ldx, row_codes,
+                       row_scales, seed, offset, codes_t, scales_t, m16);
+  else if (mode == FP4_SR)
+    hipLaunchKernelGGL((quant_dual_kernel<true, false>), grid, dim3(kDualThreads), 0, s, x, rows, cols, ldx, row_codes,
+                       row_scales, seed, offset, codes_t, scales_t, m16);
+  else if (hadamard == 32)
+    hipLaunchKernelGGL((quant_dual_kernel<false, true>), grid, dim3(kDualThreads), 0, s, x, rows, cols, ldx, row_codes,
+                       row_scales, seed, offset, codes_t, scales_t, m16);
+  else
+    hipLaunchKernelGGL((quant_dual_kernel<false, false>), grid, dim3(kDualThreads), 0, s, x, rows, cols, ldx, row_codes,
+                       row_scales, seed, offset, codes_t, scales_t, m16);
+  return launch_status();
+}
+
 fp4_status fp4_quantize_w2d32(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
                               uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
                               uint8_t* col_scales, float finer_ratio, void* stream) {
@@ -413,6 +574,6 @@ uint32_t fp4_sign_mask_from_seed(uint64_t seed) {
 
 int fp4_last_hip_error(void) { return g_last_hip_error; }
 
-int fp4_abi_version(void) { return (1 << 16) | 1; }
+int fp4_abi_version(void) { return (1 << 16) | 2; }
 
 }  // extern "C"

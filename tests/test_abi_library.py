@@ -24,7 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_hot_path_calls():
     names = declared_functions()
-    for n in ("fp4_quantize_rows", "fp4_quantize_cols", "fp4_quantize_w2d32", "fp4_gemm", "fp4_gemm_pair",
+    for n in ("fp4_quantize_rows", "fp4_quantize_cols", "fp4_quantize_dual", "fp4_quantize_w2d32", "fp4_gemm",
+              "fp4_gemm_pair",
               "fp4_swiglu_producer", "fp4_swiglu_backward", "fp4_swiglu_backward_producer"):
         assert n in names
 
@@ -48,7 +49,7 @@ def test_host_only_calls():
     from oracle import philox as P
     lib = mx.load(LIB)
     assert lib.fp4_abi_version() >> 16 == 1
-    assert lib.fp4_abi_version() & 0xFFFF >= 1      # fp4_gemm_pair
+    assert lib.fp4_abi_version() & 0xFFFF >= 2      # fp4_gemm_pair, fp4_quantize_dual
     # the library's host sign-mask helper agrees with the oracle's generator
     for seed in (0, 1, 2 ** 40 + 7):
         assert mx.fp4_sign_mask_from_seed(seed) == P.sign_mask_from_seed(seed)
@@ -65,6 +66,14 @@ def test_argument_errors_are_reported_without_gpu_work():
     assert lib.fp4_quantize_rows(v(4096), 32, 32, 32, v(4096), v(4096), 7, 0, 0, None) == 1
     assert lib.fp4_quantize_cols(v(4096), 48, 32, 32, v(4096), v(4096), 0, 0, None) == 2
     assert lib.fp4_quantize_cols(v(4096), 32, 32, 32, v(4096), v(4096), 16, 0, None) == 1
+    u64 = ctypes.c_uint64
+    d4 = [v(4096)] * 2
+    assert lib.fp4_quantize_dual(v(4096), 48, 32, 32, *d4, 1, u64(0), u64(0), *d4, 32, 0, None) == 2
+    assert lib.fp4_quantize_dual(v(4096), 32, 32, 32, *d4, 3, u64(0), u64(0), *d4, 32, 0, None) == 1
+    assert lib.fp4_quantize_dual(v(4096), 32, 32, 32, *d4, 1, u64(0), u64(0), *d4, 16, 0, None) == 1
+    assert lib.fp4_quantize_dual(v(4096), 32, 32, 32, v(4096), v(4096), 1, u64(0), u64(0), None, v(4096), 32, 0,
+                                 None) == 1
+    assert lib.fp4_quantize_dual(v(4098), 32, 32, 32, *d4, 1, u64(0), u64(0), *d4, 32, 0, None) == 3
     assert lib.fp4_quantize_w2d32(v(4096), 32, 32, 16, v(4096), v(4096), v(4096), v(4096),
                                   ctypes.c_float(0.87), None) == 2
     assert lib.fp4_gemm(32, 32, 48, v(4096), v(4096), v(4096), v(4096), v(4096), 32, 0, None) == 2
@@ -96,6 +105,7 @@ def test_empty_calls_are_noops_without_gpu_work():
     assert lib.fp4_quantize_rows(None, 5, 0, 0, None, None, 0, 0, 0, None) == 0
     assert lib.fp4_quantize_cols(None, 0, 64, 64, None, None, 32, 0, None) == 0
     assert lib.fp4_quantize_cols(None, 64, 0, 0, None, None, 0, 0, None) == 0
+    assert lib.fp4_quantize_dual(None, 0, 64, 64, None, None, 1, u64(0), u64(0), None, None, 32, 0, None) == 0
     assert lib.fp4_quantize_w2d32(None, 0, 64, 64, None, None, None, None, ctypes.c_float(0.87), None) == 0
     assert lib.fp4_gemm(0, 64, 64, None, None, None, None, None, 64, 0, None) == 0
     assert lib.fp4_gemm(64, 0, 64, None, None, None, None, None, 0, 1, None) == 0

@@ -247,6 +247,12 @@ def test_ffn_step(gpu_lib, name):
     check_cols(dac, np.ascontiguousarray(host16(cols_of(da, fc))), fc, mask, "cols(dA,H32)")
     check_cols(dbc, np.ascontiguousarray(host16(cols_of(db, fc))), fc, mask, "cols(dB,H32)")
 
+    # single-read dY producer: the same bytes as the two separate calls, everywhere
+    dual = gpu_lib.fp4_quantize_dual(dY, gpu_lib.FP4_SR, seed, 0, 32, mask)
+    for got, want, nm in zip(dual, dyr + dyc, ("dY row codes", "dY row scales", "dY col codes", "dY col scales")):
+        assert torch.equal(got, want), "dual " + nm
+    del dual
+
     # fused backward producer: the same bytes as the unfused calls, everywhere
     fused = gpu_lib.fp4_swiglu_backward_producer(dh, a, b, seed, 1, 2, mask)
     for got, want, nm in zip(fused, (dar, dbr, dac, dbc), ("dA rows", "dB rows", "dA cols", "dB cols")):

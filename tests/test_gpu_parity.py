@@ -109,6 +109,25 @@ def test_cols(gpu_lib, shape, had):
     assert_same(scales, want[1], "col scales")
 
 
+@pytest.mark.parametrize("shape", [(256, 512), (320, 544), (4128, 96), (32, 32), (160, 288)])
+@pytest.mark.parametrize("mode,had", [(1, 32), (0, 0), (1, 0), (0, 32)])
+def test_dual(gpu_lib, shape, mode, had):
+    """One read, both views: the oracle's row and column codes, and the same
+    bytes as the two separate producers."""
+    x = synthetic.tensor(shape, std=1e-3, seed=19, outlier_rate=0.01, outlier_scale=50.0)
+    mask = P.sign_mask_from_seed(4)
+    seed, offset = 2 ** 35 + 9, 3
+    got = gpu_lib.fp4_quantize_dual(dev16(x), mode, seed, offset, had, mask)
+    rows = Q.quantize_rows(x, Q.SR if mode == 1 else Q.RTN, seed, offset)
+    cols = Q.quantize_cols(x, had, mask)
+    for g, w, nm in zip(got, rows + cols, ("row codes", "row scales", "col codes", "col scales")):
+        assert_same(g, w, nm)
+    xd = dev16(x)
+    sep = gpu_lib.fp4_quantize_rows(xd, mode, seed, offset) + gpu_lib.fp4_quantize_cols(xd, had, mask)
+    for g, w in zip(got, sep):
+        assert torch.equal(g, w)
+
+
 @pytest.mark.parametrize("shape", [(512, 512), (352, 416), (32, 64), (4096, 160)])
 @pytest.mark.parametrize("ratio", [0.87, 0.0])
 def test_w2d32(gpu_lib, shape, ratio):
