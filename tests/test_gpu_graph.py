@@ -31,6 +31,8 @@ def build_step(mx, t=256, d=512, f=384, seed=3):
                  u8(f, t // 2), u8(f, t // 32), u8(f, t // 2), u8(f, t // 32)],
          "xc": (u8(d, t // 2), u8(d, t // 32)),
          "dx": torch.empty((t, d), dtype=torch.float32, device="cuda"),
+         "dx2": torch.empty((t, d), dtype=torch.float32, device="cuda"),
+         "dyd": [u8(t, d // 2), u8(t, d // 32), u8(d, t // 2), u8(d, t // 32)],
          "dw1": torch.empty((f, d), dtype=torch.float32, device="cuda"),
          "dw3": torch.empty((f, d), dtype=torch.float32, device="cuda")}
 
@@ -50,6 +52,9 @@ def build_step(mx, t=256, d=512, f=384, seed=3):
         mx.fp4_quantize_cols(dv["X"], 32, mask, codes_t=o["xc"][0], scales_t=o["xc"][1])
         mx.fp4_gemm(o["bwd"][0], o["bwd"][1], o["w1c"][0], o["w1c"][1], c=o["dx"])
         mx.fp4_gemm(o["bwd"][2], o["bwd"][3], o["w3c"][0], o["w3c"][1], c=o["dx"], accumulate=True)
+        mx.fp4_gemm_pair(o["bwd"][0], o["bwd"][1], o["w1c"][0], o["w1c"][1], o["bwd"][2], o["bwd"][3], o["w3c"][0],
+                         o["w3c"][1], c=o["dx2"])
+        mx.fp4_quantize_dual(dv["dY"], mx.FP4_SR, seed, 0, 32, mask, *o["dyd"])
         mx.fp4_gemm(o["bwd"][4], o["bwd"][5], o["xc"][0], o["xc"][1], c=o["dw1"])
         mx.fp4_gemm(o["bwd"][6], o["bwd"][7], o["xc"][0], o["xc"][1], c=o["dw3"])
 
@@ -64,8 +69,9 @@ def build_step(mx, t=256, d=512, f=384, seed=3):
     return run, snapshot, o
 
 
-def test_captured_step_replays_match_eager(gpu_lib):
-    run, snapshot, o = build_step(gpu_lib)
+@pytest.mark.parametrize("f", [384, 512])          # generic (K % 256 != 0) and fast kernels
+def test_captured_step_replays_match_eager(gpu_lib, f):
+    run, snapshot, o = build_step(gpu_lib, f=f)
     run()
     eager = snapshot()
     # poison every output, then capture
