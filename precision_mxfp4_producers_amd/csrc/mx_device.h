@@ -160,10 +160,11 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
     const uint64_t p0 = (uint64_t)M0 * c.x, p1 = (uint64_t)M1 * c.z;
     const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
     const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    // three-input XOR in one gfx950 v_bitop3_b32 (truth table 0x96: odd parity)
     u32x4 n;
-    n.x = hi1 ^ c.y ^ k0;
+    n.x = __builtin_amdgcn_bitop3_b32(hi1, c.y, k0, 0x96);
     n.y = lo1;
-    n.z = hi0 ^ c.w ^ k1;
+    n.z = __builtin_amdgcn_bitop3_b32(hi0, c.w, k1, 0x96);
     n.w = lo0;
     c = n;
     k0 += W0;
