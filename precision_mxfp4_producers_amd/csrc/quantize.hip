@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     constexpr int kJ = kDualTok / (kDualThreads / 32);
     const int ch = tid & 31;
     const bool col_ok = ch * 8 < ncol;
-#pragma unroll 4
+#pragma unroll
     for (int j0 = 0; j0 < kJ; j0 += 4) {
       uint4 v[4];
 #pragma unroll
@@ -245,16 +245,15 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
 
   // rows: 128 rows x 32 chunks; a quad covers one 32-value block
   {
-    const int64_t cpr = cols >> 3;
 #pragma unroll 2
-    for (int ci = tid; ci < kDualTok * 32; ci += kDualThreads) {
+    for (int k = 0; k < kDualTok * 32 / kDualThreads; ++k) {
+      const int ci = tid + k * kDualThreads;
       const int r = ci >> 5, ch = ci & 31;
       const uint4 v = *reinterpret_cast<const uint4*>(tile + r * kDualPitch + ch * 16);
       const uint32_t m = max_quad(bf16_absmax8(v.x, v.y, v.z, v.w));
       const int e = upward_exp(m << 16);
       if (r < ntok && ch * 8 < ncol) {
         const int64_t gr = t0 + r, c8 = (c0 >> 3) + ch;
-        (void)cpr;
         const uint32_t packed = encode_row_chunk<kSR>(v, e, gr, cols, c8, seed, offset);
         *reinterpret_cast<uint32_t*>(row_codes + gr * (cols >> 1) + c8 * 4) = packed;
         if ((ch & 3) == 0) row_scales[gr * (cols >> 5) + (c8 >> 2)] = (uint8_t)(e + 127);
