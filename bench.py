@@ -5,12 +5,13 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input.
 The default workload is the full Llama-3-8B SwiGLU FFN step (T 8192, D 4096,
-F 14336): forward (row quantize X, 2D32 W1/W3/W2, fused SwiGLU producer emitting
-h row- and column-facing, W2 Fprop) and backward (row-SR and column-H32 dY from
-one read, W2 Dgrad and Wgrad, the fused SwiGLU backward producer emitting dA/dB row-SR and
-column-H32, column-H32 X, W1/W3 Dgrad as one accumulation over K = 2F, W1/W3
-Wgrad stacked into one launch): nine contractions, 8.66 TFLOP, timed as one captured HIP
-graph (per-call times come from eager steps with events around every call).
+F 14336): forward (row-RTN and column-H32 X from one read, 2D32 W1/W3/W2, fused
+SwiGLU producer emitting h row- and column-facing, W2 Fprop) and backward
+(row-SR and column-H32 dY from one read, W2 Dgrad and Wgrad, the fused SwiGLU
+backward producer emitting dA/dB row-SR and column-H32, W1/W3 Dgrad as one
+accumulation over K = 2F, W1/W3 Wgrad stacked into one launch): nine
+contractions, 8.66 TFLOP, timed as one captured HIP graph (per-call times come
+from eager steps with events around every call).
 
 Prints one JSON line.  `value` = GEMM FLOPs of the step / step time (the
 "quantize+GEMM TFLOP/s": producer time is inside the step).  Timing uses HIP
@@ -151,12 +152,12 @@ class Step:
                            lambda: mx.fp4_quantize_cols(x, 32, self.mask, codes_t=out[0], scales_t=out[1]), 0))
         return out
 
-    def q_dual(self, label, x, offset=0):
-        """Row SR and column H32 of x from one read."""
+    def q_dual(self, label, x, mode=1, offset=0):
+        """Row-facing (SR or RTN) and column-facing H32 of x from one read."""
         mx, (R, C) = self.mx, x.shape
         out = (self.u8(R, C // 2), self.u8(R, C // 32), self.u8(C, R // 2), self.u8(C, R // 32))
         self.calls.append((label, "quant", R * C * B_DUAL,
-                           lambda: mx.fp4_quantize_dual(x, 1, self.seed, offset, 32, self.mask, *out), 0))
+                           lambda: mx.fp4_quantize_dual(x, mode, self.seed, offset, 32, self.mask, *out), 0))
         return out[:2], out[2:]
 
     def q_w(self, label, w, row_codes=None, row_scales=None):
@@ -214,7 +215,11 @@ class Step:
         X, W1, W3, W2, dY = (self.d[k] for k in ("X", "W1", "W3", "W2", "dY"))
         T, D = X.shape
         F = W1.shape[0]
-        xr = self.q_rows("rows(X)", X)
+        if self.fused_backward:
+            # X row RTN (forward) and column H32 (W1/W3 Wgrad) from one read
+            xr, xc_dual = self.q_dual("dual(X: RTN rows, H32 cols)", X, 0)
+        else:
+            xr = self.q_rows("rows(X)", X)
         w13_rc, w13_rs = self.u8(2 * F, D // 2), self.u8(2 * F, D // 32)
         w1 = self.q_w("w2d32(W1)", W1, w13_rc[:F], w13_rs[:F])
         w3 = self.q_w("w2d32(W3)", W3, w13_rc[F:], w13_rs[F:])
@@ -227,7 +232,7 @@ class Step:
                                                           a, b, hr[0], hr[1], hc[0], hc[1]), 0))
         self.gemm("W2 Fprop", hr, w2[:2])
         if self.fused_backward:
-            dyr, dyc = self.q_dual("dual(dY: SR rows, H32 cols)", dY, 0)
+            dyr, dyc = self.q_dual("dual(dY: SR rows, H32 cols)", dY, 1, 0)
         else:
             dyr = self.q_rows("rows(dY,SR)", dY, 1, 0)
             dyc = self.q_cols("cols(dY,H32)", dY)
@@ -253,18 +258,20 @@ class Step:
             dbr = self.q_rows("rows(dB,SR)", db, 1, 2)
             self.q_cols("cols(dA,H32)", da, out=dac)
             self.q_cols("cols(dB,H32)", db, out=dbc)
-        xc = self.q_cols("cols(X,H32)", X)
+        xc = xc_dual if self.fused_backward else self.q_cols("cols(X,H32)", X)
         # dX = dA W1 + dB W3: one contraction over K = 2F (no fp32 read-back of dX)
         self.gemm_pair("W1+W3 Dgrad", dar, w1[2:], dbr, w3[2:])
         self.gemm("W1|W3 Wgrad", dabc, xc)
         # each producer is charged to the first contraction that reads it
-        self.charge = {"swiglu_producer": ["rows(X)", "w2d32(W1)", "w2d32(W3)"], "W2 Fprop": ["w2d32(W2)"],
-                       "W1|W3 Wgrad": ["cols(X,H32)"]}
+        self.charge = {"swiglu_producer": ["w2d32(W1)", "w2d32(W3)"], "W2 Fprop": ["w2d32(W2)"]}
         if self.fused_backward:
+            self.charge["swiglu_producer"].append("dual(X: RTN rows, H32 cols)")
             self.charge["W2 Dgrad"] = ["dual(dY: SR rows, H32 cols)"]
         else:
+            self.charge["swiglu_producer"].append("rows(X)")
             self.charge["W2 Dgrad"] = ["rows(dY,SR)"]
             self.charge["W2 Wgrad"] = ["cols(dY,H32)"]
+            self.charge["W1|W3 Wgrad"] = ["cols(X,H32)"]
         if self.fused_backward:
             self.charge["W1+W3 Dgrad"] = ["swiglu_bwd_producer"]
         else:
