@@ -708,52 +708,54 @@ __device__ __forceinline__ void quantize_h_tile(const uint8_t* smem, int64_t m0,
 }
 
 // ------------------------------------------------------------------ kernels
-// Whole 256x256 C tile through LDS (free after the main loop), 128 rows per
-// pass: waves park their accumulators row-major, then each wave writes whole
-// 1 KB rows with 16-byte stores, so every store instruction covers complete
-// cache lines (a lane-per-row store pattern leaves 64 partly written lines per
-// instruction, which drains at about half the rate).
-constexpr int kCPitch = 260;                // floats per staged row (256 + 4: conflict-free rows)
-static_assert(128 * kCPitch * 4 <= kSmemBytes, "C staging fits in the stage buffers");
+// C out through a private LDS slice per wave (LDS is free after the main
+// loop): each 32x32 sub-tile is parked row-major (144-byte pitch: eight rows
+// at one column land on distinct banks) and read back eight lanes per row, so
+// every 16-byte store instruction writes eight whole 128-byte lines (a
+// lane-per-row pattern leaves 32 partly written lines per instruction, which
+// drains at about half the rate).  No workgroup barrier: waves stage and store
+// independently.  Measured on 8192 x 14336 x 4096: the whole-tile staging with
+// two workgroup-wide passes cost about 5 us per round of tiles.
+constexpr int kCWPitch = 144;               // bytes per staged sub-tile row (128 + 16)
+constexpr int kCWSlice = 32 * kCWPitch;     // bytes per wave
+static_assert(8 * kCWSlice <= kSmemBytes, "C staging slices fit in the stage buffers");
 
-__device__ __forceinline__ void store_c_tile_staged(uint8_t* smem, const v16f (&acc)[4][2], float* __restrict__ c,
-                                                    int64_t ldc, int64_t M, int64_t N, int64_t m0, int64_t n0,
-                                                    int wave, int lane, int wm, int wn, int hl, bool accumulate) {
-  float* cs = reinterpret_cast<float*>(smem);
+__device__ __forceinline__ void store_c_tile_wave(uint8_t* smem, const v16f (&acc)[4][2], float* __restrict__ c,
+                                                  int64_t ldc, int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                                  int wave, int lane, int wm, int wn, int hl, bool accumulate) {
+  uint8_t* buf = smem + wave * kCWSlice;
+  const int r = lane & 31, rr0 = lane >> 3, ch = lane & 7;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    // staged row s holds tile row (s/64)*128 + 64*pass + s%64
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row0 = m0 + wm * 128 + 32 * i;
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int lrow = wm * 64 + ii * 32 + (lane & 31);
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col0 = n0 + wn * 64 + 32 * j;
+      const v16f& a = acc[i][j];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float* dst = cs + lrow * kCPitch + wn * 64 + 32 * j + 4 * hl;
-        const v16f& a = acc[2 * pass + ii][j];
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(buf + r * kCWPitch + (8 * g + 4 * hl) * 4) =
+            make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+      // the wave's LDS operations run in order: the reads see the writes, and
+      // the next sub-tile's writes come after these reads
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<float4*>(dst + 8 * g) = make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
-      }
-    }
-    __syncthreads();
-    const int64_t col = n0 + 4 * lane;
-#pragma unroll 4
-    for (int sr = wave; sr < 128; sr += 8) {
-      const int64_t row = m0 + (sr >> 6) * 128 + 64 * pass + (sr & 63);
-      if (row < M && col < N) {                          // N % 32 == 0: the float4 is all-in
-        float4 v = *reinterpret_cast<const float4*>(cs + sr * kCPitch + 4 * lane);
-        float* p = c + row * ldc + col;
-        if (accumulate) {
-          const float4 prev = *reinterpret_cast<const float4*>(p);
-          v.x = __fadd_rn(prev.x, v.x);
-          v.y = __fadd_rn(prev.y, v.y);
-          v.z = __fadd_rn(prev.z, v.z);
-          v.w = __fadd_rn(prev.w, v.w);
+      for (int k = 0; k < 4; ++k) {
+        const int rr = rr0 + 8 * k;
+        float4 v = *reinterpret_cast<const float4*>(buf + rr * kCWPitch + ch * 16);
+        const int64_t row = row0 + rr;
+        if (row < M && col0 < N) {                       // N % 32 == 0: the sub-tile's columns are all in
+          float* p = c + row * ldc + col0 + 4 * ch;
+          if (accumulate) {
+            const float4 prev = *reinterpret_cast<const float4*>(p);
+            v.x = __fadd_rn(prev.x, v.x);
+            v.y = __fadd_rn(prev.y, v.y);
+            v.z = __fadd_rn(prev.z, v.z);
+            v.w = __fadd_rn(prev.w, v.w);
+          }
+          *reinterpret_cast<float4*>(p) = v;
         }
-        *reinterpret_cast<float4*>(p) = v;
       }
     }
-    __syncthreads();
   }
 }
 
@@ -923,7 +925,7 @@ __global__ __launch_bounds__(kFastThreads) void gemm_fast_kernel(
   Operand A2{a2_codes, a2_scales, M}, B2{b2_codes, b2_scales, N};
   v16f acc[4][2];
   main_loop_fast<false>(smem, A, B, m0, n0, 0, K, acc, wm, wn, &A2, &B2);
-  store_c_tile_staged(smem, acc, c, ldc, M, N, m0, n0, wave, lane, wm, wn, hl, accumulate != 0);
+  store_c_tile_wave(smem, acc, c, ldc, M, N, m0, n0, wave, lane, wm, wn, hl, accumulate != 0);
 }
 
 // SwiGLU producer output tile: 256 tokens x 128 FFN columns.
