@@ -785,25 +785,33 @@ __device__ __forceinline__ void swiglu_epilogue_staged(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int lr = wm * 128 + 32 * i + (lane & 31);
+    // a and b of the lane's 16 columns of row lr in bf16, then SiLU of all 16
+    // in one batch
+    uint32_t ab[4][2], bb[4][2];
+    float av[16], sg[16], sl[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        ab[g][u] = bf16_pack2_rne(acc[i][0][4 * g + 2 * u], acc[i][0][4 * g + 2 * u + 1]);
+        bb[g][u] = bf16_pack2_rne(acc[i][1][4 * g + 2 * u], acc[i][1][4 * g + 2 * u + 1]);
+        av[4 * g + 2 * u] = __uint_as_float(ab[g][u] << 16);
+        av[4 * g + 2 * u + 1] = __uint_as_float(ab[g][u] & 0xFFFF0000u);
+      }
+    sigmoid_silu_n<16>(av, sg, sl);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int dw = (wn * 32 + 8 * g + 4 * hl) >> 1;     // first dword of the lane's 4 columns
-      uint32_t ab[2], bb[2], hb[2];
+      uint32_t hb[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        ab[u] = bf16_pack2_rne(acc[i][0][4 * g + 2 * u], acc[i][0][4 * g + 2 * u + 1]);
-        bb[u] = bf16_pack2_rne(acc[i][1][4 * g + 2 * u], acc[i][1][4 * g + 2 * u + 1]);
-        float sg0, sl0, sg1, sl1;
-        sigmoid_silu(__uint_as_float(ab[u] << 16), sg0, sl0);
-        sigmoid_silu(__uint_as_float(ab[u] & 0xFFFF0000u), sg1, sl1);
-        hb[u] = bf16_pack2_rne(__fmul_rn(sl0, __uint_as_float(bb[u] << 16)),
-                               __fmul_rn(sl1, __uint_as_float(bb[u] & 0xFFFF0000u)));
-      }
+      for (int u = 0; u < 2; ++u)
+        hb[u] = bf16_pack2_rne(__fmul_rn(sl[4 * g + 2 * u], __uint_as_float(bb[g][u] << 16)),
+                               __fmul_rn(sl[4 * g + 2 * u + 1], __uint_as_float(bb[g][u] & 0xFFFF0000u)));
       const int off = lr * kHPitch + 4 * (dw ^ hswz(lr));
       *reinterpret_cast<uint2*>(hs + off) = make_uint2(hb[0], hb[1]);
-      *reinterpret_cast<uint2*>(as + off) = make_uint2(ab[0], ab[1]);
-      bpk[i][g][0] = bb[0];
-      bpk[i][g][1] = bb[1];
+      *reinterpret_cast<uint2*>(as + off) = make_uint2(ab[g][0], ab[g][1]);
+      bpk[i][g][0] = bb[g][0];
+      bpk[i][g][1] = bb[g][1];
     }
   }
   __syncthreads();

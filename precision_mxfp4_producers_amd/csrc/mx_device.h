@@ -216,6 +216,40 @@ __device__ __forceinline__ void sigmoid_silu(float a, float& sig, float& s) {
   s = __fmul_rn(a, sig);
 }
 
+// 1/y for y in [1, 2^126]: the hardware reciprocal and one Newton step with
+// FMAs give the IEEE quotient there (checked on gfx950 for every fp32 y in
+// that range).  Above 2^126 the hardware reciprocal flushes the subnormal
+// results, and +inf gives NaN: callers must take the division there.
+constexpr float kRecipNewtonMax = 0x1p126f;
+__device__ __forceinline__ float recip_newton(float y) {
+  const float r = __builtin_amdgcn_rcpf(y);
+  return __builtin_fmaf(__builtin_fmaf(-y, r, 1.0f), r, r);
+}
+
+// sigmoid_silu for N values at once, same results: the quotient comes from
+// recip_newton unless 1 + exp(-a) exceeds 2^126 (a < -87.3) for some value of
+// some lane of the wave, in which case the whole batch divides (one wave-wide
+// vote per batch, no per-element branch).
+template <int N>
+__device__ __forceinline__ void sigmoid_silu_n(const float (&a)[N], float (&sig)[N], float (&s)[N]) {
+  float y[N];
+  float ymax = 1.0f;                                     // y >= 1; a NaN y drops out (either path suits it)
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    y[k] = __fadd_rn(1.0f, exp_spec(-a[k]));
+    ymax = fmaxf(ymax, y[k]);
+  }
+  if (__builtin_amdgcn_ballot_w64(ymax > kRecipNewtonMax) == 0) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) sig[k] = recip_newton(y[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) sig[k] = __fdiv_rn(1.0f, y[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) s[k] = __fmul_rn(a[k], sig[k]);
+}
+
 // ---------------------------------------------------------------- buffer loads
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
 // return zero, so out-of-range lanes need no branch (a branch around a load

@@ -38,12 +38,15 @@ __global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_kernel(
     const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
     const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
     uint32_t oa[4] = {0u, 0u, 0u, 0u}, ob[4] = {0u, 0u, 0u, 0u};
+    float afv[8], sgv[8], slv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) afv[i] = bf16_bits_to_f32((aw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    sigmoid_silu_n<8>(afv, sgv, slv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float af = bf16_bits_to_f32((aw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+      const float af = afv[i];
       const float bf = bf16_bits_to_f32((bw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-      float sig, s;
-      sigmoid_silu(af, sig, s);
+      const float sig = sgv[i], s = slv[i];
       const float g = __fadd_rn(1.0f, __fmul_rn(af, __fsub_rn(1.0f, sig)));
       const float dav = __fmul_rn(__fmul_rn(__fmul_rn(dv[i], bf), sig), g);
       const float dbv = __fmul_rn(dv[i], s);
@@ -110,18 +113,20 @@ __global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_producer_kernel(
           const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
           const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
           const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+          float afv[8], sig[8], sl[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) afv[i] = bf16_bits_to_f32((aw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+          sigmoid_silu_n<8>(afv, sig, sl);
 #pragma unroll
           for (int i = 0; i < 8; i += 2) {
             float dav[2], dbv[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-              const float af = bf16_bits_to_f32((aw[i >> 1] >> (16 * u)) & 0xFFFFu);
+              const float af = afv[i + u];
               const float bf = bf16_bits_to_f32((bw[i >> 1] >> (16 * u)) & 0xFFFFu);
-              float sig, sl;
-              sigmoid_silu(af, sig, sl);
-              const float g = __fadd_rn(1.0f, __fmul_rn(af, __fsub_rn(1.0f, sig)));
-              dav[u] = __fmul_rn(__fmul_rn(__fmul_rn(dv[i + u], bf), sig), g);
-              dbv[u] = __fmul_rn(dv[i + u], sl);
+              const float g = __fadd_rn(1.0f, __fmul_rn(af, __fsub_rn(1.0f, sig[i + u])));
+              dav[u] = __fmul_rn(__fmul_rn(__fmul_rn(dv[i + u], bf), sig[i + u]), g);
+              dbv[u] = __fmul_rn(dv[i + u], sl[i + u]);
             }
             oa4[i >> 1] = bf16_pack2_rne(dav[0], dav[1]);
             ob4[i >> 1] = bf16_pack2_rne(dbv[0], dbv[1]);

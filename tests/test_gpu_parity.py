@@ -274,6 +274,26 @@ def test_swiglu_producer(gpu_lib, tfd, emit_cols):
         assert_same(hts, want_c[1], "h col scales")
 
 
+@pytest.mark.parametrize("tfd", [(256, 128, 512), (288, 160, 256)])
+def test_swiglu_producer_wide_range(gpu_lib, tfd):
+    """Pre-activations spread over about +-300, so many waves hold some
+    a < -87.3 (1 + exp(-a) > 2^126, where the batch divides instead of using
+    the Newton reciprocal) and others none: h codes still bit-exact."""
+    t, f, d = tfd
+    x = synthetic.tensor((t, d), std=1.0, seed=27)
+    w13 = synthetic.tensor((2 * f, d), std=4.0, seed=28)
+    mask = P.sign_mask_from_seed(2)
+    xr = gpu_lib.fp4_quantize_rows(dev16(x))
+    wq = gpu_lib.fp4_quantize_w2d32(dev16(w13), 0.87)
+    a, b, hc, hs, htc, hts = gpu_lib.fp4_swiglu_producer(xr[0], xr[1], wq[0], wq[1], mask, True)
+    av = F.bf16_bits_to_f64(host16(a))
+    assert (av < -87.4).any() and (av > -87.0).any()
+    h = S.swiglu_h(host16(a), host16(b))
+    for got, want, nm in zip((hc, hs, htc, hts), Q.quantize_rows(h) + Q.quantize_cols(h, 32, mask),
+                             ("h row codes", "h row scales", "h col codes", "h col scales")):
+        assert_same(got, want, nm)
+
+
 @pytest.mark.parametrize("tf", [(64, 288), (256, 512), (32, 32)])
 def test_swiglu_backward(gpu_lib, tf):
     t, f = tf
