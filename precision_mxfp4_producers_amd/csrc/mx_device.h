@@ -187,11 +187,12 @@ __device__ __forceinline__ float exp_spec(float x) {
   const float LOG2E = 0x1.715476p+0f;                      // RN(1/ln 2)
   const float LN2_HI = 0.693359375f;                       // 355/512
   const float LN2_LO = -0x1.bd0106p-13f;                   // RN(ln 2 - 355/512)
-  // out-of-range inputs run the polynomial on 0 and are replaced at the end:
-  // no branch (a branch per element splits the unrolled element loops into
-  // exec-masked regions the scheduler cannot interleave)
-  const bool over = x > 89.0f, under = x < -104.0f;
-  const float xs = (over || under) ? 0.0f : x;
+  // inputs beyond [-104, 89] clamp to its ends, where this same arithmetic
+  // already gives +inf (x = 89) and +0 (x = -104): one v_med3, no branch (a
+  // branch per element splits the unrolled element loops into exec-masked
+  // regions the scheduler cannot interleave).  A NaN x may come out finite;
+  // every caller multiplies by the NaN argument itself, so results stay NaN.
+  const float xs = __builtin_amdgcn_fmed3f(x, -104.0f, 89.0f);
   float n = rintf(__fmul_rn(xs, LOG2E));
   float r = __fsub_rn(__fsub_rn(xs, __fmul_rn(n, LN2_HI)), __fmul_rn(n, LN2_LO));
   float p = 0x1.a01a02p-13f;                               // RN(1/7!)
@@ -206,8 +207,7 @@ __device__ __forceinline__ float exp_spec(float x) {
   // 2^(n - floor(n/2)), whose first step is exact here, equals gfx950's
   // v_ldexp_f32 for every fp32 p in [0.5, 2) and n in [-160, 130] (checked on
   // the GPU; here p in [0.7, 1.42], n in [-150, 128])
-  const float e = __builtin_amdgcn_ldexpf(p, (int)n);
-  return under ? 0.0f : (over ? __builtin_inff() : e);
+  return __builtin_amdgcn_ldexpf(p, (int)n);
 }
 
 // sig = 1/(1+exp(-a)), s = a*sig
