@@ -9,19 +9,21 @@ and fusion changes data movement, not the model.
 Reading of the precision chain (the pages print none): the serial BF16
 schedule.  a, b are the fp32 GEMM outputs rounded to bf16 (RNE) and saved;
 all further steps are single fp32 IEEE round-to-nearest operations in the
-written order, with no fused multiply-add:
+written order, with no fused multiply-add outside exp_spec:
   sig = 1 / (1 + exp_spec(-a));  s = a * sig;  h = bf16(s * b)
   dA  = bf16(((dH * b) * sig) * (1 + a * (1 - sig)));  dB = bf16(dH * s)
 dH is the fp32 output of the W2 Dgrad contraction, used without rounding.
 
 exp_spec is a textbook Cody-Waite exponential written from its definition, so
-that both sides can evaluate it identically:
+that both sides can evaluate it identically.  fma(u, v, w) is RN_fp32(u*v + w)
+with a single rounding:
   n  = rint(x * LOG2E)                       (fp32 product, ties to even)
-  r  = (x - n * LN2_HI) - n * LN2_LO         (LN2_HI = 355/512: n * LN2_HI exact)
-  p  = degree-7 Taylor polynomial of e^r in Horner form, coefficients RN_fp32(1/k!)
+  r  = fma(-n, LN2_LO, fma(-n, LN2_HI, x))   (LN2_HI = 355/512: n * LN2_HI exact)
+  p  = degree-7 Taylor polynomial of e^r, coefficients RN_fp32(1/k!), in Horner
+       form with one fma per degree
   e^x = (p * 2^floor(n/2)) * 2^(n - floor(n/2))
   x > 89 -> +inf, x < -104 -> +0.
-Accuracy against float64 exp is pinned in the tests.
+Accuracy against float64 exp and the exactness of fma_f32 are pinned in the tests.
 """
 
 import math
@@ -43,16 +45,42 @@ def _pow2_f32(n):
     return ((n + 127).astype(np.uint32) << np.uint32(23)).view(np.float32)
 
 
+def fma_f32(a, b, c):
+    """RN_fp32(a*b + c) with one rounding, for fp32 a, b, c (finite results).
+
+    a*b is exact in float64 (two 24-bit significands).  s = fl64(a*b + c) and
+    its two-sum error e satisfy a*b + c = s + e exactly.  An fp32 midpoint is
+    itself a float64, so the exact sum and s lie on the same side of every
+    midpoint unless s is one: rounding s to fp32 is then already correct, and
+    at a midpoint the sign of e decides (e = 0: ties to even).
+    """
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    c = np.asarray(c, dtype=np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        p = a.astype(np.float64) * b.astype(np.float64)
+        c64 = c.astype(np.float64)
+        s = p + c64
+        bv = s - p
+        e = (p - (s - bv)) + (c64 - bv)
+        r = s.astype(np.float32)
+        r64 = r.astype(np.float64)
+        other = np.nextafter(r, np.where(s > r64, np.float32(np.inf), np.float32(-np.inf)).astype(np.float32))
+        mid = (s != r64) & (2.0 * s == r64 + other.astype(np.float64))
+        hi, lo = np.maximum(r, other), np.minimum(r, other)
+        r = np.where(mid & (e > 0), hi, np.where(mid & (e < 0), lo, r))
+    return np.asarray(r, dtype=np.float32)
+
+
 def exp_spec(x):
     x = np.asarray(x, dtype=np.float32)
     with np.errstate(over="ignore", under="ignore", invalid="ignore"):
         xc = np.clip(x, EXP_X_LO, EXP_X_HI).astype(np.float32)
         n = np.rint((xc * LOG2E_F32).astype(np.float32)).astype(np.float32)
-        r = ((xc - (n * LN2_HI_F32).astype(np.float32)).astype(np.float32)
-             - (n * LN2_LO_F32).astype(np.float32)).astype(np.float32)
+        r = fma_f32(-n, LN2_LO_F32, fma_f32(-n, LN2_HI_F32, xc))
         p = EXP_COEFFS_F32[7]
         for k in range(6, -1, -1):
-            p = ((p * r).astype(np.float32) + EXP_COEFFS_F32[k]).astype(np.float32)
+            p = fma_f32(p, r, EXP_COEFFS_F32[k])
         ni = n.astype(np.int64)
         n1 = np.floor_divide(ni, 2)
         n2 = ni - n1

@@ -181,7 +181,9 @@ __device__ __forceinline__ u32x4 sr_words(uint64_t blk, uint64_t seed, uint64_t 
 
 // ---------------------------------------------------------------- exp
 // Cody-Waite exponential used by the SwiGLU producer and its backward; every
-// operation is one fp32 IEEE rounding (no contraction), matching the oracle.
+// operation is one fp32 IEEE rounding, matching the oracle: the two reduction
+// steps and the seven Horner steps are fused multiply-adds (v_fma_f32, one
+// rounding each), everything else is plain.
 
 __device__ __forceinline__ float exp_spec(float x) {
   const float LOG2E = 0x1.715476p+0f;                      // RN(1/ln 2)
@@ -193,16 +195,17 @@ __device__ __forceinline__ float exp_spec(float x) {
   // regions the scheduler cannot interleave).  A NaN x may come out finite;
   // every caller multiplies by the NaN argument itself, so results stay NaN.
   const float xs = __builtin_amdgcn_fmed3f(x, -104.0f, 89.0f);
-  float n = rintf(__fmul_rn(xs, LOG2E));
-  float r = __fsub_rn(__fsub_rn(xs, __fmul_rn(n, LN2_HI)), __fmul_rn(n, LN2_LO));
+  const float n = rintf(__fmul_rn(xs, LOG2E));
+  // |n| <= 150, so n * LN2_HI (8 x 9 significant bits) is exact in the first step
+  const float r = __builtin_fmaf(-n, LN2_LO, __builtin_fmaf(-n, LN2_HI, xs));
   float p = 0x1.a01a02p-13f;                               // RN(1/7!)
-  p = __fadd_rn(__fmul_rn(p, r), 0x1.6c16c2p-10f);          // RN(1/6!)
-  p = __fadd_rn(__fmul_rn(p, r), 0x1.111112p-7f);           // RN(1/5!)
-  p = __fadd_rn(__fmul_rn(p, r), 0x1.555556p-5f);           // RN(1/4!)
-  p = __fadd_rn(__fmul_rn(p, r), 0x1.555556p-3f);           // RN(1/3!)
-  p = __fadd_rn(__fmul_rn(p, r), 0.5f);                    // 1/2!
-  p = __fadd_rn(__fmul_rn(p, r), 1.0f);                    // 1/1!
-  p = __fadd_rn(__fmul_rn(p, r), 1.0f);                    // 1/0!
+  p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);                // RN(1/6!)
+  p = __builtin_fmaf(p, r, 0x1.111112p-7f);                 // RN(1/5!)
+  p = __builtin_fmaf(p, r, 0x1.555556p-5f);                 // RN(1/4!)
+  p = __builtin_fmaf(p, r, 0x1.555556p-3f);                 // RN(1/3!)
+  p = __builtin_fmaf(p, r, 0.5f);                          // 1/2!
+  p = __builtin_fmaf(p, r, 1.0f);                          // 1/1!
+  p = __builtin_fmaf(p, r, 1.0f);                          // 1/0!
   // p * 2^n with one rounding: the two-step product (p * 2^floor(n/2)) *
   // 2^(n - floor(n/2)), whose first step is exact here, equals gfx950's
   // v_ldexp_f32 for every fp32 p in [0.5, 2) and n in [-160, 130] (checked on

@@ -80,6 +80,60 @@ def test_gemm_library_special_case_and_bound():
     assert G.within_bound(c32 + prev, C, E, c_prev=prev).all()
 
 
+def _rn_f32_exact(q):
+    """Nearest fp32 to the rational q (ties to even), by exact comparison of candidates."""
+    x = np.float32(float(q))
+    cands = [np.nextafter(x, np.float32(-np.inf)), x, np.nextafter(x, np.float32(np.inf))]
+    best = min(abs(Fraction(float(c)) - q) for c in cands)
+    near = [c for c in cands if abs(Fraction(float(c)) - q) == best]
+    if len(near) > 1:
+        near = [c for c in near if int(np.float32(c).view(np.uint32)) % 2 == 0]
+    return np.float32(near[0])
+
+
+def _midpoint_factors(down):
+    """24-bit A, B with A*B = 2^47 + j (down: 2^47 - j), 1 <= j < 2^18."""
+    for A in range(1 << 23, 1 << 24):
+        B = -(-(1 << 47) // A) if not down else (1 << 47) // A
+        j = abs(A * B - (1 << 47))
+        if 1 <= j < (1 << 18) and B < (1 << 24):
+            return A, B
+    raise AssertionError("no factors")
+
+
+def test_fma_f32_single_rounding():
+    rng = np.random.default_rng(21)
+    n = 3000
+    a = (rng.standard_normal(n) * np.exp2(rng.integers(-20, 20, n))).astype(np.float32)
+    b = (rng.standard_normal(n) * np.exp2(rng.integers(-20, 20, n))).astype(np.float32)
+    c = (rng.standard_normal(n) * np.exp2(rng.integers(-40, 40, n))).astype(np.float32)
+    c[: n // 3] = -(a[: n // 3] * b[: n // 3])            # cancellation: the product's rounding error
+    c[n // 3: n // 2] = 0.0
+    # a*b + c lands an fp64 rounding exactly on an fp32 midpoint, the exact sum just above (up)
+    # or just below (down) it: a plain fp64-then-fp32 rounding goes the wrong way in both
+    A, B = _midpoint_factors(False)
+    a_up, b_up = np.float32(A * 2.0 ** -24), np.float32(B * 2.0 ** -47)
+    A, B = _midpoint_factors(True)
+    a_dn, b_dn = np.float32(A * 2.0 ** -24), np.float32(B * 2.0 ** -47)
+    c_dn = np.float32(1 + 2.0 ** -23)
+    a = np.concatenate([a, [a_up, a_dn, np.float32(2.0 ** -75)]]).astype(np.float32)
+    b = np.concatenate([b, [b_up, b_dn, np.float32(2.0 ** -70)]]).astype(np.float32)
+    c = np.concatenate([c, [np.float32(1.0), c_dn, np.float32(2.0 ** -140)]]).astype(np.float32)
+    got = S.fma_f32(a, b, c)
+    for i in range(len(a)):
+        want = _rn_f32_exact(Fraction(float(a[i])) * Fraction(float(b[i])) + Fraction(float(c[i])))
+        assert got[i].view(np.uint32) == want.view(np.uint32), (i, a[i], b[i], c[i], got[i], want)
+    assert got[-3] == np.float32(1 + 2.0 ** -23)           # naive double rounding gives 1.0
+    assert got[-2] == c_dn                                 # naive double rounding gives 1 + 2^-22
+    assert (np.float32(1.0) + np.float32(2.0 ** -24)) == np.float32(1.0)
+    # exact product error: fl(a*b) + fma(a, b, -fl(a*b)) == a*b in float64 (no underflow here)
+    x = (rng.standard_normal(5000) * 8).astype(np.float32)
+    y = (rng.standard_normal(5000) * 8).astype(np.float32)
+    pr = (x * y).astype(np.float32)
+    err = S.fma_f32(x, y, -pr)
+    assert np.array_equal(pr.astype(np.float64) + err.astype(np.float64), x.astype(np.float64) * y.astype(np.float64))
+
+
 def test_exp_spec_accuracy():
     x = np.linspace(-87.0, 88.0, 400_001, dtype=np.float32)
     x = np.concatenate([x, np.float32([0.0, -0.0, 1e-8, -1e-8, 0.3465, -0.3466])])
