@@ -105,9 +105,9 @@ def f32_to_bf16_rne(x):
 
 def sigmoid_silu(a_f32):
     one = np.float32(1.0)
-    with np.errstate(over="ignore"):
+    with np.errstate(over="ignore", invalid="ignore"):
         sig = (one / (one + exp_spec(-a_f32)).astype(np.float32)).astype(np.float32)
-    s = (a_f32 * sig).astype(np.float32)
+        s = (a_f32 * sig).astype(np.float32)
     return sig, s
 
 

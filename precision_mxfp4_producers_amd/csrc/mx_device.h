@@ -19,14 +19,14 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> packed bf16 (x low), round to nearest even, NaN -> 0x7FC0.
 // gfx950's v_cvt_pk_bf16_f32 rounds to nearest even on every non-NaN fp32
-// pattern (checked against the integer rounding on all 2^32 inputs); NaNs keep
-// a payload there, so they are replaced by the canonical quiet NaN.
+// pattern (checked against the integer rounding on all 2^32 inputs); a NaN
+// keeps its sign and upper payload bits there, so NaN inputs are first
+// replaced by the canonical fp32 quiet NaN 0x7FC00000, which converts to
+// 0x7FC0 (one compare and one select per value).
 __device__ __forceinline__ uint32_t bf16_pack2_rne(float x, float y) {
-  const bf16x2_t v = {(__bf16)x, (__bf16)y};
-  uint32_t r = __builtin_bit_cast(uint32_t, v);
-  r = (x != x) ? ((r & 0xFFFF0000u) | 0x7FC0u) : r;
-  r = (y != y) ? ((r & 0x0000FFFFu) | 0x7FC00000u) : r;
-  return r;
+  const float qnan = __uint_as_float(0x7FC00000u);
+  const bf16x2_t v = {(__bf16)((x != x) ? qnan : x), (__bf16)((y != y) ? qnan : y)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // fp32 -> bf16 bits, round to nearest even; NaN -> 0x7FC0.

@@ -300,8 +300,14 @@ def test_swiglu_backward(gpu_lib, tf):
     a = synthetic.tensor((t, f), std=1.3, seed=24)
     b = synthetic.tensor((t, f), std=1.3, seed=25)
     a[0, :8] = np.array([0x0000, 0x8000, 0x4300, 0xC300, 0x42C8, 0xC2C8, 0x7F7F, 0xFF7F], dtype=np.uint16)
+    # non-finite inputs: NaNs with payloads and either sign, infinities; every NaN result is 0x7FC0
+    a[1, :8] = np.array([0x7FC1, 0xFFC0, 0x7F81, 0x7F80, 0xFF80, 0x3F80, 0xBF80, 0x0000], dtype=np.uint16)
+    b[1, 4:8] = np.array([0x7F80, 0xFFA0, 0x0000, 0x7FFF], dtype=np.uint16)
     rng = np.random.default_rng(26)
     dh = (rng.standard_normal((t, f)) * 1e-3).astype(np.float32)
+    dh[1, 8:12] = np.array([np.inf, -np.inf, np.nan, 0.0], dtype=np.float32)
+    dh[1, 12:16] = np.uint32([0x7FC00001, 0xFFC00000, 0x7FA00000, 0x7F800001]).view(np.float32)
+    b[1, 8:16] = np.array([0x0000, 0x3F80, 0x3F80, 0x7F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80], dtype=np.uint16)
     da, db = gpu_lib.fp4_swiglu_backward(torch.from_numpy(dh).cuda(), dev16(a), dev16(b))
     want_da, want_db = S.swiglu_backward(dh, a, b)
     assert np.array_equal(host16(da), want_da)
