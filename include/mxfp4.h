@@ -178,9 +178,11 @@ fp4_status fp4_gemm_pair(int64_t m, int64_t n, int64_t k,
  * Fused gated-FFN producer (§3.2): a = X W1^T and b = X W3^T computed together
  * on the block-scaled MFMA, rounded to bf16 (RNE) and saved for backward; then
  *   sig = 1/(1 + exp(-a)), s = a*sig, h = bf16(s*b)
- * in fp32 with single roundings and no fused multiply-add (exp: Cody-Waite
- * reduction with LN2 split 355/512 + remainder, degree-7 Taylor polynomial in
- * Horner form, two-step power-of-two scaling; x > 89 -> inf, x < -104 -> 0).
+ * in fp32 with single roundings and no fused multiply-add outside the exp
+ * (exp: Cody-Waite reduction with LN2 split 355/512 + remainder, degree-7
+ * Taylor polynomial in Horner form, the reduction and Horner steps as fused
+ * multiply-adds with one rounding each, two-step power-of-two scaling;
+ * x > 89 -> inf, x < -104 -> 0; a NaN result of any step is stored as 0x7FC0).
  * h is emitted directly as MXFP4: row-facing RTN (input of W2 Fprop) and,
  * if ht_codes is non-NULL, column-facing with H32 (input of W2 Wgrad).
  *   x_codes [t][d/2], x_scales [t][d/32]       (Q_r(X))
@@ -200,7 +202,8 @@ fp4_status fp4_swiglu_producer(int64_t t, int64_t f, int64_t d,
 
 /*
  * SwiGLU backward, elementwise (§3.2), from the fp32 W2 Dgrad output dH and
- * the saved bf16 a, b, in fp32 with single roundings and no FMA:
+ * the saved bf16 a, b, in fp32 with single roundings and no FMA outside the
+ * exp (the same exp as fp4_swiglu_producer); NaN results are stored as 0x7FC0:
  *   dA = bf16(((dH*b)*sig) * (1 + a*(1 - sig))),   dB = bf16(dH*(a*sig))
  *   dh [t][lddh] fp32; a_bf16, b_bf16, da_bf16, db_bf16 [t][f]
  */

@@ -3,7 +3,8 @@
 // gate/up outputs a, b,
 //   sig = 1/(1+exp(-a)), s = a*sig
 //   dA = bf16(((dH*b)*sig) * (1 + a*(1 - sig))),  dB = bf16(dH*s)
-// with single fp32 roundings in this order and no FMA.  HBM-bound: 12 bytes
+// with single fp32 roundings in this order and no FMA outside the exp (whose
+// reduction and Horner steps are fused multiply-adds).  HBM-bound: 12 bytes
 // per element (4 read dH, 2+2 read a/b, 2+2 written dA/dB).
 //
 // The fused backward producer applies the same arithmetic and emits dA and dB
