@@ -227,8 +227,9 @@ fp4_status fp4_swiglu_backward(int64_t t, int64_t f, const float* dh, int64_t ld
  *   da_codes, db_codes [t][f/2]; da_scales, db_scales [t][f/32]
  *   dat_codes, dbt_codes [f][t/2]; dat_scales, dbt_scales [f][t/32]
  * Errors: FP4_EINVAL null pointer; FP4_ESHAPE t or f negative or not a
- * multiple of 32, lddh < f; FP4_EALIGN dh, a, b or a code buffer not 16-byte aligned, or lddh
- * not a multiple of 4.
+ * multiple of 32, lddh < f, or lddh >= 2^23 (the kernel addresses a 64-row
+ * chunk of dh with 32-bit offsets); FP4_EALIGN dh, a, b or a code buffer not
+ * 16-byte aligned, or lddh not a multiple of 4.
  */
 fp4_status fp4_swiglu_backward_producer(int64_t t, int64_t f, const float* dh, int64_t lddh,
                                         const uint16_t* a_bf16, const uint16_t* b_bf16,

@@ -83,6 +83,38 @@ struct FbOut {
   uint64_t offset;                                       // SR counter offset
 };
 
+// Inputs of one chunk for one thread: rows rg + 16k (k = 0..3), 8 columns.
+struct FbIn {
+  float4 d[4][2];
+  uint4 a[4], b[4];
+};
+
+// Chunk `ck` of the workgroup's tile (t0, c0): buffer resources span the
+// chunk's rows that lie inside the tensor (none for a chunk past the tile), so
+// loads of later rows return zero; columns past f are sent past every
+// resource (kOffNone).  Byte offsets stay below 2^31: 64 rows x lddh x 4 with
+// lddh < 2^23, checked on the host.
+__device__ __forceinline__ void fb_load(FbIn& in, const float* dh, int64_t lddh, const uint16_t* a,
+                                        const uint16_t* b, int64_t Fdim, int64_t t0, int64_t c0, int ntok, int ck,
+                                        int rg, int cc, bool col_ok) {
+  const int rows = max(0, min(kFbChunk, ntok - ck * kFbChunk));
+  const int64_t r0 = t0 + (int64_t)ck * kFbChunk;
+  const int64_t base = rows > 0 ? r0 : t0;               // keep the base inside the tensor
+  const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(dh + base * lddh + c0, (int64_t)rows * lddh * 4);
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a + base * Fdim + c0, (int64_t)rows * Fdim * 2);
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(b + base * Fdim + c0, (int64_t)rows * Fdim * 2);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t r = (uint32_t)(rg + 16 * k);
+    const uint32_t od = col_ok ? r * (uint32_t)lddh * 4u + (uint32_t)cc * 32u : kOffNone;
+    const uint32_t oab = col_ok ? r * (uint32_t)Fdim * 2u + (uint32_t)cc * 16u : kOffNone;
+    in.d[k][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rd, od, 0, 0));
+    in.d[k][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rd, od + 16u, 0, 0));
+    in.a[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, oab, 0, 0));
+    in.b[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, oab, 0, 0));
+  }
+}
+
 __global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_producer_kernel(
     int64_t T, int64_t Fdim, const float* __restrict__ dh, int64_t lddh, const uint16_t* __restrict__ a,
     const uint16_t* __restrict__ b, FbOut oa, FbOut ob, uint64_t seed, uint32_t sign_mask16) {
@@ -94,49 +126,53 @@ __global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_producer_kernel(
   const int ncol = (int)min<int64_t>(kFbCols, Fdim - c0);          // multiple of 32
   const int ntok = (int)min<int64_t>(kFbTok, T - t0);              // multiple of 32
 
-  for (int ck = 0; ck * kFbChunk < ntok; ++ck) {
+  // 1. dA, dB inputs of a chunk: thread (8 columns from cc*8, rows rg + 16k)
+  // through buffer resources over the chunk's valid rows, so rows past T and
+  // columns past f read zero and need no branch; the next chunk's loads are
+  // issued right after this chunk's values are consumed and arrive while its
+  // SR and H32 passes run.
+  const int cc = tid & 15, rg = tid >> 4;
+  const bool col_ok = cc * 8 < ncol;
+  const int nchunks = (ntok + kFbChunk - 1) / kFbChunk;
+  FbIn in;
+  fb_load(in, dh, lddh, a, b, Fdim, t0, c0, ntok, 0, rg, cc, col_ok);
+  for (int ck = 0; ck < nchunks; ++ck) {
     const int nrow = min(kFbChunk, ntok - ck * kFbChunk);           // 32 or 64
     const int64_t r0 = t0 + ck * kFbChunk;
-    // 1. dA, dB
     {
-      const int cc = tid & 15, rg = tid >> 4;
-      const bool col_ok = cc * 8 < ncol;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int r = rg + 16 * k;
-        uint32_t oa4[4] = {0u, 0u, 0u, 0u}, ob4[4] = {0u, 0u, 0u, 0u};
-        if (col_ok && r < nrow) {
-          const float* dp = dh + (r0 + r) * lddh + c0 + cc * 8;
-          const float4 d0 = *reinterpret_cast<const float4*>(dp);
-          const float4 d1 = *reinterpret_cast<const float4*>(dp + 4);
-          const uint4 av = *reinterpret_cast<const uint4*>(a + (r0 + r) * Fdim + c0 + cc * 8);
-          const uint4 bv = *reinterpret_cast<const uint4*>(b + (r0 + r) * Fdim + c0 + cc * 8);
-          const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-          const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-          const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
-          float afv[8], sig[8], sl[8];
+        // zero inputs (rows or columns past the tensor) give +0 for dA and dB
+        const float dv[8] = {in.d[k][0].x, in.d[k][0].y, in.d[k][0].z, in.d[k][0].w,
+                             in.d[k][1].x, in.d[k][1].y, in.d[k][1].z, in.d[k][1].w};
+        const uint32_t aw[4] = {in.a[k].x, in.a[k].y, in.a[k].z, in.a[k].w};
+        const uint32_t bw[4] = {in.b[k].x, in.b[k].y, in.b[k].z, in.b[k].w};
+        uint32_t oa4[4], ob4[4];
+        float afv[8], sig[8], sl[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) afv[i] = bf16_bits_to_f32((aw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-          sigmoid_silu_n<8>(afv, sig, sl);
+        for (int i = 0; i < 8; ++i) afv[i] = bf16_bits_to_f32((aw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+        sigmoid_silu_n<8>(afv, sig, sl);
 #pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            float dav[2], dbv[2];
+        for (int i = 0; i < 8; i += 2) {
+          float dav[2], dbv[2];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const float af = afv[i + u];
-              const float bf = bf16_bits_to_f32((bw[i >> 1] >> (16 * u)) & 0xFFFFu);
-              const float g = __fadd_rn(1.0f, __fmul_rn(af, __fsub_rn(1.0f, sig[i + u])));
-              dav[u] = __fmul_rn(__fmul_rn(__fmul_rn(dv[i + u], bf), sig[i + u]), g);
-              dbv[u] = __fmul_rn(dv[i + u], sl[i + u]);
-            }
-            oa4[i >> 1] = bf16_pack2_rne(dav[0], dav[1]);
-            ob4[i >> 1] = bf16_pack2_rne(dbv[0], dbv[1]);
+          for (int u = 0; u < 2; ++u) {
+            const float af = afv[i + u];
+            const float bf = bf16_bits_to_f32((bw[i >> 1] >> (16 * u)) & 0xFFFFu);
+            const float g = __fadd_rn(1.0f, __fmul_rn(af, __fsub_rn(1.0f, sig[i + u])));
+            dav[u] = __fmul_rn(__fmul_rn(__fmul_rn(dv[i + u], bf), sig[i + u]), g);
+            dbv[u] = __fmul_rn(dv[i + u], sl[i + u]);
           }
+          oa4[i >> 1] = bf16_pack2_rne(dav[0], dav[1]);
+          ob4[i >> 1] = bf16_pack2_rne(dbv[0], dbv[1]);
         }
         *reinterpret_cast<uint4*>(gs[0] + r * kFbPitch + cc * 16) = make_uint4(oa4[0], oa4[1], oa4[2], oa4[3]);
         *reinterpret_cast<uint4*>(gs[1] + r * kFbPitch + cc * 16) = make_uint4(ob4[0], ob4[1], ob4[2], ob4[3]);
       }
     }
+    // the next chunk's inputs (a chunk past the tile reads zero: empty resources)
+    fb_load(in, dh, lddh, a, b, Fdim, t0, c0, ntok, ck + 1, rg, cc, col_ok);
     __syncthreads();
     // 2. row-facing SR: thread (row tid/4, block tid%4) of each tensor
     {
@@ -263,7 +299,7 @@ extern "C" fp4_status fp4_swiglu_backward_producer(
       !aligned16(db_codes) || !aligned16(dat_codes) || !aligned16(dbt_codes) || (lddh % 4) != 0)
     return FP4_EALIGN;
   const int64_t gx = (f + kFbCols - 1) / kFbCols, gy = (t + kFbTok - 1) / kFbTok;
-  if (gy > kMaxGridY) return FP4_ESHAPE;
+  if (gy > kMaxGridY || lddh >= (int64_t(1) << 23)) return FP4_ESHAPE;   // 32-bit buffer offsets
   const FbOut oa{da_codes, da_scales, dat_codes, dat_scales, offset_a};
   const FbOut ob{db_codes, db_scales, dbt_codes, dbt_scales, offset_b};
   hipLaunchKernelGGL(swiglu_bwd_producer_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kBwdThreads), 0,

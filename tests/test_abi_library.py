@@ -94,6 +94,9 @@ def test_argument_errors_are_reported_without_gpu_work():
                                             0, *bufs, None) == 1
     assert lib.fp4_swiglu_backward_producer(32, 32, v(4100), 32, v(4096), v(4096), u64(0), u64(0), u64(1),
                                             0, *bufs, None) == 3
+    # dh row pitch of 2^23 floats or more: the kernel's 32-bit buffer offsets would overflow
+    assert lib.fp4_swiglu_backward_producer(32, 32, v(4096), 1 << 23, v(4096), v(4096), u64(0), u64(0), u64(1),
+                                            0, *bufs, None) == 2
 
 
 def test_empty_calls_are_noops_without_gpu_work():

@@ -343,6 +343,28 @@ def test_swiglu_backward_producer(gpu_lib, tf):
         assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1])
 
 
+@pytest.mark.parametrize("tfp", [(352, 160, 96), (96, 288, 8)])
+def test_swiglu_backward_producer_strided_dh(gpu_lib, tfp):
+    """dH read with a row pitch beyond f (a column slice of a wider buffer),
+    and tiles whose last 64-token chunk holds only 32 tokens."""
+    t, f, pad = tfp
+    a = synthetic.tensor((t, f), std=1.3, seed=43)
+    b = synthetic.tensor((t, f), std=1.3, seed=44)
+    rng = np.random.default_rng(45)
+    wide = (rng.standard_normal((t, f + pad)) * 1e-3).astype(np.float32)
+    dh = np.ascontiguousarray(wide[:, :f])
+    seed, oa, ob, mask = 3, 1, 2, P.sign_mask_from_seed(0)
+    dhd = torch.from_numpy(wide).cuda()[:, :f]
+    assert dhd.stride(0) == f + pad
+    got = gpu_lib.fp4_swiglu_backward_producer(dhd, dev16(a), dev16(b), seed, oa, ob, mask)
+    da, db = S.swiglu_backward(dh, a, b)
+    want = (Q.quantize_rows(da, Q.SR, seed, oa), Q.quantize_rows(db, Q.SR, seed, ob),
+            Q.quantize_cols(da, 32, mask), Q.quantize_cols(db, 32, mask))
+    for g, w, nm in zip(got, want, ("dA rows", "dB rows", "dA cols", "dB cols")):
+        assert_same(g[0], w[0], nm + " codes")
+        assert_same(g[1], w[1], nm + " scales")
+
+
 def test_empty_tensors(gpu_lib):
     """Empty inputs give empty outputs (no launch)."""
     x = torch.empty((0, 64), dtype=torch.int16, device="cuda")
