@@ -111,13 +111,14 @@ constexpr int kColRowsPerLoad = kThreads / kColChunks;   // token rows one load 
 constexpr int kColPitch = kColW * 2 + 4;                 // bytes per staged token row (+4: spread banks)
 constexpr int kColCodePitch = kColTok / 2 + 16;          // bytes per staged column of codes
 static_assert(kColTok % kColRowsPerLoad == 0 && kColTok % 32 == 0 && kColW % 32 == 0, "column tile shape");
+static_assert((kColW / 2) * (kColTok / 32) == kThreads, "one column item per lane");
+static_assert(kColW * kColCodePitch <= kColTok * kColPitch, "column codes fit in the tile buffer");
 
 template <bool kH32>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, uint32_t sign_mask16) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kColTok * kColPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t ctile[kColW * kColCodePitch];
   __shared__ uint8_t stile[kColW][kColTok / 32];
   const int tid = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * kColW, t0 = (int64_t)blockIdx.y * kColTok;
@@ -145,28 +146,38 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
   }
   __syncthreads();
 
-  // encode: item (column pair i % (kColW/2), token block i / (kColW/2))
-  for (int i = tid; i < (kColW / 2) * (kColTok / 32); i += kThreads) {
-    const int cp = i % (kColW / 2), tb = i / (kColW / 2);
-    if (2 * cp < ncol && 32 * tb < ntok) {
-      uint32_t v[32];
+  // encode: one item (column pair tid % (kColW/2), token block tid / (kColW/2))
+  // per lane; the codes are kept in registers until every lane has read its
+  // values, then parked in the tile buffer (one LDS array: four workgroups
+  // per CU)
+  const int cp = tid % (kColW / 2), tb = tid / (kColW / 2);
+  const bool live = 2 * cp < ncol && 32 * tb < ntok;
+  uint4 code[2];
+  int ex[2];
+  {
+    uint32_t v[32];
 #pragma unroll
-      for (int k = 0; k < 32; ++k) v[k] = *reinterpret_cast<const uint32_t*>(tile + (32 * tb + k) * kColPitch + cp * 4);
+    for (int k = 0; k < 32; ++k) v[k] = *reinterpret_cast<const uint32_t*>(tile + (32 * tb + k) * kColPitch + cp * 4);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float f[32];
+    for (int c = 0; c < 2; ++c) {
+      float f[32];
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
-          uint32_t bb = (v[k] >> (16 * c)) & 0xFFFFu;
-          if constexpr (kH32) bb ^= ((sign_mask16 >> (k & 15)) & 1u) << 15;   // d_(k mod 16)
-          f[k] = bf16_bits_to_f32(bb);
-        }
-        if constexpr (kH32) h32_fp32(f);
-        int e;
-        const uint4 code = encode32_rtn(f, e);
-        *reinterpret_cast<uint4*>(ctile + (2 * cp + c) * kColCodePitch + tb * 16) = code;
-        stile[2 * cp + c][tb] = (uint8_t)(e + 127);
+      for (int k = 0; k < 32; ++k) {
+        uint32_t bb = (v[k] >> (16 * c)) & 0xFFFFu;
+        if constexpr (kH32) bb ^= ((sign_mask16 >> (k & 15)) & 1u) << 15;   // d_(k mod 16)
+        f[k] = bf16_bits_to_f32(bb);
       }
+      if constexpr (kH32) h32_fp32(f);
+      code[c] = encode32_rtn(f, ex[c]);
+    }
+  }
+  __syncthreads();
+  uint8_t* ctile = tile;
+  if (live) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      *reinterpret_cast<uint4*>(ctile + (2 * cp + c) * kColCodePitch + tb * 16) = code[c];
+      stile[2 * cp + c][tb] = (uint8_t)(ex[c] + 127);
     }
   }
   __syncthreads();
@@ -546,7 +557,8 @@ fp4_status fp4_quantize_w2d32(const uint16_t* w, int64_t n, int64_t k, int64_t l
   const int64_t gk = (k + 127) / 128, gy = (n + 127) / 128;
   if (gy > kMaxGridY || ldw >= ((int64_t)1 << 22)) return FP4_ESHAPE;   // 128-row strips stay < 2 GiB
   // about 512 workgroups (2 per CU, each long-running), each walking a run of
-  // consecutive macro tiles along K
+  // consecutive macro tiles along K (three per CU, with the registers held to
+  // 168 per lane, measured 10-15% slower on 8192-14336 x 4096)
   const int64_t want_x = std::max<int64_t>(1, 512 / gy);
   const int per = (int)((gk + want_x - 1) / want_x);
   const int64_t gx = (gk + per - 1) / per;
