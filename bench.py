@@ -2,6 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--eager] [--unfused-backward] [--quality] [--copy-calibration]
+                    [--quantizer-sweep]
 
 A step is one pass of the whole hot path over one batch of synthetic input.
 The default workload is the full Llama-3-8B SwiGLU FFN step (T 8192, D 4096,
@@ -61,6 +62,9 @@ def parse():
                    help="numerical quality of the MXFP4 contractions against fp32 on the bf16 inputs, with ablations")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of known size (for scaling HBM byte counters)")
+    p.add_argument("--quantizer-sweep", action="store_true",
+                   help="each producer alone at the FFN step's shapes after a read-only cache flush, beside a plain "
+                        "streaming kernel with the same bytes read and written per element")
     return p.parse_args()
 
 
@@ -106,6 +110,61 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
                       "launches": 3}), flush=True)
+
+
+def quantizer_sweep(mx, torch, reps=9):
+    """Each producer alone, after a read-only pass over 1 GiB (evicts the
+    256 MB Infinity Cache without leaving dirty lines), timed with HIP events;
+    beside it a plain elementwise kernel with the same traffic per element
+    (reads 2 B, writes 0.5 B: a not-equal over the bf16 pairs as int32 into a
+    bool per pair), which shows what a simple streaming kernel reaches at that
+    size on this part."""
+    import synthetic
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    dev = torch.device("cuda:0")
+
+    def timed(fn):
+        ts = []
+        for r in range(reps + 2):
+            flush.max()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    mask = mx.fp4_sign_mask_from_seed(0)
+    rows = []
+    for (R, C) in ((8192, 4096), (14336, 4096), (8192, 14336)):
+        x = torch.from_numpy(synthetic.tensor((R, C), std=1.0, seed=5).view(np.int16)).to(dev)
+        n = R * C
+        pairs = x.view(torch.int32).view(-1)
+        flags = torch.empty(pairs.numel(), dtype=torch.bool, device=dev)
+        rc, rs = torch.empty((R, C // 2), dtype=torch.uint8, device=dev), torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
+        cc, cs = torch.empty((C, R // 2), dtype=torch.uint8, device=dev), torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
+        ref_ms = timed(lambda: torch.ne(pairs, 0, out=flags))
+        ref_gbps = n * 2.5 / (ref_ms * 1e-3) / 1e9
+        calls = [
+            ("rows RTN", B_SINGLE, lambda: mx.fp4_quantize_rows(x, 0, 0, 0, codes=rc, scales=rs)),
+            ("rows SR", B_SINGLE, lambda: mx.fp4_quantize_rows(x, 1, 0, 0, codes=rc, scales=rs)),
+            ("cols H32", B_SINGLE, lambda: mx.fp4_quantize_cols(x, 32, mask, codes_t=cc, scales_t=cs)),
+            ("dual RTN rows + H32 cols", B_DUAL, lambda: mx.fp4_quantize_dual(x, 0, 0, 0, 32, mask, rc, rs, cc, cs)),
+            ("dual SR rows + H32 cols", B_DUAL, lambda: mx.fp4_quantize_dual(x, 1, 0, 0, 32, mask, rc, rs, cc, cs)),
+            ("2D32", B_2D32, lambda: mx.fp4_quantize_w2d32(x, 0.87, rc, rs, cc, cs)),
+        ]
+        for label, bpe, fn in calls:
+            ms = timed(fn)
+            gbps = n * bpe / (ms * 1e-3) / 1e9
+            rows.append({"shape": f"{R}x{C}", "call": label, "us": round(ms * 1e3, 1), "gbps": round(gbps, 1),
+                         "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                         "frac_streaming_reference": round(gbps / ref_gbps, 4)})
+        rows.append({"shape": f"{R}x{C}", "call": "streaming reference (2 B in, 0.5 B out)",
+                     "us": round(ref_ms * 1e3, 1), "gbps": round(ref_gbps, 1),
+                     "frac_hbm_peak": round(ref_gbps / PEAK_HBM_GBPS, 4), "frac_streaming_reference": 1.0})
+    return rows
 
 
 class Step:
@@ -442,6 +501,9 @@ def main():
     torch.cuda.set_device(0)
     if args.quality:
         print(json.dumps({"quality": quality_report(mx, torch)}), flush=True)
+        return
+    if args.quantizer_sweep:
+        print(json.dumps({"quantizer_sweep": quantizer_sweep(mx, torch)}), flush=True)
         return
     print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
     step = Step(args.workload, args.seed, mx, torch, fused_backward=not args.unfused_backward)
