@@ -61,19 +61,28 @@ __global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_kernel(
 
 
 // ------------------------------------------------------------ fused producer
-// A workgroup owns kFbCols FFN columns x kFbTok tokens, walked in chunks of
-// kFbChunk tokens:
-//   1. dA, dB of the chunk in bf16 into LDS (thread: 8 columns x 4 rows);
-//   2. row-facing SR of every 32-column block (thread: one block of one row;
-//      four threads cover a row's 64 code bytes), draws indexed by the
-//      element's row-major index in the full [t][f] tensor;
-//   3. column-facing H32 of every 32-token block (thread: one column pair),
-//      codes parked in LDS per column;
+// A workgroup of kFbThreads lanes owns kFbCols FFN columns x kFbTok tokens,
+// walked in chunks of kFbChunk tokens:
+//   1. dA, dB of the chunk in bf16 into LDS (lane: 8 columns x 2 rows);
+//   2. row-facing SR of every 32-column block (lane: one block of one row of
+//      one tensor; four lanes cover a row's 64 code bytes), draws indexed by
+//      the element's row-major index in the full [t][f] tensor;
+//   3. column-facing H32 of every 32-token block (lane: one column of one
+//      tensor), codes parked in LDS per column;
 // and finally each column's kFbTok/2 code bytes -- a whole 128-byte line --
-// go out with coalesced stores.
+// go out with coalesced stores.  The kernel is ALU-bound (the exp chain, the
+// Philox draws, the H32 butterflies): the LDS (two workgroups per CU) sets the
+// occupancy, so each workgroup has eight waves and the per-lane work is
+// split finely enough that a lane stays within 128 registers (four waves per
+// SIMD).
+constexpr int kFbThreads = 512;
 constexpr int kFbCols = 128, kFbTok = 256, kFbChunk = 64;
+constexpr int kFbRowsPerLane = kFbChunk * (kFbCols / 8) / kFbThreads;   // 2
 constexpr int kFbPitch = 272;                            // bytes per staged bf16 row (256 + 16)
 constexpr int kFbCodePitch = kFbTok / 2 + 16;            // bytes per staged column of codes
+static_assert(kFbRowsPerLane * kFbThreads == kFbChunk * (kFbCols / 8), "phase 1 covers the chunk");
+static_assert(2 * kFbChunk * (kFbCols / 32) == kFbThreads, "phase 2: one (tensor, row, block) per lane");
+static_assert(2 * (kFbChunk / 32) * kFbCols == kFbThreads, "phase 3: one (tensor, token block, column) per lane");
 
 struct FbOut {
   uint8_t* codes;                                        // row-facing [t][f/2]
@@ -83,10 +92,10 @@ struct FbOut {
   uint64_t offset;                                       // SR counter offset
 };
 
-// Inputs of one chunk for one thread: rows rg + 16k (k = 0..3), 8 columns.
+// Inputs of one chunk for one lane: rows rg + 32k (k < kFbRowsPerLane), 8 columns.
 struct FbIn {
-  float4 d[4][2];
-  uint4 a[4], b[4];
+  float4 d[kFbRowsPerLane][2];
+  uint4 a[kFbRowsPerLane], b[kFbRowsPerLane];
 };
 
 // Chunk `ck` of the workgroup's tile (t0, c0): buffer resources span the
@@ -104,8 +113,8 @@ __device__ __forceinline__ void fb_load(FbIn& in, const float* dh, int64_t lddh,
   const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a + base * Fdim + c0, (int64_t)rows * Fdim * 2);
   const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(b + base * Fdim + c0, (int64_t)rows * Fdim * 2);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t r = (uint32_t)(rg + 16 * k);
+  for (int k = 0; k < kFbRowsPerLane; ++k) {
+    const uint32_t r = (uint32_t)(rg + 32 * k);
     const uint32_t od = col_ok ? r * (uint32_t)lddh * 4u + (uint32_t)cc * 32u : kOffNone;
     const uint32_t oab = col_ok ? r * (uint32_t)Fdim * 2u + (uint32_t)cc * 16u : kOffNone;
     in.d[k][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rd, od, 0, 0));
@@ -115,7 +124,7 @@ __device__ __forceinline__ void fb_load(FbIn& in, const float* dh, int64_t lddh,
   }
 }
 
-__global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_producer_kernel(
+__global__ __launch_bounds__(kFbThreads) void swiglu_bwd_producer_kernel(
     int64_t T, int64_t Fdim, const float* __restrict__ dh, int64_t lddh, const uint16_t* __restrict__ a,
     const uint16_t* __restrict__ b, FbOut oa, FbOut ob, uint64_t seed, uint32_t sign_mask16) {
   __shared__ __attribute__((aligned(16))) uint8_t gs[2][kFbChunk * kFbPitch];          // dA, dB chunk
@@ -126,7 +135,7 @@ __global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_producer_kernel(
   const int ncol = (int)min<int64_t>(kFbCols, Fdim - c0);          // multiple of 32
   const int ntok = (int)min<int64_t>(kFbTok, T - t0);              // multiple of 32
 
-  // 1. dA, dB inputs of a chunk: thread (8 columns from cc*8, rows rg + 16k)
+  // 1. dA, dB inputs of a chunk: lane (8 columns from cc*8, rows rg + 32k)
   // through buffer resources over the chunk's valid rows, so rows past T and
   // columns past f read zero and need no branch; the next chunk's loads are
   // issued right after this chunk's values are consumed and arrive while its
@@ -141,8 +150,8 @@ __global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_producer_kernel(
     const int64_t r0 = t0 + ck * kFbChunk;
     {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int r = rg + 16 * k;
+      for (int k = 0; k < kFbRowsPerLane; ++k) {
+        const int r = rg + 32 * k;
         // zero inputs (rows or columns past the tensor) give +0 for dA and dB
         const float dv[8] = {in.d[k][0].x, in.d[k][0].y, in.d[k][0].z, in.d[k][0].w,
                              in.d[k][1].x, in.d[k][1].y, in.d[k][1].z, in.d[k][1].w};
@@ -174,80 +183,75 @@ __global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_producer_kernel(
     // the next chunk's inputs (a chunk past the tile reads zero: empty resources)
     fb_load(in, dh, lddh, a, b, Fdim, t0, c0, ntok, ck + 1, rg, cc, col_ok);
     __syncthreads();
-    // 2. row-facing SR: thread (row tid/4, block tid%4) of each tensor
+    // 2. row-facing SR: lane (tensor tid/256, row (tid/4)%64, block tid%4);
+    // the tensor is uniform over each wave
     {
-      const int r = tid >> 2, blk = tid & 3;
+      const int k = tid >> 8, r = (tid >> 2) & 63, blk = tid & 3;
+      const FbOut& o = k ? ob : oa;
       const int64_t row = r0 + r, col0 = c0 + 32 * blk;
       const bool ok = r < nrow && 32 * blk < ncol;
+      uint32_t w[16];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const FbOut& o = k ? ob : oa;
-        uint32_t w[16];
+      for (int q = 0; q < 4; ++q) {
+        const uint4 d = *reinterpret_cast<const uint4*>(gs[k] + r * kFbPitch + blk * 64 + q * 16);
+        w[4 * q] = d.x; w[4 * q + 1] = d.y; w[4 * q + 2] = d.z; w[4 * q + 3] = d.w;
+      }
+      uint32_t m = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 d = *reinterpret_cast<const uint4*>(gs[k] + r * kFbPitch + blk * 64 + q * 16);
-          w[4 * q] = d.x; w[4 * q + 1] = d.y; w[4 * q + 2] = d.z; w[4 * q + 3] = d.w;
+      for (int q = 0; q < 4; ++q) m = max(m, bf16_absmax8(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]));
+      const int e = upward_exp(m << 16);
+      const float inv = inv_pow2(e);
+      const uint64_t blk0 = ((uint64_t)row * (uint64_t)Fdim + (uint64_t)col0) >> 2;   // first Philox counter
+      uint32_t packed[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {                      // 8 elements per output word
+        const u32x4 u0 = sr_words(blk0 + 2 * q, seed, o.offset);
+        const u32x4 u1 = sr_words(blk0 + 2 * q + 1, seed, o.offset);
+        const uint32_t u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        uint32_t pk = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t bits = (w[4 * q + (j >> 1)] >> (16 * (j & 1))) & 0xFFFFu;
+          const uint32_t mag = bits & 0x7FFFu;
+          const float y = bf16_bits_to_f32(mag) * inv;
+          pk |= (e2m1_sr(y, u[j], min(mag, 1u)) | ((bits >> 12) & 8u)) << (4 * j);
         }
-        uint32_t m = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) m = max(m, bf16_absmax8(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]));
-        const int e = upward_exp(m << 16);
-        const float inv = inv_pow2(e);
-        const uint64_t blk0 = ((uint64_t)row * (uint64_t)Fdim + (uint64_t)col0) >> 2;   // first Philox counter
-        uint32_t packed[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {                    // 8 elements per output word
-          const u32x4 u0 = sr_words(blk0 + 2 * q, seed, o.offset);
-          const u32x4 u1 = sr_words(blk0 + 2 * q + 1, seed, o.offset);
-          const uint32_t u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-          uint32_t pk = 0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t bits = (w[4 * q + (j >> 1)] >> (16 * (j & 1))) & 0xFFFFu;
-            const uint32_t mag = bits & 0x7FFFu;
-            const float y = bf16_bits_to_f32(mag) * inv;
-            pk |= (e2m1_sr(y, u[j], min(mag, 1u)) | ((bits >> 12) & 8u)) << (4 * j);
-          }
-          packed[q] = pk;
-        }
-        if (ok) {
-          *reinterpret_cast<uint4*>(o.codes + row * (Fdim >> 1) + (col0 >> 1)) =
-              make_uint4(packed[0], packed[1], packed[2], packed[3]);
-          o.scales[row * (Fdim >> 5) + (col0 >> 5)] = (uint8_t)(e + 127);
-        }
+        packed[q] = pk;
+      }
+      if (ok) {
+        *reinterpret_cast<uint4*>(o.codes + row * (Fdim >> 1) + (col0 >> 1)) =
+            make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        o.scales[row * (Fdim >> 5) + (col0 >> 5)] = (uint8_t)(e + 127);
       }
     }
-    // 3. column-facing H32: thread (tensor tid/128, token block (tid/64)%2, column pair tid%64)
+    // 3. column-facing H32: lane (tensor tid/256, column-in-pair (tid/128)%2,
+    // token block (tid/64)%2, column pair tid%64); all but the pair index are
+    // uniform over each wave
     {
-      const int k = tid >> 7, tb = (tid >> 6) & 1, cp = tid & 63;
+      const int k = tid >> 8, c = (tid >> 7) & 1, tb = (tid >> 6) & 1, cp = tid & 63;
       if (32 * tb < nrow && 2 * cp < ncol) {
-        uint32_t v[32];
+        float f[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = *reinterpret_cast<const uint32_t*>(gs[k] + (32 * tb + i) * kFbPitch + cp * 4);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          float f[32];
-#pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            uint32_t bb = (v[i] >> (16 * c)) & 0xFFFFu;
-            bb ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;   // d_(i mod 16)
-            f[i] = bf16_bits_to_f32(bb);
-          }
-          h32_fp32(f);
-          int e;
-          const uint4 code = encode32_rtn(f, e);
-          const int tblk = ck * (kFbChunk / 32) + tb;   // token block within the workgroup
-          *reinterpret_cast<uint4*>(cs[k] + (2 * cp + c) * kFbCodePitch + tblk * 16) = code;
-          ss[k][2 * cp + c][tblk] = (uint8_t)(e + 127);
+        for (int i = 0; i < 32; ++i) {
+          const uint32_t v = *reinterpret_cast<const uint32_t*>(gs[k] + (32 * tb + i) * kFbPitch + cp * 4);
+          uint32_t bb = (v >> (16 * c)) & 0xFFFFu;
+          bb ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;   // d_(i mod 16)
+          f[i] = bf16_bits_to_f32(bb);
         }
+        h32_fp32(f);
+        int e;
+        const uint4 code = encode32_rtn(f, e);
+        const int tblk = ck * (kFbChunk / 32) + tb;     // token block within the workgroup
+        *reinterpret_cast<uint4*>(cs[k] + (2 * cp + c) * kFbCodePitch + tblk * 16) = code;
+        ss[k][2 * cp + c][tblk] = (uint8_t)(e + 127);
       }
     }
     __syncthreads();
   }
-  // 4. column codes out: piece p = (tensor, column, 16-byte piece); 8 threads per column
+  // 4. column codes out: piece p = (tensor, column, 16-byte piece); 8 lanes per column
 #pragma unroll
-  for (int pass = 0; pass < 8; ++pass) {
-    const int p = tid + kBwdThreads * pass;
+  for (int pass = 0; pass < 2 * kFbCols * (kFbTok / 32) / kFbThreads; ++pass) {
+    const int p = tid + kFbThreads * pass;
     const int k = p >> 10, col = (p >> 3) & 127, q = p & 7;
     if (col < ncol && 32 * q < ntok) {
       const FbOut& o = k ? ob : oa;
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_producer_kernel(
           *reinterpret_cast<const uint4*>(cs[k] + col * kFbCodePitch + 16 * q);
     }
   }
-  {
+  if (tid < 2 * kFbCols) {
     const int k = tid >> 7, col = tid & 127;
     if (col < ncol) {
       const FbOut& o = k ? ob : oa;
@@ -302,7 +306,7 @@ extern "C" fp4_status fp4_swiglu_backward_producer(
   if (gy > kMaxGridY || lddh >= (int64_t(1) << 23)) return FP4_ESHAPE;   // 32-bit buffer offsets
   const FbOut oa{da_codes, da_scales, dat_codes, dat_scales, offset_a};
   const FbOut ob{db_codes, db_scales, dbt_codes, dbt_scales, offset_b};
-  hipLaunchKernelGGL(swiglu_bwd_producer_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kBwdThreads), 0,
+  hipLaunchKernelGGL(swiglu_bwd_producer_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kFbThreads), 0,
                      as_stream(stream), t, f, dh, lddh, a_bf16, b_bf16, oa, ob, seed, sign_mask16 & 0xFFFFu);
   return launch_status();
 }
