@@ -8,9 +8,10 @@
 //   §2.5    SR on the Dgrad-facing dY only (Eq. 9); paired H32 on the Wgrad
 //           operands, applied in registers during column quantization (Eq. 10)
 //
-// All producers are HBM-bound: each reads its bf16 input once with coalesced
-// 16-byte (rows, 2D32) or 4-byte-per-lane row segments (cols) and writes packed
-// codes plus one scale byte per 32 values.
+// The RTN producers are HBM-bound: each reads its bf16 input once with
+// coalesced 16-byte loads (the column, dual and 2D32 producers stage the tile
+// in LDS and read it back by columns) and writes packed codes plus one scale
+// byte per 32 values.  The SR producers are bound by the Philox draws.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
