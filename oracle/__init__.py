@@ -16,9 +16,10 @@ Modules
 -------
 formats   E2M1 grid, upward E8M0 exponent, RTN and adjacent-bin SR decisions,
           nibble packing, decode.
-philox    Philox4x32-10 counter generator and the fixed sign mask.
-          PARITY UNPINNED against published known-answer vectors (none are
-          available offline); pinned by structure and statistics only.
+philox    Philox4x32-10 counter generator and the fixed sign mask; pinned
+          against rocRAND's independent Philox4x32-10 engine (host build of
+          its open-source header), since no published known-answer vectors
+          are available offline, and by structure and statistics.
 hadamard  Fixed-sign H32 transform (signs, Sylvester butterfly, 2^-2.5).
 quant     Row-facing, column-facing (optionally H32) and 2D32 producers.
 gemm      Decode-then-contract reference and the per-element error bound.

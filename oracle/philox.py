@@ -16,10 +16,13 @@ where i is the element's row-major index in the logical tensor.  Draws depend
 only on (seed, offset, i), never on tiling, and distinct offsets address
 disjoint counter ranges.
 
-PARITY UNPINNED against published known-answer vectors: none are available
-offline.  The tests pin this module by structure (bijectivity of a round,
-key-schedule and layout invariants) and statistics only; agreement with the GPU
-generator is checked separately.
+Pins: published known-answer vectors are not available offline, so the tests
+check this module against an independent implementation of the same generator,
+rocRAND's host-callable Philox4x32-10 engine compiled from its open-source
+header (every draw and the sign mask, with the SR offset as rocRAND's
+subsequence and the element index as its offset), besides structure
+(bijectivity of a round, key-schedule and layout invariants) and statistics.
+Agreement with the GPU generator is checked separately.
 """
 
 import numpy as np
