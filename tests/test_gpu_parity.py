@@ -343,6 +343,41 @@ def test_swiglu_backward_producer(gpu_lib, tf):
         assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1])
 
 
+def test_swiglu_backward_producer_nonfinite(gpu_lib):
+    """NaN payloads of both signs and infinities in dH, a and b: the fused
+    producer gives the bytes of the unfused calls (whose bf16 dA, dB carry the
+    canonical NaN 0x7FC0), so a wave that meets a NaN takes the canonical
+    packing.  Quantizer codes of non-finite blocks are outside the contract;
+    only the fused/unfused agreement is checked there."""
+    t, f = 128, 256
+    a = synthetic.tensor((t, f), std=1.3, seed=46)
+    b = synthetic.tensor((t, f), std=1.3, seed=47)
+    rng = np.random.default_rng(48)
+    dh = (rng.standard_normal((t, f)) * 1e-3).astype(np.float32)
+    bits = dh.view(np.uint32)
+    bits[3, 5] = 0x7FC00001
+    bits[3, 6] = 0xFFA00000
+    bits[70, 40] = 0x7F800001
+    dh[9, 100] = np.inf
+    dh[9, 101] = -np.inf
+    a[20, 7] = 0x7F80                                    # +inf
+    a[20, 8] = 0xFF80                                    # -inf
+    a[90, 200] = 0x7FC3                                  # NaN with payload
+    b[33, 64] = 0xFFC1
+    b[33, 65] = 0x7F80
+    dhd, ad, bd = torch.from_numpy(dh).cuda(), dev16(a), dev16(b)
+    seed, oa, ob, mask = 5, 1, 2, P.sign_mask_from_seed(2)
+    fused = gpu_lib.fp4_swiglu_backward_producer(dhd, ad, bd, seed, oa, ob, mask)
+    dag, dbg = gpu_lib.fp4_swiglu_backward(dhd, ad, bd)
+    want_da, want_db = S.swiglu_backward(dh, a, b)
+    assert np.array_equal(host16(dag), want_da) and np.array_equal(host16(dbg), want_db)
+    assert (want_da == 0x7FC0).sum() > 0 and (want_db == 0x7FC0).sum() > 0
+    ref = (gpu_lib.fp4_quantize_rows(dag, gpu_lib.FP4_SR, seed, oa), gpu_lib.fp4_quantize_rows(dbg, gpu_lib.FP4_SR, seed, ob),
+           gpu_lib.fp4_quantize_cols(dag, 32, mask), gpu_lib.fp4_quantize_cols(dbg, 32, mask))
+    for got, want, nm in zip(fused, ref, ("dA rows", "dB rows", "dA cols", "dB cols")):
+        assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1]), nm
+
+
 @pytest.mark.parametrize("tfp", [(352, 160, 96), (96, 288, 8)])
 def test_swiglu_backward_producer_strided_dh(gpu_lib, tfp):
     """dH read with a row pitch beyond f (a column slice of a wider buffer),
