@@ -822,8 +822,8 @@ __device__ __forceinline__ void swiglu_epilogue_staged(
     const int r = 32 * p + (tid >> 4);
     const int64_t row = m0 + r, col = n0 + 8 * ch;
     if (row < T && col < Fdim)
-      *reinterpret_cast<uint4*>(a_out + row * Fdim + col) =
-          *reinterpret_cast<const uint4*>(as + r * kHPitch + 4 * ((4 * ch) ^ hswz(r)));
+      __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(as + r * kHPitch + 4 * ((4 * ch) ^ hswz(r))),
+                                  reinterpret_cast<v4i*>(a_out + row * Fdim + col));
   }
   // h row codes: thread (row b/4, block b%4)
 #pragma unroll
@@ -886,8 +886,8 @@ __device__ __forceinline__ void swiglu_epilogue_staged(
     const int r = 32 * p + (tid >> 4);
     const int64_t row = m0 + r, col = n0 + 8 * ch;
     if (row < T && col < Fdim)
-      *reinterpret_cast<uint4*>(b_out + row * Fdim + col) =
-          *reinterpret_cast<const uint4*>(as + r * kHPitch + 4 * ((4 * ch) ^ hswz(r)));
+      __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(as + r * kHPitch + 4 * ((4 * ch) ^ hswz(r))),
+                                  reinterpret_cast<v4i*>(b_out + row * Fdim + col));
   }
 }
 
