@@ -43,6 +43,7 @@ namespace mx {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256;
 constexpr int BKB = 128;                    // code bytes per row per K step (256 values)
@@ -722,7 +723,8 @@ static_assert(8 * kCWSlice <= kSmemBytes, "C staging slices fit in the stage buf
 
 __device__ __forceinline__ void store_c_tile_wave(uint8_t* smem, const v16f (&acc)[4][2], float* __restrict__ c,
                                                   int64_t ldc, int64_t M, int64_t N, int64_t m0, int64_t n0,
-                                                  int wave, int lane, int wm, int wn, int hl, bool accumulate) {
+                                                  int wave, int lane, int wm, int wn, int hl, bool accumulate,
+                                                  bool stream_c) {
   uint8_t* buf = smem + wave * kCWSlice;
   const int r = lane & 31, rr0 = lane >> 3, ch = lane & 7;
 #pragma unroll
@@ -752,7 +754,8 @@ __device__ __forceinline__ void store_c_tile_wave(uint8_t* smem, const v16f (&ac
             v.z = __fadd_rn(prev.z, v.z);
             v.w = __fadd_rn(prev.w, v.w);
           }
-          *reinterpret_cast<float4*>(p) = v;
+          if (stream_c) __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f*>(p));
+          else *reinterpret_cast<float4*>(p) = v;
         }
       }
     }
@@ -917,12 +920,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_generic_kernel(
 }
 
 // a2_codes == nullptr: C (+)= A B^T.  Otherwise C (+)= A B^T + A2 B2^T as one
-// fp32 accumulation over both K ranges (each K long).
+// fp32 accumulation over both K ranges (each K long).  `flags`: bit 0
+// accumulate, bit 1 write C with non-temporal (streaming) stores.
 __global__ __launch_bounds__(kFastThreads) void gemm_fast_kernel(
     int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, const uint8_t* __restrict__ a2_codes,
     const uint8_t* __restrict__ a2_scales, const uint8_t* __restrict__ b2_codes,
-    const uint8_t* __restrict__ b2_scales, float* __restrict__ c, int64_t ldc, int accumulate) {
+    const uint8_t* __restrict__ b2_scales, float* __restrict__ c, int64_t ldc, int flags) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   int64_t tm, tn;
   tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
@@ -933,7 +937,8 @@ __global__ __launch_bounds__(kFastThreads) void gemm_fast_kernel(
   Operand A2{a2_codes, a2_scales, M}, B2{b2_codes, b2_scales, N};
   v16f acc[4][2];
   main_loop_fast<false>(smem, A, B, m0, n0, 0, K, acc, wm, wn, &A2, &B2);
-  store_c_tile_wave(smem, acc, c, ldc, M, N, m0, n0, wave, lane, wm, wn, hl, accumulate != 0);
+  store_c_tile_wave(smem, acc, c, ldc, M, N, m0, n0, wave, lane, wm, wn, hl, (flags & 1) != 0,
+                    (flags & 2) != 0);
 }
 
 // SwiGLU producer output tile: 256 tokens x 128 FFN columns.
@@ -1000,6 +1005,18 @@ __global__ __launch_bounds__(256) void fill_rows_f32_kernel(float* __restrict__ 
 
 using namespace mx;
 
+// Kernel flags of the fast GEMM: accumulate, and streaming (non-temporal) C
+// stores when C is larger than three quarters of the 256 MB Infinity Cache.
+// Such an output cannot stay cached for its reader anyway, and written
+// through the cache it evicts the operands of the next launches (same-box
+// A/B over the FFN step: the 235 and 470 MB Wgrad and Dgrad outputs gained
+// 5-15 us each, and the kernels after them too; the 134 MB outputs lost
+// about 7 us each, so they keep ordinary stores).
+static int fast_flags(int64_t m, int64_t n, int accumulate) {
+  constexpr int64_t kStreamCBytes = (int64_t)192 << 20;
+  return accumulate | (m * n * 4 > kStreamCBytes ? 2 : 0);
+}
+
 extern "C" {
 
 fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
@@ -1026,7 +1043,7 @@ fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, con
   // the fast path needs K % 256 == 0 and buffer offsets below 2^31 per tile
   if ((k % 256) == 0 && 256 * (k / 2) < 0x7FFFFFFF)
     hipLaunchKernelGGL(gemm_fast_kernel, dim3((unsigned)tiles), dim3(kFastThreads), 0, s, m, n, k, a_codes, a_scales,
-                       b_codes, b_scales, nullptr, nullptr, nullptr, nullptr, c, ldc, accumulate);
+                       b_codes, b_scales, nullptr, nullptr, nullptr, nullptr, c, ldc, fast_flags(m, n, accumulate));
   else
     hipLaunchKernelGGL(gemm_generic_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, m, n, k, a_codes,
                        a_scales, b_codes, b_scales, c, ldc, accumulate);
@@ -1053,7 +1070,7 @@ fp4_status fp4_gemm_pair(int64_t m, int64_t n, int64_t k, const uint8_t* a1_code
   if ((k % 256) == 0 && 256 * (k / 2) < 0x7FFFFFFF) {
     hipLaunchKernelGGL(gemm_fast_kernel, dim3((unsigned)tiles), dim3(kFastThreads), 0, as_stream(stream), m, n, k,
                        a1_codes, a1_scales, b1_codes, b1_scales, a2_codes, a2_scales, b2_codes, b2_scales, c, ldc,
-                       accumulate);
+                       fast_flags(m, n, accumulate));
     return launch_status();
   }
   // K not a multiple of 256: the second product is added to the first's result
