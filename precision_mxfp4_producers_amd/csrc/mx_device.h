@@ -253,6 +253,18 @@ __device__ __forceinline__ void sigmoid_silu_n(const float (&a)[N], float (&sig)
   for (int k = 0; k < N; ++k) s[k] = __fmul_rn(a[k], sig[k]);
 }
 
+// ---------------------------------------------------------------- one-shot loads
+// Inputs a kernel reads exactly once (the producers' bf16 tensors, the
+// backward producer's dH, a, b) are loaded with the non-temporal hint, so that
+// streaming them does not evict the freshly written codes and operands that
+// the next launches read from the caches.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_once_u4(const void* p) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+constexpr int kLoadOnce = 2;                             // buffer-load cache policy: non-temporal
+
 // ---------------------------------------------------------------- buffer loads
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
 // return zero, so out-of-range lanes need no branch (a branch around a load

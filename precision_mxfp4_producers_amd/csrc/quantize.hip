@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     for (int j = 0; j < kRowsPerPass; ++j) {
       const int64_t r = r0 + j * rstep;
       v[j] = make_uint4(0u, 0u, 0u, 0u);
-      if (col_ok && r < rows) v[j] = *reinterpret_cast<const uint4*>(x + r * ldx + c8 * 8);
+      if (col_ok && r < rows) v[j] = load_once_u4(x + r * ldx + c8 * 8);
     }
 #pragma unroll
     for (int j = 0; j < kRowsPerPass; ++j) {
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     for (int j = 0; j < kJ; ++j) {
       const int r = tid / kColChunks + kColRowsPerLoad * j;
       v[j] = make_uint4(0u, 0u, 0u, 0u);
-      if (col_ok && r < ntok) v[j] = *reinterpret_cast<const uint4*>(x + (t0 + r) * ldx + c0 + ch * 8);
+      if (col_ok && r < ntok) v[j] = load_once_u4(x + (t0 + r) * ldx + c0 + ch * 8);
     }
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
       for (int u = 0; u < 4; ++u) {
         const int r = (tid >> 5) + (kDualThreads / 32) * (j0 + u);
         v[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (col_ok && r < ntok) v[u] = *reinterpret_cast<const uint4*>(x + (t0 + r) * ldx + c0 + ch * 8);
+        if (col_ok && r < ntok) v[u] = load_once_u4(x + (t0 + r) * ldx + c0 + ch * 8);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -356,7 +356,7 @@ __device__ __forceinline__ void w2d32_load(__amdgpu_buffer_rsrc_t rs, int64_t N,
     const int row = 32 * w + 4 * q + (l >> 4);
     const bool ok = n0 + row < N && col < K;
     const v4i d = __builtin_bit_cast(
-        v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? (uint32_t)(row * ldw + col) * 2u : kOffNone, 0, 0));
+        v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? (uint32_t)(row * ldw + col) * 2u : kOffNone, 0, kLoadOnce));
     v[4 * q] = d[0]; v[4 * q + 1] = d[1]; v[4 * q + 2] = d[2]; v[4 * q + 3] = d[3];
   }
 }
