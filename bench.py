@@ -6,13 +6,13 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input.
 The default workload is the full Llama-3-8B SwiGLU FFN step (T 8192, D 4096,
-F 14336): forward (row-RTN and column-H32 X from one read, 2D32 W1/W3/W2, fused
-SwiGLU producer emitting h row- and column-facing, W2 Fprop) and backward
-(row-SR and column-H32 dY from one read, W2 Dgrad and Wgrad, the fused SwiGLU
-backward producer emitting dA/dB row-SR and column-H32, W1/W3 Dgrad as one
-accumulation over K = 2F, W1/W3 Wgrad stacked into one launch): nine
-contractions, 8.66 TFLOP, timed as one captured HIP graph (per-call times come
-from eager steps with events around every call).
+F 14336), in launch order: forward (row-RTN and column-H32 X from one read,
+2D32 W1/W3, fused SwiGLU producer emitting h row- and column-facing, 2D32 W2,
+W2 Fprop) and backward (row-SR and column-H32 dY from one read, W2 Dgrad and
+Wgrad, the fused SwiGLU backward producer emitting dA/dB row-SR and column-H32,
+W1/W3 Wgrad stacked into one launch, W1/W3 Dgrad as one accumulation over
+K = 2F): nine contractions, 8.66 TFLOP, timed as one captured HIP graph
+(per-call times come from eager steps with events around every call).
 
 Prints one JSON line.  `value` = GEMM FLOPs of the step / step time (the
 "quantize+GEMM TFLOP/s": producer time is inside the step).  Timing uses HIP
@@ -282,13 +282,16 @@ class Step:
         w13_rc, w13_rs = self.u8(2 * F, D // 2), self.u8(2 * F, D // 32)
         w1 = self.q_w("w2d32(W1)", W1, w13_rc[:F], w13_rs[:F])
         w3 = self.q_w("w2d32(W3)", W3, w13_rc[F:], w13_rs[F:])
-        w2 = self.q_w("w2d32(W2)", W2)
         a, b = self.e((T, F), torch.int16), self.e((T, F), torch.int16)
         hr = (self.u8(T, F // 2), self.u8(T, F // 32))
         hc = (self.u8(F, T // 2), self.u8(F, T // 32))
         self.calls.append(("swiglu_producer", "producer", 2.0 * T * 2 * F * D,
                            lambda: mx.fp4_swiglu_producer(xr[0], xr[1], w13_rc, w13_rs, self.mask, True,
                                                           a, b, hr[0], hr[1], hc[0], hc[1]), 0))
+        # W2's producer runs right before the contraction that reads it, so its
+        # codes are still in the Infinity Cache (launch orders measured on one
+        # MI355X: this and the Wgrad-before-Dgrad order below save about 1%)
+        w2 = self.q_w("w2d32(W2)", W2)
         self.gemm("W2 Fprop", hr, w2[:2])
         if self.fused_backward:
             dyr, dyc = self.q_dual("dual(dY: SR rows, H32 cols)", dY, 1, 0)
@@ -318,9 +321,10 @@ class Step:
             self.q_cols("cols(dA,H32)", da, out=dac)
             self.q_cols("cols(dB,H32)", db, out=dbc)
         xc = xc_dual if self.fused_backward else self.q_cols("cols(X,H32)", X)
-        # dX = dA W1 + dB W3: one contraction over K = 2F (no fp32 read-back of dX)
-        self.gemm_pair("W1+W3 Dgrad", dar, w1[2:], dbr, w3[2:])
+        # the stacked Wgrad reads the column-facing dA, dB just written; then
+        # dX = dA W1 + dB W3 as one contraction over K = 2F (no fp32 read-back of dX)
         self.gemm("W1|W3 Wgrad", dabc, xc)
+        self.gemm_pair("W1+W3 Dgrad", dar, w1[2:], dbr, w3[2:])
         # each producer is charged to the first contraction that reads it
         self.charge = {"swiglu_producer": ["w2d32(W1)", "w2d32(W3)"], "W2 Fprop": ["w2d32(W2)"]}
         if self.fused_backward:
