@@ -867,7 +867,8 @@ __device__ __forceinline__ void swiglu_epilogue_staged(
       int e;
       const uint4 code = encode32_rtn(fv, e);
       if (r0 < T && col < Fdim) {
-        *reinterpret_cast<uint4*>(ht_codes + col * (T >> 1) + (r0 >> 1)) = code;
+        __builtin_nontemporal_store(v4i{(int)code.x, (int)code.y, (int)code.z, (int)code.w},
+                                    reinterpret_cast<v4i*>(ht_codes + col * (T >> 1) + (r0 >> 1)));
         ht_scales[col * (T >> 5) + (r0 >> 5)] = (uint8_t)(e + 127);
       }
     }
