@@ -276,6 +276,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 constexpr uint32_t kOffNone = 0x80000000u;               // beyond any resource: reads zero
 
+// ---------------------------------------------------------------- XCD-aware block order
+// The hardware deals a grid's workgroups round-robin to the 8 XCDs in linear
+// order (x fastest), and each XCD has its own L2.  Two workgroups that write
+// the two halves of one 128-byte line should share an L2, or the line is
+// assembled from partial writes of two XCDs.  xcd_block returns the block
+// (bx, by) of a logical order in which `fast` (0: x, 1: y) varies fastest and
+// each XCD owns one contiguous range of it; grids whose size is not a
+// multiple of 8 keep the hardware order.
+__device__ __forceinline__ void xcd_block(int fast, uint32_t& bx, uint32_t& by) {
+  const uint64_t gx = gridDim.x, gy = gridDim.y, num = gx * gy;
+  uint64_t l = blockIdx.x + gx * blockIdx.y;
+  if ((num & 7u) == 0) l = (l & 7u) * (num >> 3) + (l >> 3);
+  if (fast == 0) { bx = (uint32_t)(l % gx); by = (uint32_t)(l / gx); }
+  else { by = (uint32_t)(l % gy); bx = (uint32_t)(l / gy); }
+}
+
 // ---------------------------------------------------------------- reductions
 // max over each group of 4 consecutive lanes (DPP quad permutes; all lanes active)
 __device__ __forceinline__ uint32_t max_quad(uint32_t v) {

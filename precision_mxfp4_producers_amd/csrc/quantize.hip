@@ -441,9 +441,13 @@ __global__ __launch_bounds__(kThreads) void quant_w2d32_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t tile[128 * kWPitch];
   __shared__ __attribute__((aligned(16))) uint8_t ccodes[128 * kWCodePitch];
   __shared__ int tile_e[4][4];
-  const int64_t n0 = (int64_t)blockIdx.y * 128;
+  // neighbouring 128-row strips write the two halves of each column-code
+  // line: keep them on one XCD
+  uint32_t bx, by;
+  xcd_block(1, bx, by);
+  const int64_t n0 = (int64_t)by * 128;
   const int64_t gk = (K + 127) / 128;
-  int64_t kt = (int64_t)blockIdx.x * per;
+  int64_t kt = (int64_t)bx * per;
   const int64_t kt_end = min(gk, kt + per);
   if (kt >= kt_end) return;                              // uniform over the workgroup
   const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w + n0 * ldw, (std::min<int64_t>(128, N - n0) - 1) * ldw * 2 + K * 2);

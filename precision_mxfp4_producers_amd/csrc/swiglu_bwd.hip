@@ -131,7 +131,11 @@ __global__ __launch_bounds__(kFbThreads) void swiglu_bwd_producer_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t cs[2][kFbCols * kFbCodePitch];       // column codes
   __shared__ uint8_t ss[2][kFbCols][kFbTok / 32];                                      // column scales
   const int tid = threadIdx.x;
-  const int64_t c0 = (int64_t)blockIdx.x * kFbCols, t0 = (int64_t)blockIdx.y * kFbTok;
+  // neighbouring column tiles write the two halves of each row-code line:
+  // keep them on one XCD
+  uint32_t bx, by;
+  xcd_block(0, bx, by);
+  const int64_t c0 = (int64_t)bx * kFbCols, t0 = (int64_t)by * kFbTok;
   const int ncol = (int)min<int64_t>(kFbCols, Fdim - c0);          // multiple of 32
   const int ntok = (int)min<int64_t>(kFbTok, T - t0);              // multiple of 32
 
