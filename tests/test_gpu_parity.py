@@ -128,7 +128,8 @@ def test_dual(gpu_lib, shape, mode, had):
         assert torch.equal(g, w)
 
 
-@pytest.mark.parametrize("shape", [(512, 512), (352, 416), (32, 64), (4096, 160)])
+@pytest.mark.parametrize("shape", [(512, 512), (352, 416), (32, 64), (4096, 160),
+                                   (1024, 256)])   # 2 x 8 workgroups: the XCD-aware block order
 @pytest.mark.parametrize("ratio", [0.87, 0.0])
 def test_w2d32(gpu_lib, shape, ratio):
     w = synthetic.tensor(shape, std=0.02, seed=15)
@@ -314,7 +315,8 @@ def test_swiglu_backward(gpu_lib, tf):
     assert np.array_equal(host16(db), want_db)
 
 
-@pytest.mark.parametrize("tf", [(256, 256), (288, 160), (64, 96), (32, 32), (320, 416), (512, 128)])
+@pytest.mark.parametrize("tf", [(256, 256), (288, 160), (64, 96), (32, 32), (320, 416), (512, 128),
+                                (512, 1024)])   # 8 x 2 workgroups: the XCD-aware block order
 def test_swiglu_backward_producer(gpu_lib, tf):
     """Fused backward producer == SwiGLU backward, then SR rows and H32 cols
     of dA and dB (oracle composition and the unfused GPU calls)."""
