@@ -13,6 +13,18 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running CPU test")
 
 
+# Every GPU test gets its own time limit (thread method: it can interrupt a test
+# blocked inside a GPU call), so a stuck kernel ends that test with its name
+# instead of stalling the whole run.  The whole GPU suite runs in about 20 s.
+GPU_TEST_TIMEOUT_S = 180
+
+
+def pytest_collection_modifyitems(config, items):
+    for item in items:
+        if item.get_closest_marker("gpu") is not None and item.get_closest_marker("timeout") is None:
+            item.add_marker(pytest.mark.timeout(GPU_TEST_TIMEOUT_S, method="thread"))
+
+
 @pytest.fixture(scope="session")
 def gpu_lib():
     """The HIP binding; GPU tests fail loudly if the library or device is missing."""
