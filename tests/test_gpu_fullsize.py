@@ -171,6 +171,27 @@ def test_wgrad_h32_8192x14336x4096(gpu_lib):
     check_gemm(dw, dyc, xc, rng, "Wgrad")
 
 
+def test_gemm_streamed_c_ragged(gpu_lib):
+    """A C larger than 192 MB is written with non-temporal stores; here with M
+    and N that are not multiples of the 256 x 256 tile, plain and accumulating."""
+    m, n, k = 7200, 7232, 512
+    assert m * n * 4 > (192 << 20)
+    rng = np.random.default_rng(104)
+    x = synthetic.tensor((m, k), std=1.0, seed=61, outlier_rate=0.001, outlier_scale=20.0)
+    w = synthetic.tensor((n, k), std=0.02, seed=62)
+    a = gpu_lib.fp4_quantize_rows(dev(x))
+    b = gpu_lib.fp4_quantize_rows(dev(w))
+    c = gpu_lib.fp4_gemm(a[0], a[1], b[0], b[1])
+    check_gemm(c, a, b, rng, "streamed C")
+    c_first = c.clone()
+    gpu_lib.fp4_gemm(a[0], a[1], b[0], b[1], c=c, accumulate=True)
+    check_gemm(c, a, b, rng, "streamed C (+=)",
+               c_prev=lambda ms_, ns_: host(cols_of(rows_of(c_first, ms_), ns_)))
+    a2 = gpu_lib.fp4_quantize_rows(dev(synthetic.tensor((m, k), std=1e-3, seed=63)))
+    cp = gpu_lib.fp4_gemm_pair(a[0], a[1], b[0], b[1], a2[0], a2[1], b[0], b[1])
+    check_gemm_pair(cp, a, b, a2, b, rng, "streamed C, paired")
+
+
 @pytest.mark.parametrize("name", ["ffn_step_8192x4096x14336", "ffn_large_32768x8192x28672"])
 def test_ffn_step(gpu_lib, name):
     """The whole SwiGLU FFN step, forward and backward, as the benchmark runs it."""
