@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 constexpr int kColTok = MX_COL_TOK, kColW = MX_COL_W;
 constexpr int kColChunks = kColW / 8;                    // 16-byte chunks per token row
 constexpr int kColRowsPerLoad = kThreads / kColChunks;   // token rows one load instruction round covers
-constexpr int kColPitch = kColW * 2 + 4;                 // bytes per staged token row (+4: spread banks)
+constexpr int kColPitch = kColW * 2 + 16;                // bytes per staged token row (16-byte aligned rows)
 constexpr int kColCodePitch = kColTok / 2 + 16;          // bytes per staged column of codes
 static_assert(kColTok % kColRowsPerLoad == 0 && kColTok % 32 == 0 && kColW % 32 == 0, "column tile shape");
 static_assert((kColW / 2) * (kColTok / 32) == kThreads, "one column item per lane");
@@ -141,8 +141,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       const int r = tid / kColChunks + kColRowsPerLoad * j;
-      uint32_t* d = reinterpret_cast<uint32_t*>(tile + r * kColPitch + ch * 16);
-      d[0] = v[j].x; d[1] = v[j].y; d[2] = v[j].z; d[3] = v[j].w;
+      *reinterpret_cast<uint4*>(tile + r * kColPitch + ch * 16) = v[j];
     }
   }
   __syncthreads();
@@ -214,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 // tensor: the same per-block encoders run on the same values.
 constexpr int kDualTok = 128, kDualW = 256;
 constexpr int kDualThreads = 512;                        // one column item per lane
-constexpr int kDualPitch = kDualW * 2 + 4;               // bytes per staged token row
+constexpr int kDualPitch = kDualW * 2 + 16;              // bytes per staged token row (16-byte aligned rows)
 constexpr int kDualCodePitch = kDualTok / 2 + 16;        // bytes per staged column of codes
 static_assert(kDualW * kDualCodePitch <= kDualTok * kDualPitch, "column codes fit in the tile buffer");
 
@@ -248,8 +247,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = (tid >> 5) + (kDualThreads / 32) * (j0 + u);
-        uint32_t* d = reinterpret_cast<uint32_t*>(tile + r * kDualPitch + ch * 16);
-        d[0] = v[u].x; d[1] = v[u].y; d[2] = v[u].z; d[3] = v[u].w;
+        *reinterpret_cast<uint4*>(tile + r * kDualPitch + ch * 16) = v[u];
       }
     }
   }
