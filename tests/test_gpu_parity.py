@@ -83,6 +83,26 @@ def test_rows_strided_input(gpu_lib):
     assert_same(scales, want[1], "scales")
 
 
+def test_cols_dual_w2d32_strided_input(gpu_lib):
+    """The column, single-read and 2D32 producers on a row-strided view
+    (ldx = 640, cols = 512, starting 64 values into each row)."""
+    full = synthetic.tensor((96, 640), std=1.0, seed=21, outlier_rate=0.01, outlier_scale=30.0)
+    x = np.ascontiguousarray(full[:, 64:576])
+    xd = dev16(full)[:, 64:576]
+    mask = P.sign_mask_from_seed(7)
+    codes_t, scales_t = gpu_lib.fp4_quantize_cols(xd, 32, mask)
+    want_c = Q.quantize_cols(x, 32, mask)
+    assert_same(codes_t, want_c[0], "col codes")
+    assert_same(scales_t, want_c[1], "col scales")
+    got = gpu_lib.fp4_quantize_dual(xd, 1, 11, 2, 32, mask)
+    want_r = Q.quantize_rows(x, Q.SR, 11, 2)
+    for g, w, nm in zip(got, want_r + want_c, ("row codes", "row scales", "col codes", "col scales")):
+        assert_same(g, w, "dual " + nm)
+    got = gpu_lib.fp4_quantize_w2d32(xd, 0.87)
+    for g, w, nm in zip(got, Q.quantize_w2d32(x, 0.87), ("row codes", "row scales", "col codes", "col scales")):
+        assert_same(g, w, "2D32 " + nm)
+
+
 def test_rows_extreme_values(gpu_lib):
     # subnormals, huge values and tiny-next-to-huge blocks (SR threshold at 1)
     rng = np.random.default_rng(3)
