@@ -39,7 +39,12 @@
  *     a = b = h = +0 and quantizes that h as usual (the H32 view of a zero
  *     block holds the signed zeros the fixed signs produce).
  *   - Outputs must not alias inputs or each other.
- *   - Inputs must be finite; Inf/NaN inputs give unspecified codes.
+ *   - Inputs must be finite; Inf/NaN inputs give unspecified codes.  With
+ *     the fixed-sign H32 (hadamard = 32, and the H32 views of the fused
+ *     producers) the transformed values must be finite too: every 32-token
+ *     block's fp32 butterfly sums must stay below 2^128, which |x| < 2^122
+ *     guarantees; a block beyond that has no upward scale and unspecified
+ *     codes.
  *   - Each call validates its arguments on the host, enqueues its kernels on
  *     `stream` (a hipStream_t; NULL = default stream) and returns without
  *     synchronising.  Results are valid once the stream has reached them.
@@ -85,6 +90,9 @@ enum { FP4_RTN = 0, FP4_SR = 1 };
  * checkpoint (seed, offset) so resumed runs never reuse draws (App. A.1).
  *   x       [rows][ldx] bf16, reads rows x cols
  *   codes   [rows][cols/2] u8,   scales [rows][cols/32] u8
+ * Errors: FP4_EINVAL bad mode or null pointer; FP4_ESHAPE rows < 0, cols not
+ * a non-negative multiple of 32, or ldx < cols; FP4_EALIGN x or codes not
+ * 16-byte aligned, or ldx not a multiple of 8.
  */
 fp4_status fp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* codes, uint8_t* scales,
@@ -101,6 +109,10 @@ fp4_status fp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
  * same sign_mask16.  hadamard = 0 quantizes the values directly.
  *   x        [rows][ldx] bf16
  *   codes_t  [cols][rows/2] u8,   scales_t [cols][rows/32] u8
+ * Errors: FP4_EINVAL hadamard not 0 or 32, or null pointer; FP4_ESHAPE rows
+ * or cols not a non-negative multiple of 32, ldx < cols, or rows > 8388480
+ * (more than 65535 tiles of 128 tokens); FP4_EALIGN x or codes_t not 16-byte
+ * aligned, or ldx not a multiple of 8.
  */
 fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* codes_t, uint8_t* scales_t,
@@ -116,7 +128,9 @@ fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int6
  *   x         [rows][ldx] bf16
  *   row_codes [rows][cols/2], row_scales [rows][cols/32]
  *   codes_t   [cols][rows/2], scales_t   [cols][rows/32]
- * Errors as the two calls (FP4_EINVAL for a bad mode or hadamard).
+ * Errors as the two calls (FP4_EINVAL for a bad mode or hadamard; FP4_ESHAPE
+ * also for rows > 8388480, more than 65535 tiles of 128 tokens; FP4_EALIGN
+ * also for row_codes).
  */
 fp4_status fp4_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* row_codes, uint8_t* row_scales,
@@ -135,6 +149,11 @@ fp4_status fp4_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
  *   w           [n][ldw] bf16 (W of Y = X W^T: n outputs, k inputs)
  *   row_codes   [n][k/2],  row_scales [n][k/32]   (Fprop view, K-major)
  *   col_codes   [k][n/2],  col_scales [k][n/32]   (Dgrad view, N-major)
+ * Errors: FP4_EINVAL finer_ratio outside [0, 1] or null pointer; FP4_ESHAPE n
+ * or k not a non-negative multiple of 32, ldw < k, n > 8388480 (more than
+ * 65535 strips of 128 rows), or ldw >= 2^22 (a 128-row strip is addressed
+ * with 32-bit byte offsets); FP4_EALIGN w, row_codes or col_codes not 16-byte
+ * aligned, or ldw not a multiple of 8.
  */
 fp4_status fp4_quantize_w2d32(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
                               uint8_t* row_codes, uint8_t* row_scales,
@@ -150,6 +169,10 @@ fp4_status fp4_quantize_w2d32(const uint16_t* w, int64_t n, int64_t k, int64_t l
  * layout.  Wgrad: A = Q_c(dY), B = Q_c(X).  Deterministic (no split-K).
  *   a_codes [m][k/2], a_scales [m][k/32]; b_codes [n][k/2], b_scales [n][k/32]
  *   c       [m][ldc] fp32
+ * Errors: FP4_EINVAL accumulate not 0 or 1, or null pointer; FP4_ESHAPE m, n
+ * or k not a non-negative multiple of 32, ldc < n, or more than 2^31 - 1
+ * output tiles of 256 x 256; FP4_EALIGN an operand or c not 16-byte aligned,
+ * or ldc not a multiple of 4.
  */
 fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k,
                     const uint8_t* a_codes, const uint8_t* a_scales,
@@ -191,6 +214,11 @@ fp4_status fp4_gemm_pair(int64_t m, int64_t n, int64_t k,
  *   a_bf16, b_bf16 [t][f]
  *   h_codes [t][f/2], h_scales [t][f/32]
  *   ht_codes [f][t/2], ht_scales [f][t/32]     (optional; both or neither)
+ * Errors: FP4_EINVAL exactly one of ht_codes, ht_scales NULL, or another null
+ * pointer (the operands may be NULL when d = 0); FP4_ESHAPE t, f or d not a
+ * non-negative multiple of 32, or more than 2^31 - 1 tiles of 256 tokens x
+ * 128 columns; FP4_EALIGN an operand, a_bf16, b_bf16, h_codes or ht_codes not
+ * 16-byte aligned.
  */
 fp4_status fp4_swiglu_producer(int64_t t, int64_t f, int64_t d,
                                const uint8_t* x_codes, const uint8_t* x_scales,
@@ -206,6 +234,9 @@ fp4_status fp4_swiglu_producer(int64_t t, int64_t f, int64_t d,
  * exp (the same exp as fp4_swiglu_producer); NaN results are stored as 0x7FC0:
  *   dA = bf16(((dH*b)*sig) * (1 + a*(1 - sig))),   dB = bf16(dH*(a*sig))
  *   dh [t][lddh] fp32; a_bf16, b_bf16, da_bf16, db_bf16 [t][f]
+ * Errors: FP4_EINVAL null pointer; FP4_ESHAPE t or f not a non-negative
+ * multiple of 32, or lddh < f; FP4_EALIGN a pointer not 16-byte aligned, or
+ * lddh not a multiple of 4.
  */
 fp4_status fp4_swiglu_backward(int64_t t, int64_t f, const float* dh, int64_t lddh,
                                const uint16_t* a_bf16, const uint16_t* b_bf16,
@@ -241,8 +272,11 @@ fp4_status fp4_swiglu_backward_producer(int64_t t, int64_t f, const float* dh, i
                                         uint8_t* dbt_codes, uint8_t* dbt_scales, void* stream);
 
 /*
- * Fixed 16-entry sign vector for H32 as a bit mask (bit j set => d_j = -1):
- * the low 16 bits of word 0 of Philox4x32-10 at counter (0,0,0,0) under key
+ * Fixed 16-entry sign vector for H32 as a bit mask (bit j set => d_j = -1).
+ * App. A.1 fixes one 16-entry sign vector, shared by both Wgrad operands and
+ * repeated over the two halves of each 32-value block, but its literal
+ * entries are not given; this library derives it from a seed: the low 16
+ * bits of word 0 of Philox4x32-10 at counter (0,0,0,0) under key
  * (lo32(seed), hi32(seed)).  Host-only, no device work.
  */
 uint32_t fp4_sign_mask_from_seed(uint64_t seed);

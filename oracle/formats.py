@@ -49,6 +49,11 @@ def upward_exponent(amax):
     element saturates.  amax == 0 gives -127.
     """
     amax = np.asarray(amax, dtype=np.float64)
+    if not np.all(np.isfinite(amax)):
+        # an infinite or NaN block maximum has no admissible exponent: such
+        # blocks (non-finite inputs, or an H32 sum beyond the fp32 range) lie
+        # outside the quantizer contract
+        raise ValueError("block maximum is not finite: outside the quantizer contract")
     _, E = np.frexp(amax)            # amax in [2**(E-1), 2**E)
     e = E.astype(np.int64) - 4       # 6 * 2**(E-4) < 2**(E-1) <= amax: too small
     for _ in range(4):               # walk up to the smallest admissible e

@@ -72,6 +72,9 @@ def quantize_cols(x_bits, hadamard=0, sign_mask16=0):
 
     With hadamard == 32 each block is first transformed by the fixed-sign H32
     in fp32; the upward scale and RTN then apply to the transformed values.
+    The transformed values must be finite (every block's fp32 butterfly sums
+    stay below 2^128, e.g. |x| < 2^123); otherwise the block has no upward
+    scale and the call is outside the contract (ValueError).
     Rounding is always deterministic here (the Wgrad view).
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)

@@ -204,11 +204,36 @@ def fp4_gemm_pair(a1_codes, a1_scales, b1_codes, b1_scales, a2_codes, a2_scales,
     return c
 
 
+def _u8_2d(t, name, shape=None):
+    _dev(t, name)
+    if t.dtype != torch.uint8 or t.dim() != 2 or not t.is_contiguous():
+        raise Fp4Error(f"{name} must be a contiguous 2-D uint8 tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise Fp4Error(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    return t
+
+
+def _bf16_tf(x, name, shape):
+    _dev(x, name)
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not x.is_contiguous() or tuple(x.shape) != shape:
+        raise Fp4Error(f"{name} must be a contiguous bf16 tensor of shape {shape}")
+    return x
+
+
 def fp4_swiglu_producer(x_codes, x_scales, w13_codes, w13_scales, sign_mask16=0, emit_cols=True,
                         a=None, b=None, h_codes=None, h_scales=None, ht_codes=None, ht_scales=None):
+    _u8_2d(x_codes, "x_codes")
+    _u8_2d(w13_codes, "w13_codes")
     t, d2 = x_codes.shape
     d = 2 * d2
-    f = w13_codes.shape[0] // 2
+    f2, wd2 = w13_codes.shape
+    if wd2 != d2:
+        raise Fp4Error(f"w13_codes has {2 * wd2} values per row, x_codes {d}")
+    if f2 % 2:
+        raise Fp4Error("w13_codes must stack W1 and W3: an even number of rows")
+    f = f2 // 2
+    _u8_2d(x_scales, "x_scales", (t, d // 32))
+    _u8_2d(w13_scales, "w13_scales", (f2, d // 32))
     dev = x_codes.device
     a = _out(a, (t, f), torch.int16, dev, "a") if a is not None else torch.empty((t, f), dtype=torch.int16, device=dev)
     b = _out(b, (t, f), torch.int16, dev, "b") if b is not None else torch.empty((t, f), dtype=torch.int16, device=dev)
@@ -227,9 +252,12 @@ def fp4_swiglu_producer(x_codes, x_scales, w13_codes, w13_scales, sign_mask16=0,
 
 def fp4_swiglu_backward(dh, a, b, da=None, db=None):
     _dev(dh, "dh")
+    _dev(a, "a")
     t, f = a.shape
     if dh.dtype != torch.float32 or dh.dim() != 2 or dh.stride(1) != 1 or tuple(dh.shape) != (t, f):
         raise Fp4Error("dh must be fp32 [t][f] with unit column stride")
+    _bf16_tf(a, "a", (t, f))
+    _bf16_tf(b, "b", (t, f))
     da = _out(da, (t, f), torch.int16, a.device, "da") if da is not None else torch.empty((t, f), dtype=torch.int16, device=a.device)
     db = _out(db, (t, f), torch.int16, a.device, "db") if db is not None else torch.empty((t, f), dtype=torch.int16, device=a.device)
     _check(load().fp4_swiglu_backward(t, f, _p(dh), dh.stride(0), _p(a), _p(b), _p(da), _p(db), _stream()))
@@ -241,12 +269,12 @@ def fp4_swiglu_backward_producer(dh, a, b, seed, offset_a, offset_b, sign_mask16
     ((da_codes, da_scales), (db_codes, db_scales), (dat_codes, dat_scales),
     (dbt_codes, dbt_scales)) -- row-facing SR and column-facing H32."""
     _dev(dh, "dh")
+    _dev(a, "a")
     t, f = a.shape
     if dh.dtype != torch.float32 or dh.dim() != 2 or dh.stride(1) != 1 or tuple(dh.shape) != (t, f):
         raise Fp4Error("dh must be fp32 [t][f] with unit column stride")
-    for x, nm in ((a, "a"), (b, "b")):
-        if x.dtype not in (torch.int16, torch.bfloat16) or not x.is_contiguous() or tuple(x.shape) != (t, f):
-            raise Fp4Error(f"{nm} must be a contiguous bf16 [t][f] tensor")
+    _bf16_tf(a, "a", (t, f))
+    _bf16_tf(b, "b", (t, f))
     dev = a.device
     shapes = [(t, f // 2), (t, f // 32), (t, f // 2), (t, f // 32),
               (f, t // 2), (f, t // 32), (f, t // 2), (f, t // 32)]

@@ -1013,6 +1013,16 @@ using namespace mx;
 // A/B over the FFN step: the 235 and 470 MB Wgrad and Dgrad outputs gained
 // 5-15 us each, and the kernels after them too; the 134 MB outputs lost
 // about 7 us each, so they keep ordinary stores).
+// Number of (bm x bn) output tiles of an m x n result, or -1 when it exceeds
+// the 2^31 - 1 workgroups of a one-dimensional grid (checked before the
+// product, which could overflow int64 for huge m, n).
+static int64_t grid_tiles(int64_t m, int64_t bm, int64_t n, int64_t bn) {
+  const int64_t tm = (m + bm - 1) / bm, tn = (n + bn - 1) / bn;
+  if (tm == 0 || tn == 0) return 0;
+  if (tm > 0x7FFFFFFF / tn) return -1;
+  return tm * tn;
+}
+
 static int fast_flags(int64_t m, int64_t n, int accumulate) {
   constexpr int64_t kStreamCBytes = (int64_t)192 << 20;
   return accumulate | (m * n * 4 > kStreamCBytes ? 2 : 0);
@@ -1029,8 +1039,9 @@ fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, con
   if (!c) return FP4_EINVAL;
   if (k == 0) {                                           // empty sums: C = 0, or C unchanged when accumulating
     if (accumulate) return FP4_OK;
-    const int64_t gy = std::min<int64_t>(m, 65535);
-    hipLaunchKernelGGL(fill_rows_f32_kernel, dim3((unsigned)((n + 255) / 256), (unsigned)gy), dim3(256), 0,
+    const int64_t gx = (n + 255) / 256, gy = std::min<int64_t>(m, 65535);
+    if (gx > 0x7FFFFFFF) return FP4_ESHAPE;
+    hipLaunchKernelGGL(fill_rows_f32_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
                        as_stream(stream), c, m, n, ldc);
     return launch_status();
   }
@@ -1038,8 +1049,8 @@ fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, con
   if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned16(a_scales) || !aligned16(b_scales) ||
       !aligned16(c) || (ldc % 4) != 0)
     return FP4_EALIGN;
-  const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  if (tiles > 0x7FFFFFFF) return FP4_ESHAPE;
+  const int64_t tiles = grid_tiles(m, BM, n, BN);
+  if (tiles < 0) return FP4_ESHAPE;
   hipStream_t s = as_stream(stream);
   // the fast path needs K % 256 == 0 and buffer offsets below 2^31 per tile
   if ((k % 256) == 0 && 256 * (k / 2) < 0x7FFFFFFF)
@@ -1066,8 +1077,8 @@ fp4_status fp4_gemm_pair(int64_t m, int64_t n, int64_t k, const uint8_t* a1_code
       !aligned16(a2_codes) || !aligned16(b2_codes) || !aligned16(a2_scales) || !aligned16(b2_scales) ||
       !aligned16(c) || (ldc % 4) != 0)
     return FP4_EALIGN;
-  const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  if (tiles > 0x7FFFFFFF) return FP4_ESHAPE;
+  const int64_t tiles = grid_tiles(m, BM, n, BN);
+  if (tiles < 0) return FP4_ESHAPE;
   if ((k % 256) == 0 && 256 * (k / 2) < 0x7FFFFFFF) {
     hipLaunchKernelGGL(gemm_fast_kernel, dim3((unsigned)tiles), dim3(kFastThreads), 0, as_stream(stream), m, n, k,
                        a1_codes, a1_scales, b1_codes, b1_scales, a2_codes, a2_scales, b2_codes, b2_scales, c, ldc,
@@ -1096,8 +1107,8 @@ fp4_status fp4_swiglu_producer(int64_t t, int64_t f, int64_t d, const uint8_t* x
   if (!aligned16(x_codes) || !aligned16(w13_codes) || !aligned16(h_codes) || !aligned16(x_scales) ||
       !aligned16(w13_scales) || !aligned16(a_bf16) || !aligned16(b_bf16) || (ht_codes && !aligned16(ht_codes)))
     return FP4_EALIGN;
-  const int64_t tiles = ((t + BM - 1) / BM) * ((f + 127) / 128);
-  if (tiles > 0x7FFFFFFF) return FP4_ESHAPE;
+  const int64_t tiles = grid_tiles(t, BM, f, 128);
+  if (tiles < 0) return FP4_ESHAPE;
   hipStream_t s = as_stream(stream);
   if ((d % 256) == 0 && 256 * (d / 2) < 0x7FFFFFFF)
     hipLaunchKernelGGL(swiglu_fast_kernel, dim3((unsigned)tiles), dim3(kFastThreads), 0, s, t, f, d, x_codes, x_scales,

@@ -99,6 +99,32 @@ def test_argument_errors_are_reported_without_gpu_work():
                                             0, *bufs, None) == 2
 
 
+def test_size_limit_errors_are_reported_without_gpu_work():
+    """The launch-shape limits each declaration states come back as
+    FP4_ESHAPE from the host checks (no pointer is dereferenced)."""
+    import precision_mxfp4_producers_amd as mx
+    lib = mx.load(LIB)
+    v, u64 = ctypes.c_void_p, ctypes.c_uint64
+    d4 = [v(4096)] * 2
+    big_rows = 65536 * 128                                 # 65536 tiles of 128 tokens
+    assert lib.fp4_quantize_cols(v(4096), big_rows, 32, 32, v(4096), v(4096), 32, 0, None) == 2
+    assert lib.fp4_quantize_dual(v(4096), big_rows, 32, 32, *d4, 1, u64(0), u64(0), *d4, 32, 0, None) == 2
+    assert lib.fp4_quantize_w2d32(v(4096), big_rows, 32, 32, v(4096), v(4096), v(4096), v(4096),
+                                  ctypes.c_float(0.87), None) == 2
+    assert lib.fp4_quantize_w2d32(v(4096), 32, 32, 1 << 22, v(4096), v(4096), v(4096), v(4096),
+                                  ctypes.c_float(0.87), None) == 2
+    assert lib.fp4_quantize_w2d32(v(4096), 32, 32, 32, v(4096), v(4096), v(4096), v(4096),
+                                  ctypes.c_float(1.5), None) == 1
+    huge = 1 << 40                                         # (2^32)^2 tiles of 256 x 256
+    assert lib.fp4_gemm(huge, huge, 32, v(4096), v(4096), v(4096), v(4096), v(4096), huge, 0, None) == 2
+    assert lib.fp4_gemm_pair(huge, huge, 256, *([v(4096)] * 8), v(4096), huge, 0, None) == 2
+    assert lib.fp4_swiglu_producer(huge, huge, 32, *([v(4096)] * 10), 0, None) == 2
+    # just inside the limits the checks pass on to the (here absent) alignment check
+    assert lib.fp4_quantize_cols(v(4098), big_rows - 128, 32, 32, v(4096), v(4096), 32, 0, None) == 3
+    assert lib.fp4_quantize_w2d32(v(4098), 32, 32, (1 << 22) - 8, v(4096), v(4096), v(4096), v(4096),
+                                  ctypes.c_float(0.87), None) == 3
+
+
 def test_empty_calls_are_noops_without_gpu_work():
     """An output with no elements: FP4_OK, NULL pointers allowed, no device call."""
     import precision_mxfp4_producers_amd as mx

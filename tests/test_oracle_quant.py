@@ -184,3 +184,21 @@ def test_w2d32_finer_rule_fraction_of_tiles():
     e_up = F.upward_exponent(np.abs(tiles).max(axis=(1, 3)))
     finer = (rs[::32].astype(int) - 127) == e_up - 1
     assert 0.5 < finer.mean() <= 1.0
+
+
+def test_cols_h32_requires_finite_transform():
+    """H32 sums beyond the fp32 range have no upward scale: the oracle refuses
+    them (the header states the bound), while inputs just inside it still
+    encode: a constant block of 1.984 * 2^122 (0x7CFF) transforms to
+    t_0 = 2^-2.5 * 32 * 1.984 * 2^122 = 1.40 * 2^125 and zeros, whose upward
+    exponent is 123 (6 * 2^122 = 1.5 * 2^125), scale byte 250."""
+    x = np.zeros((32, 32), dtype=np.uint16)
+    x[:2, 0] = 0x7F7F                                    # two largest finite values in one block
+    with pytest.raises(ValueError):
+        Q.quantize_cols(x, 32, 0)
+    near = np.full((32, 32), 0x7CFF, dtype=np.uint16)   # butterfly sums reach 1.98 * 2^127
+    codes, scales = Q.quantize_cols(near, 32, 0)
+    vals = F.decode(codes, scales)
+    assert np.all(np.isfinite(vals)) and np.all(scales == 250)
+    with pytest.raises(ValueError):
+        Q.quantize_rows(np.full((1, 32), 0x7F80, dtype=np.uint16))
