@@ -115,11 +115,18 @@ def copy_calibration():
 def quantizer_sweep(mx, torch, reps=9):
     """Each producer alone, after a read-only pass over 1 GiB (evicts the
     256 MB Infinity Cache without leaving dirty lines), timed with HIP events;
-    beside it a plain elementwise kernel with the same traffic per element
-    (reads 2 B, writes 0.5 B: a not-equal over the bf16 pairs as int32 into a
-    bool per pair), which shows what a simple streaming kernel reaches at that
+    beside it a hand-written streaming kernel with the traffic of a
+    one-orientation producer (2 B read with 16-byte loads, 0.5 B of nibbles
+    written as whole lines and 1/32 B of side bytes per element, no rounding
+    work: libmxfp4_bench.so), which shows what plain streaming reaches at that
     size on this part."""
+    import ctypes
     import synthetic
+    from precision_mxfp4_producers_amd.build import BENCH_LIB
+    blib = ctypes.CDLL(BENCH_LIB)
+    blib.mxfp4_stream_reference.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+    blib.mxfp4_stream_reference.restype = ctypes.c_int
     flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
     dev = torch.device("cuda:0")
 
@@ -141,12 +148,15 @@ def quantizer_sweep(mx, torch, reps=9):
     for (R, C) in ((8192, 4096), (14336, 4096), (8192, 14336)):
         x = torch.from_numpy(synthetic.tensor((R, C), std=1.0, seed=5).view(np.int16)).to(dev)
         n = R * C
-        pairs = x.view(torch.int32).view(-1)
-        flags = torch.empty(pairs.numel(), dtype=torch.bool, device=dev)
         rc, rs = torch.empty((R, C // 2), dtype=torch.uint8, device=dev), torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
         cc, cs = torch.empty((C, R // 2), dtype=torch.uint8, device=dev), torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
-        ref_ms = timed(lambda: torch.ne(pairs, 0, out=flags))
-        ref_gbps = n * 2.5 / (ref_ms * 1e-3) / 1e9
+        def stream_ref():
+            st = blib.mxfp4_stream_reference(x.data_ptr(), n, rc.data_ptr(), rs.data_ptr(),
+                                             torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"streaming reference launch failed ({st})")
+        ref_ms = timed(stream_ref)
+        ref_gbps = n * B_SINGLE / (ref_ms * 1e-3) / 1e9
         calls = [
             ("rows RTN", B_SINGLE, lambda: mx.fp4_quantize_rows(x, 0, 0, 0, codes=rc, scales=rs)),
             ("rows SR", B_SINGLE, lambda: mx.fp4_quantize_rows(x, 1, 0, 0, codes=rc, scales=rs)),
@@ -161,7 +171,7 @@ def quantizer_sweep(mx, torch, reps=9):
             rows.append({"shape": f"{R}x{C}", "call": label, "us": round(ms * 1e3, 1), "gbps": round(gbps, 1),
                          "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
                          "frac_streaming_reference": round(gbps / ref_gbps, 4)})
-        rows.append({"shape": f"{R}x{C}", "call": "streaming reference (2 B in, 0.5 B out)",
+        rows.append({"shape": f"{R}x{C}", "call": "streaming reference (2 B in, 0.53125 B out)",
                      "us": round(ref_ms * 1e3, 1), "gbps": round(ref_gbps, 1),
                      "frac_hbm_peak": round(ref_gbps / PEAK_HBM_GBPS, 4), "frac_streaming_reference": 1.0})
     return rows
@@ -444,6 +454,21 @@ QUALITY_CASES = {
 }
 
 
+def quality_metrics(c, ref):
+    """Error of an MXFP4 contraction c against its fp32 reference ref (both
+    converted to float64): relative L2 error ||c - ref|| / ||ref||, the SNR
+    -20 log10 of it in dB, the cosine <c, ref> / (||c|| ||ref||), and the
+    bias mean(c - ref) / rms(ref).  Accepts numpy arrays or torch tensors."""
+    c = np.asarray(c.double().cpu().numpy() if hasattr(c, "double") else c, dtype=np.float64).ravel()
+    ref = np.asarray(ref.double().cpu().numpy() if hasattr(ref, "double") else ref, dtype=np.float64).ravel()
+    d = c - ref
+    rl2 = float(np.linalg.norm(d) / np.linalg.norm(ref))
+    return {"rel_l2": round(rl2, 6),
+            "snr_db": round(-20 * math.log10(rl2), 2) if rl2 > 0 else float("inf"),
+            "cosine": round(float(c @ ref / (np.linalg.norm(c) * np.linalg.norm(ref))), 7),
+            "bias": round(float(d.mean() / np.sqrt(np.mean(ref * ref))), 7)}
+
+
 def quality_report(mx, torch):
     """Relative L2 error, cosine and bias of each MXFP4 contraction against the
     fp32 contraction of the same bf16 tensors, with the method's ablations:
@@ -462,13 +487,8 @@ def quality_report(mx, torch):
         refs = {"Fprop": f32(X) @ f32(W).T, "Dgrad": f32(dY) @ f32(W), "Wgrad": f32(dY).T.contiguous() @ f32(X)}
 
         def score(kind, variant, c):
-            r = refs[kind].double()
-            d = c.double() - r
-            rl2 = (d.norm() / r.norm()).item()
-            out.append({"workload": name, "contraction": kind, "variant": variant, "rel_l2": round(rl2, 6),
-                        "snr_db": round(-20 * math.log10(rl2), 2),
-                        "cosine": round((c.double() * r).sum().item() / (c.double().norm() * r.norm()).item(), 7),
-                        "bias": round((d.mean() / r.pow(2).mean().sqrt()).item(), 7)})
+            out.append({"workload": name, "contraction": kind, "variant": variant,
+                        **quality_metrics(c, refs[kind])})
 
         xr = mx.fp4_quantize_rows(X)
         for ratio, tag in ((0.87, "2D32, finer rule 0.87"), (0.0, "2D32, finer rule off")):

@@ -11,6 +11,11 @@ float64; its own error (<= K * 2^-53 * E) is negligible against the bound.
 
 Acceptance (per element): |C_gpu - C_ref| <= 1e-5 * E with
 E[m][n] = sum_k |dec(A)[m,k] * dec(B)[n,k]|; where E == 0, C_gpu must be 0.
+Below 2^-126 fp32 has a fixed spacing of 2^-149, so a sum accumulated in
+fp32 there can be off by up to half that spacing per accumulated term, an
+absolute amount the relative bound cannot cover; given the reduction length
+K, the bound therefore gains K * 2^-150 (negligible for results in the
+normal range).
 """
 
 import numpy as np
@@ -31,11 +36,15 @@ def gemm_ref(a_codes, a_scales, b_codes, b_scales, rows=None):
     return C, E
 
 
-def within_bound(c_gpu, c_ref, e_bound, c_prev=None, tol=GEMM_REL_TOL):
+F32_SUBNORMAL_HALF_SPACING = 2.0 ** -150
+
+
+def within_bound(c_gpu, c_ref, e_bound, c_prev=None, tol=GEMM_REL_TOL, k=None):
     """Boolean mask of elements meeting the bound.
 
     With accumulation the previous value is one more term of the sum, so it
     joins both the reference and the magnitude sum: |c_prev| is added to E.
+    Given the reduction length k, the fp32 subnormal term k * 2^-150 is added.
     """
     c_gpu = np.asarray(c_gpu, dtype=np.float64)
     if c_prev is None:
@@ -43,7 +52,8 @@ def within_bound(c_gpu, c_ref, e_bound, c_prev=None, tol=GEMM_REL_TOL):
     else:
         prev = np.asarray(c_prev, dtype=np.float64)
         ref, bound = c_ref + prev, e_bound + np.abs(prev)
-    ok = np.abs(c_gpu - ref) <= tol * bound
+    floor = 0.0 if k is None else float(k) * F32_SUBNORMAL_HALF_SPACING
+    ok = np.abs(c_gpu - ref) <= tol * bound + floor
     if c_prev is None:
         ok &= ~((e_bound == 0) & (c_gpu != 0))
     return ok

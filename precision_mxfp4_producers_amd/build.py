@@ -28,8 +28,24 @@ FLAGS = [
 ]
 
 
+# Test-only probes (tests/hip/*.hip): each becomes tests/hip/lib<name>.so.
+# They run device helpers of the library on inputs a test chooses; nothing in
+# the package loads them.
+TEST_HIP = os.path.join(os.path.dirname(HERE), "tests", "hip")
+
+
+# Measurement-only kernels (bench_kernels/*.hip): one library that bench.py
+# loads for its reference measurements; not part of the ABI.
+BENCH_SRC = os.path.join(HERE, "bench_kernels")
+BENCH_LIB = os.path.join(HERE, "libmxfp4_bench.so")
+
+
 def lib_path():
     return os.path.join(HERE, LIB_NAME)
+
+
+def probe_path(name):
+    return os.path.join(TEST_HIP, f"lib{name}.so")
 
 
 def build(verbose=False, jobs=4):
@@ -57,6 +73,46 @@ def build(verbose=False, jobs=4):
     return lib_path()
 
 
+def build_bench_kernels(verbose=False):
+    """Compile bench_kernels/*.hip into libmxfp4_bench.so."""
+    srcs = sorted(os.path.join(BENCH_SRC, f) for f in os.listdir(BENCH_SRC) if f.endswith(".hip"))
+    cmd = [HIPCC] + FLAGS + ["-shared"] + srcs + ["-o", BENCH_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    _wait(("bench_kernels", _Done(p)))
+    os.replace(BENCH_LIB + ".tmp", BENCH_LIB)
+    return BENCH_LIB
+
+
+def build_test_probes(verbose=False):
+    """Compile every tests/hip/*.hip into its own shared library."""
+    built = []
+    if not os.path.isdir(TEST_HIP):
+        return built
+    for src in sorted(f for f in os.listdir(TEST_HIP) if f.endswith(".hip")):
+        name = os.path.splitext(src)[0]
+        out = probe_path(name)
+        cmd = [HIPCC] + FLAGS + ["-shared", os.path.join(TEST_HIP, src), "-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        _wait((src, _Done(p)))
+        os.replace(out + ".tmp", out)
+        built.append(out)
+    return built
+
+
+class _Done:
+    """A finished subprocess.run result in the shape _wait expects."""
+
+    def __init__(self, r):
+        self.returncode, self._out = r.returncode, r.stdout
+
+    def communicate(self):
+        return self._out, None
+
+
 def _wait(item):
     src, p = item
     out, _ = p.communicate()
@@ -70,3 +126,5 @@ def _wait(item):
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_bench_kernels(verbose=True))
+    print(build_test_probes(verbose=True))

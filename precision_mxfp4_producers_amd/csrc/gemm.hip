@@ -688,17 +688,13 @@ __device__ __forceinline__ void quantize_h_tile(const uint8_t* smem, int64_t m0,
     uint32_t v[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) v[i] = *reinterpret_cast<const uint32_t*>(smem + (32 * tb + i) * kHPitch + cp * 4);
+    h32_sign_words(v, sign_mask16);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int64_t col = n0 + 2 * cp + c;
       if (col >= Fdim) continue;
       float fv[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        uint32_t bits = (v[i] >> (16 * c)) & 0xFFFFu;
-        bits ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;
-        fv[i] = bf16_bits_to_f32(bits);
-      }
+      h32_half(v, c, fv);
       h32_fp32(fv);
       int e;
       const uint4 code = encode32_rtn(fv, e);
@@ -853,16 +849,12 @@ __device__ __forceinline__ void swiglu_epilogue_staged(
     uint32_t v[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) v[i] = *reinterpret_cast<const uint32_t*>(hs + (32 * tb + i) * kHPitch + 4 * (cp ^ (tb << 3)));
+    h32_sign_words(v, sign_mask16);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int64_t col = n0 + 2 * cp + c;
       float fv[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        uint32_t bits = (v[i] >> (16 * c)) & 0xFFFFu;
-        bits ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;
-        fv[i] = bf16_bits_to_f32(bits);
-      }
+      h32_half(v, c, fv);
       h32_fp32(fv);
       int e;
       const uint4 code = encode32_rtn(fv, e);

@@ -16,6 +16,7 @@ namespace mx {
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> packed bf16 (x low), round to nearest even, NaN -> 0x7FC0.
 // gfx950's v_cvt_pk_bf16_f32 rounds to nearest even on every non-NaN fp32
@@ -108,6 +109,102 @@ __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u, uint32_t nonzer
   return lo + (u < thr ? 1u : 0u);
 }
 
+// Exact SR nibbles (sign | code, element k at bits 4k) of eight bf16 values
+// (four packed words) under block exponent e: e2m1_sr per element.
+__device__ __forceinline__ uint32_t sr8_exact(const uint32_t* w, int e, const uint32_t* u) {
+  const float inv = inv_pow2(e);
+  uint32_t packed = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t bits = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+    const uint32_t mag = bits & 0x7FFFu;
+    const float y = bf16_bits_to_f32(mag) * inv;         // exact (power-of-two scale)
+    packed |= (e2m1_sr(y, u[k], min(mag, 1u)) | ((bits >> 12) & 8u)) << (4 * k);
+  }
+  return packed;
+}
+
+// Fast SR form, exact for every element whose scaled magnitude y = |x| 2^-e
+// is 0 or at least 2^-16.  E2M1's magnitude code is the bit pattern of a
+// float with one fraction bit, exponent bias 1 and subnormals, which is the
+// pattern of fp32 with its low 22 fraction bits dropped once the value is
+// moved by 2^-126: z = y 2^-126 is an fp32 subnormal for y < 1 and normal
+// above, and bits(z) >> 22 is the code of y rounded toward zero.  For such y
+// (8 significant bits, the lowest at 2^-23 or above) z is exact, and the
+// contract's threshold ceil(frac 2^32) is the low 22 bits of bits(z) times
+// 2^10, so "u < threshold" is the carry out of those 22 bits when
+// floor(~u / 2^10) = (u >> 10) ^ (2^22 - 1) is added.  z comes from
+// v_ldexp_f32, exact for these values (normal inputs, subnormal results
+// included).  The signs come from
+// the hardware RTN converter applied to the signed zeros of the sign bits (it
+// keeps the sign of a zero: nibble 0 or 8).
+// (x ^ y) + z in one v_xad_u32; the compiler rewrites the xor with a low-bit
+// mask into a not and a shift and loses the fused form.
+__device__ __forceinline__ uint32_t xad_u32(uint32_t x, uint32_t y, uint32_t z) {
+  uint32_t r;
+  asm("v_xad_u32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(y), "v"(z));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t sr8_fast(const uint32_t* w, int e, const uint32_t* u) {
+  const int sh = -126 - e;
+  uint32_t packed = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    // the value with its sign: ldexp keeps the sign in bit 31, and bits 25-30
+    // of bits(z) stay clear for |y| <= 6, so the code field is unaffected
+    const uint32_t xb = (k & 1) ? (w[k >> 1] & 0xFFFF0000u) : (w[k >> 1] << 16);
+    const uint32_t zb = __float_as_uint(__builtin_amdgcn_ldexpf(__uint_as_float(xb), sh));
+    const uint32_t s = xad_u32(u[k] >> 10, 0x3FFFFFu, zb);   // code in bits 22-24
+    packed |= __builtin_amdgcn_ubfe(s, 22, 3) << (4 * k);
+  }
+  return packed | rtn8_bf16(w[0] & 0x80008000u, w[1] & 0x80008000u, w[2] & 0x80008000u, w[3] & 0x80008000u, 1.0f);
+}
+
+// True when some of the NW/2 x 2 values of a block with exponent e needs the
+// exact form: a non-zero magnitude below 2^(e-16), i.e. bf16 pattern
+// 1 <= mag < bits(2^(e-16)), taken as max(e + 111, 1) << 7 (exact for
+// e >= -110; below that every subnormal input goes to the exact form); or a
+// block exponent of 126 or more, which a finite block reaches only with a
+// maximum of at least 1.5 * 2^127 and every non-finite one reaches (so that
+// non-finite blocks, outside the contract, give the same bytes whichever
+// kernel encodes them).  One packed 16-bit subtract and min per two values.
+template <int NW>
+__device__ __forceinline__ bool sr_needs_exact(const uint32_t* w, int e) {
+  u16x2_t m = {0xFFFFu, 0xFFFFu};
+  const u16x2_t one = {1u, 1u};
+#pragma unroll
+  for (int j = 0; j < NW; ++j)
+    m = __builtin_elementwise_min(m, __builtin_bit_cast(u16x2_t, w[j] & 0x7FFF7FFFu) - one);   // 0 wraps to 0xFFFF
+  const uint32_t lim = (uint32_t)max(e + 111, 1) << 7;
+  return (min((uint32_t)m[0], (uint32_t)m[1]) < lim - 1u) || e >= 126;
+}
+
+// SR nibbles of NW/4 groups of eight bf16 values (NW packed words) sharing one
+// block exponent: the fast form unless some lane of the wave holds a value
+// that needs the exact one (one wave-uniform branch).  draws(q, u) fills the
+// eight SR words of group q; it is called inside the branch, so that the
+// words of one group at a time are live.
+template <int NW, typename Draws>
+__device__ __forceinline__ void sr_encode(const uint32_t* w, int e, Draws&& draws, uint32_t* packed) {
+  static_assert(NW % 4 == 0, "groups of eight values");
+  if (__builtin_amdgcn_ballot_w64(sr_needs_exact<NW>(w, e)) == 0) {
+#pragma unroll
+    for (int q = 0; q < NW / 4; ++q) {
+      uint32_t u[8];
+      draws(q, u);
+      packed[q] = sr8_fast(w + 4 * q, e, u);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < NW / 4; ++q) {
+      uint32_t u[8];
+      draws(q, u);
+      packed[q] = sr8_exact(w + 4 * q, e, u);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- H32
 // Fixed-sign 32-point Hadamard of one block (signs already applied): fp32
 // butterflies (lo, hi) <- (lo + hi, lo - hi) with strides 1, 2, 4, 8, 16, then
@@ -129,6 +226,19 @@ __device__ __forceinline__ void h32_fp32(float (&f)[32]) {
   for (int j = 0; j < 32; ++j) f[j] = __fmul_rn(f[j], c);
 }
 
+// Fixed-sign H32 inputs of a column pair: word k holds token k of two
+// columns (low and high bf16); the sign d_(k mod 16) flips both halves at
+// once, and h32_half then unpacks the values of one column as fp32.
+__device__ __forceinline__ void h32_sign_words(uint32_t (&v)[32], uint32_t sign_mask16) {
+#pragma unroll
+  for (int k = 0; k < 32; ++k) v[k] ^= ((sign_mask16 >> (k & 15)) & 1u) * 0x80008000u;
+}
+
+__device__ __forceinline__ void h32_half(const uint32_t (&v)[32], int c, float (&f)[32]) {
+#pragma unroll
+  for (int k = 0; k < 32; ++k) f[k] = __uint_as_float(c ? (v[k] & 0xFFFF0000u) : (v[k] << 16));
+}
+
 // RTN MXFP4 of one 32-value fp32 block: upward scale of its maximum, codes.
 __device__ __forceinline__ uint4 encode32_rtn(const float (&f)[32], int& e_out) {
   float am = 0.0f;
@@ -141,7 +251,6 @@ __device__ __forceinline__ uint4 encode32_rtn(const float (&f)[32], int& e_out) 
 }
 
 // Largest 15-bit magnitude pattern among eight bf16 values (four words).
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t bf16_absmax8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
   const u16x2_t a = __builtin_bit_cast(u16x2_t, w0 & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2_t, w1 & 0x7FFF7FFFu);
   const u16x2_t c = __builtin_bit_cast(u16x2_t, w2 & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2_t, w3 & 0x7FFF7FFFu);

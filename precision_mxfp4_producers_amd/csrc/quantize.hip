@@ -25,6 +25,7 @@ thread_local int g_last_hip_error = 0;
 
 constexpr int kThreads = 256;
 constexpr int kMaxGridY = 65535;
+constexpr int64_t kMaxGridX = 0x7FFFFFFF;
 constexpr int64_t kTargetBlocks = 8192;                  // 32 workgroups per CU
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -42,20 +43,13 @@ template <bool kSR>
 __device__ __forceinline__ uint32_t encode_row_chunk(uint4 v, int e, int64_t r, int64_t cols, int64_t c8,
                                                      uint64_t seed, uint64_t offset) {
   if constexpr (kSR) {
-    const uint64_t idx0 = (uint64_t)r * (uint64_t)cols + (uint64_t)c8 * 8u;
-    const u32x4 a = sr_words(idx0 >> 2, seed, offset);
-    const u32x4 b = sr_words((idx0 >> 2) + 1u, seed, offset);
-    const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint64_t blk0 = ((uint64_t)r * (uint64_t)cols + (uint64_t)c8 * 8u) >> 2;   // first Philox counter
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    const float inv = inv_pow2(e);
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t bits = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-      const uint32_t mag = bits & 0x7FFFu;
-      const float y = bf16_bits_to_f32(mag) * inv;       // exact (power-of-two scale)
-      packed |= (e2m1_sr(y, u[i], min(mag, 1u)) | ((bits >> 12) & 8u)) << (4 * i);
-    }
+    uint32_t packed;
+    sr_encode<4>(w, e, [&](int, uint32_t* u) {
+      const u32x4 a = sr_words(blk0, seed, offset), b = sr_words(blk0 + 1u, seed, offset);
+      u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w; u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
+    }, &packed);
     return packed;
   } else {
     return rtn8_bf16(v.x, v.y, v.z, v.w, pow2_scale(e));
@@ -158,15 +152,11 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     uint32_t v[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) v[k] = *reinterpret_cast<const uint32_t*>(tile + (32 * tb + k) * kColPitch + cp * 4);
+    if constexpr (kH32) h32_sign_words(v, sign_mask16);                // d_(k mod 16)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float f[32];
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        uint32_t bb = (v[k] >> (16 * c)) & 0xFFFFu;
-        if constexpr (kH32) bb ^= ((sign_mask16 >> (k & 15)) & 1u) << 15;   // d_(k mod 16)
-        f[k] = bf16_bits_to_f32(bb);
-      }
+      h32_half(v, c, f);
       if constexpr (kH32) h32_fp32(f);
       code[c] = encode32_rtn(f, ex[c]);
     }
@@ -286,15 +276,11 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     uint32_t v[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) v[k] = *reinterpret_cast<const uint32_t*>(tile + (32 * tb + k) * kDualPitch + cp * 4);
+    if constexpr (kH32) h32_sign_words(v, sign_mask16);                // d_(k mod 16)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float f[32];
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        uint32_t bb = (v[k] >> (16 * c)) & 0xFFFFu;
-        if constexpr (kH32) bb ^= ((sign_mask16 >> (k & 15)) & 1u) << 15;   // d_(k mod 16)
-        f[k] = bf16_bits_to_f32(bb);
-      }
+      h32_half(v, c, f);
       if constexpr (kH32) h32_fp32(f);
       code[u][c] = encode32_rtn(f, ex[u][c]);
     }
@@ -482,6 +468,7 @@ fp4_status fp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
   if (!aligned16(x) || !aligned16(codes) || (ldx % 8) != 0) return FP4_EALIGN;
   const int64_t cpr = cols >> 3;
   const int64_t gx = (cpr + kThreads - 1) / kThreads;
+  if (gx > kMaxGridX) return FP4_ESHAPE;
   // about kTargetBlocks workgroups, each taking whole passes of kRowsPerPass rows
   int64_t gy = std::max<int64_t>(1, kTargetBlocks / gx);
   gy = std::min<int64_t>(gy, (rows + kRowsPerPass - 1) / kRowsPerPass);
@@ -506,7 +493,7 @@ fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int6
   if (!x || !codes_t || !scales_t) return FP4_EINVAL;
   if (!aligned16(x) || !aligned16(codes_t) || (ldx % 8) != 0) return FP4_EALIGN;
   const int64_t gx = (cols + kColW - 1) / kColW, gy = (rows + kColTok - 1) / kColTok;
-  if (gy > kMaxGridY) return FP4_ESHAPE;
+  if (gy > kMaxGridY || gx > kMaxGridX) return FP4_ESHAPE;
   dim3 grid((unsigned)gx, (unsigned)gy);
   hipStream_t s = as_stream(stream);
   if (hadamard == 32)
@@ -529,7 +516,7 @@ fp4_status fp4_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
   if (!x || !row_codes || !row_scales || !codes_t || !scales_t) return FP4_EINVAL;
   if (!aligned16(x) || !aligned16(row_codes) || !aligned16(codes_t) || (ldx % 8) != 0) return FP4_EALIGN;
   const int64_t gx = (cols + kDualW - 1) / kDualW, gy = (rows + kDualTok - 1) / kDualTok;
-  if (gy > kMaxGridY) return FP4_ESHAPE;
+  if (gy > kMaxGridY || gx > kMaxGridX) return FP4_ESHAPE;
   dim3 grid((unsigned)gx, (unsigned)gy);
   hipStream_t s = as_stream(stream);
   const uint32_t m16 = hadamard == 32 ? (sign_mask16 & 0xFFFFu) : 0u;

@@ -21,6 +21,7 @@ namespace mx {
 
 constexpr int kBwdThreads = 256;
 constexpr int kMaxGridY = 65535;
+constexpr int64_t kMaxGridX = 0x7FFFFFFF;
 
 // One lane handles 8 consecutive elements of a row.
 __global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_kernel(
@@ -204,24 +205,12 @@ __global__ __launch_bounds__(kFbThreads) void swiglu_bwd_producer_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) m = max(m, bf16_absmax8(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]));
       const int e = upward_exp(m << 16);
-      const float inv = inv_pow2(e);
       const uint64_t blk0 = ((uint64_t)row * (uint64_t)Fdim + (uint64_t)col0) >> 2;   // first Philox counter
       uint32_t packed[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {                      // 8 elements per output word
-        const u32x4 u0 = sr_words(blk0 + 2 * q, seed, o.offset);
-        const u32x4 u1 = sr_words(blk0 + 2 * q + 1, seed, o.offset);
-        const uint32_t u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-        uint32_t pk = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t bits = (w[4 * q + (j >> 1)] >> (16 * (j & 1))) & 0xFFFFu;
-          const uint32_t mag = bits & 0x7FFFu;
-          const float y = bf16_bits_to_f32(mag) * inv;
-          pk |= (e2m1_sr(y, u[j], min(mag, 1u)) | ((bits >> 12) & 8u)) << (4 * j);
-        }
-        packed[q] = pk;
-      }
+      sr_encode<16>(w, e, [&](int q, uint32_t* u) {
+        const u32x4 a = sr_words(blk0 + 2 * q, seed, o.offset), b = sr_words(blk0 + 2 * q + 1, seed, o.offset);
+        u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w; u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
+      }, packed);
       if (ok) {
         *reinterpret_cast<uint4*>(o.codes + row * (Fdim >> 1) + (col0 >> 1)) =
             make_uint4(packed[0], packed[1], packed[2], packed[3]);
@@ -287,7 +276,9 @@ extern "C" fp4_status fp4_swiglu_backward(int64_t t, int64_t f, const float* dh,
       (lddh % 4) != 0)
     return FP4_EALIGN;
   const int64_t cpr = f >> 3;
-  dim3 grid((unsigned)((cpr + kBwdThreads - 1) / kBwdThreads), (unsigned)(t < kMaxGridY ? t : kMaxGridY));
+  const int64_t gx = (cpr + kBwdThreads - 1) / kBwdThreads;
+  if (gx > kMaxGridX) return FP4_ESHAPE;
+  dim3 grid((unsigned)gx, (unsigned)(t < kMaxGridY ? t : kMaxGridY));
   hipLaunchKernelGGL(swiglu_bwd_kernel, grid, dim3(kBwdThreads), 0, as_stream(stream), t, f, dh, lddh, a_bf16,
                      b_bf16, da_bf16, db_bf16);
   return launch_status();
@@ -307,7 +298,7 @@ extern "C" fp4_status fp4_swiglu_backward_producer(
       !aligned16(db_codes) || !aligned16(dat_codes) || !aligned16(dbt_codes) || (lddh % 4) != 0)
     return FP4_EALIGN;
   const int64_t gx = (f + kFbCols - 1) / kFbCols, gy = (t + kFbTok - 1) / kFbTok;
-  if (gy > kMaxGridY || lddh >= (int64_t(1) << 23)) return FP4_ESHAPE;   // 32-bit buffer offsets
+  if (gy > kMaxGridY || gx > kMaxGridX || lddh >= (int64_t(1) << 23)) return FP4_ESHAPE;   // 32-bit buffer offsets
   const FbOut oa{da_codes, da_scales, dat_codes, dat_scales, offset_a};
   const FbOut ob{db_codes, db_scales, dbt_codes, dbt_scales, offset_b};
   hipLaunchKernelGGL(swiglu_bwd_producer_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kFbThreads), 0,

@@ -201,3 +201,25 @@ def test_swiglu_backward_matches_analytic_derivative():
     f = lambda t: t / (1 + np.exp(-t)) * bv
     fd = (f(av + eps) - f(av - eps)) / (2 * eps) * dhv
     assert np.allclose(fd, ref_da, rtol=1e-5, atol=1e-7)
+
+
+def test_bound_covers_fp32_accumulation_in_the_subnormal_range():
+    """The subnormal floor of the GEMM bound: a running fp32 sum of K exact
+    products spread from far below the fp32 range up to its subnormals (each
+    product reaches the fp32 grid with one rounding, at most 2^-150, and
+    sums of grid values below 2^-126 are exact) stays within
+    1e-5 * sum|p| + K * 2^-150 of the exact sum rounded once, while the
+    relative term alone misses many such sums (the floor is needed)."""
+    rng = np.random.default_rng(11)
+    K = 512
+    rel_only_misses = 0
+    for _ in range(200):
+        p = rng.integers(-36, 37, size=K) * 2.0 ** rng.integers(-180, -140, size=K).astype(np.float64)
+        acc = np.float32(0.0)
+        for v in p:
+            acc = np.float32(acc + np.float32(v))
+        exact = float(np.sum(p))                        # fp64: its error is far below 2^-150
+        e = float(np.abs(p).sum())
+        assert bool(G.within_bound(np.float64(acc), np.float64(np.float32(exact)), e, k=K))
+        rel_only_misses += int(not G.within_bound(np.float64(acc), np.float64(np.float32(exact)), e))
+    assert rel_only_misses > 0
