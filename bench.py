@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--unfused-backward", action="store_true",
                    help="FFN step: separate producer calls (SR rows and H32 cols of dY as two calls; SwiGLU backward, "
                         "SR rows and H32 cols of dA/dB as five)")
+    p.add_argument("--dgrad-epilogue", action="store_true",
+                   help="FFN step: W2 Dgrad with the SwiGLU backward producer in its epilogue (one launch; dH never "
+                        "in memory) instead of W2 Dgrad followed by the backward producer")
     p.add_argument("--eager", action="store_true",
                    help="time the step as eager launches instead of one captured HIP graph")
     p.add_argument("--quality", action="store_true",
@@ -180,8 +183,9 @@ def quantizer_sweep(mx, torch, reps=9):
 class Step:
     """Holds device inputs/outputs and enqueues one step as a list of named calls."""
 
-    def __init__(self, name, seed, mx, torch, fused_backward=True):
+    def __init__(self, name, seed, mx, torch, fused_backward=True, dgrad_epilogue=False):
         self.fused_backward = fused_backward
+        self.dgrad_epilogue = dgrad_epilogue and fused_backward
         import synthetic
         self.mx, self.torch = mx, torch
         self.name = name
@@ -308,7 +312,16 @@ class Step:
         else:
             dyr = self.q_rows("rows(dY,SR)", dY, 1, 0)
             dyc = self.q_cols("cols(dY,H32)", dY)
-        dh = self.gemm("W2 Dgrad", dyr, w2[2:])
+        if self.dgrad_epilogue:
+            # dH = dY W2 with the SwiGLU backward producer in the epilogue
+            shapes = [(T, F // 2), (T, F // 32)] * 2
+            outs = [self.u8(*shp) for shp in shapes] + [None] * 4
+            label = "W2 Dgrad + swiglu_bwd_producer"
+            self.calls.append((label, "producer", 2.0 * T * F * D,
+                               lambda: mx.fp4_gemm_swiglu_backward_producer(dyr[0], dyr[1], w2[2], w2[3], a, b,
+                                                                            self.seed, 1, 2, self.mask, outs), 0))
+        else:
+            dh = self.gemm("W2 Dgrad", dyr, w2[2:])
         self.gemm("W2 Wgrad", dyc, hc)
         # column-facing dA and dB land in one stacked [2F][T/2] buffer, so that
         # the W1 and W3 Wgrads (same B operand, X column-facing) run as one
@@ -316,7 +329,10 @@ class Step:
         # each) become 1792 (7 full rounds)
         dabc = (self.u8(2 * F, T // 2), self.u8(2 * F, T // 32))
         dac, dbc = (dabc[0][:F], dabc[1][:F]), (dabc[0][F:], dabc[1][F:])
-        if self.fused_backward:
+        if self.dgrad_epilogue:
+            outs[4:] = [dac[0], dac[1], dbc[0], dbc[1]]
+            dar, dbr = (outs[0], outs[1]), (outs[2], outs[3])
+        elif self.fused_backward:
             shapes = [(T, F // 2), (T, F // 32)] * 2
             outs = [self.u8(*shp) for shp in shapes] + [dac[0], dac[1], dbc[0], dbc[1]]
             dar, dbr = (outs[0], outs[1]), (outs[2], outs[3])
@@ -337,7 +353,10 @@ class Step:
         self.gemm_pair("W1+W3 Dgrad", dar, w1[2:], dbr, w3[2:])
         # each producer is charged to the first contraction that reads it
         self.charge = {"swiglu_producer": ["w2d32(W1)", "w2d32(W3)"], "W2 Fprop": ["w2d32(W2)"]}
-        if self.fused_backward:
+        if self.dgrad_epilogue:
+            self.charge["swiglu_producer"].append("dual(X: RTN rows, H32 cols)")
+            self.charge["W2 Dgrad + swiglu_bwd_producer"] = ["dual(dY: SR rows, H32 cols)"]
+        elif self.fused_backward:
             self.charge["swiglu_producer"].append("dual(X: RTN rows, H32 cols)")
             self.charge["W2 Dgrad"] = ["dual(dY: SR rows, H32 cols)"]
         else:
@@ -345,7 +364,9 @@ class Step:
             self.charge["W2 Dgrad"] = ["rows(dY,SR)"]
             self.charge["W2 Wgrad"] = ["cols(dY,H32)"]
             self.charge["W1|W3 Wgrad"] = ["cols(X,H32)"]
-        if self.fused_backward:
+        if self.dgrad_epilogue:
+            pass
+        elif self.fused_backward:
             self.charge["W1+W3 Dgrad"] = ["swiglu_bwd_producer"]
         else:
             self.charge["W1+W3 Dgrad"] = ["swiglu_backward", "rows(dA,SR)", "rows(dB,SR)"]
@@ -454,6 +475,9 @@ QUALITY_CASES = {
 }
 
 
+SR_DRAWS = 8
+
+
 def quality_metrics(c, ref):
     """Error of an MXFP4 contraction c against its fp32 reference ref (both
     converted to float64): relative L2 error ||c - ref|| / ||ref||, the SNR
@@ -498,6 +522,15 @@ def quality_report(mx, torch):
                 for mode, mtag in ((mx.FP4_SR, "SR"), (mx.FP4_RTN, "RTN")):
                     dyr = mx.fp4_quantize_rows(dY, mode, seed, 0)
                     score("Dgrad", f"dY {mtag}, W 2D32 columns", mx.fp4_gemm(dyr[0], dyr[1], wq[2], wq[3]))
+                # SR's point is an unbiased estimate across steps: the mean of
+                # independent draws (offsets 0..7) approaches the exact product
+                # while RTN's error stays
+                acc = None
+                for off in range(SR_DRAWS):
+                    dyr = mx.fp4_quantize_rows(dY, mx.FP4_SR, seed, off)
+                    c = mx.fp4_gemm(dyr[0], dyr[1], wq[2], wq[3])
+                    acc = c if acc is None else acc.add_(c)
+                score("Dgrad", f"dY SR, mean of {SR_DRAWS} draws, W 2D32 columns", acc.div_(SR_DRAWS))
         wr = mx.fp4_quantize_rows(W)
         score("Fprop", "1x32 weight blocks", mx.fp4_gemm(xr[0], xr[1], wr[0], wr[1]))
         for had, tag in ((32, "paired fixed-sign H32"), (0, "no Hadamard")):
@@ -530,7 +563,8 @@ def main():
         print(json.dumps({"quantizer_sweep": quantizer_sweep(mx, torch)}), flush=True)
         return
     print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
-    step = Step(args.workload, args.seed, mx, torch, fused_backward=not args.unfused_backward)
+    step = Step(args.workload, args.seed, mx, torch, fused_backward=not args.unfused_backward,
+                dgrad_epilogue=args.dgrad_epilogue)
     ncalls = len(step.calls)
     print(f"[bench] warmup {args.warmup} steps, {ncalls} calls per step", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -616,7 +650,8 @@ def main():
         "dtype": "e2m1/e8m0 operands, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": args.workload, "gemm_tflop_per_step": round(flops / 1e12, 3),
-                   "swiglu_backward": "unfused" if args.unfused_backward else "fused producer",
+                   "swiglu_backward": ("unfused" if args.unfused_backward else
+                                       "in the W2 Dgrad epilogue" if step.dgrad_epilogue else "fused producer"),
                    "launch": mode,
                    "quantizer_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1) if q_ms > 0 else None,
                    "quantizer_frac_hbm_peak": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if q_ms > 0 else None},

@@ -272,6 +272,37 @@ fp4_status fp4_swiglu_backward_producer(int64_t t, int64_t f, const float* dh, i
                                         uint8_t* dbt_codes, uint8_t* dbt_scales, void* stream);
 
 /*
+ * W2 data gradient with the fused SwiGLU backward producer in its epilogue
+ * (§3.2: the backward combines the W2 data gradient with the SiLU derivative
+ * and produces the representations the W1/W3 data- and weight-gradient
+ * contractions consume; §3.1).  Bit-identical to
+ *   fp4_gemm(t, f, d, dy_codes, dy_scales, w2c_codes, w2c_scales) -> dH (fp32)
+ *   fp4_swiglu_backward_producer(t, f, dH, f, a, b, seed, offset_a, offset_b,
+ *                                sign_mask16, ...)
+ * without writing or reading dH: each 256 x 256 tile of dH stays on chip.
+ *   dy_codes [t][d/2], dy_scales [t][d/32]      (Q_r(dY), SR)
+ *   w2c_codes [f][d/2], w2c_scales [f][d/32]    (2D32 column layout of W2 [d][f])
+ *   a_bf16, b_bf16 [t][f]                       (saved gate / up outputs)
+ *   da_codes, db_codes [t][f/2]; da_scales, db_scales [t][f/32]
+ *   dat_codes, dbt_codes [f][t/2]; dat_scales, dbt_scales [f][t/32]
+ * Errors: FP4_EINVAL null pointer; FP4_ESHAPE t, f or d not a non-negative
+ * multiple of 32, d not a positive multiple of 256 (the fused main loop's K
+ * step), f >= 2^22 or d >= 2^24 (32-bit offsets within a 256-row panel), or
+ * more than 2^31 - 1 tiles; FP4_EALIGN an operand, a_bf16, b_bf16 or a code
+ * buffer not 16-byte aligned.
+ */
+fp4_status fp4_gemm_swiglu_backward_producer(int64_t t, int64_t f, int64_t d,
+                                             const uint8_t* dy_codes, const uint8_t* dy_scales,
+                                             const uint8_t* w2c_codes, const uint8_t* w2c_scales,
+                                             const uint16_t* a_bf16, const uint16_t* b_bf16,
+                                             uint64_t seed, uint64_t offset_a, uint64_t offset_b,
+                                             uint32_t sign_mask16,
+                                             uint8_t* da_codes, uint8_t* da_scales,
+                                             uint8_t* db_codes, uint8_t* db_scales,
+                                             uint8_t* dat_codes, uint8_t* dat_scales,
+                                             uint8_t* dbt_codes, uint8_t* dbt_scales, void* stream);
+
+/*
  * Fixed 16-entry sign vector for H32 as a bit mask (bit j set => d_j = -1).
  * App. A.1 fixes one 16-entry sign vector, shared by both Wgrad operands and
  * repeated over the two halves of each 32-value block, but its literal

@@ -34,6 +34,7 @@ _SIGS = {
     "fp4_swiglu_producer": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u32, _vp],
     "fp4_swiglu_backward": [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp],
     "fp4_swiglu_backward_producer": [_i64, _i64, _vp, _i64, _vp, _vp, _u64, _u64, _u64, _u32] + [_vp] * 9,
+    "fp4_gemm_swiglu_backward_producer": [_i64, _i64, _i64] + [_vp] * 6 + [_u64, _u64, _u64, _u32] + [_vp] * 9,
     "fp4_sign_mask_from_seed": [_u64],
     "fp4_last_hip_error": [],
     "fp4_abi_version": [],
@@ -283,6 +284,36 @@ def fp4_swiglu_backward_producer(dh, a, b, seed, offset_a, offset_b, sign_mask16
     bufs = [_out(o, shp, torch.uint8, dev, nm) for o, shp, nm in zip(out, shapes, names)]
     _check(load().fp4_swiglu_backward_producer(t, f, _p(dh), dh.stride(0), _p(a), _p(b), int(seed), int(offset_a),
                                                int(offset_b), int(sign_mask16), *[_p(x) for x in bufs], _stream()))
+    return (bufs[0], bufs[1]), (bufs[2], bufs[3]), (bufs[4], bufs[5]), (bufs[6], bufs[7])
+
+
+def fp4_gemm_swiglu_backward_producer(dy_codes, dy_scales, w2c_codes, w2c_scales, a, b, seed, offset_a, offset_b,
+                                      sign_mask16, out=None):
+    """W2 Dgrad dH = Q_r(dY) W2_c^T with the SwiGLU backward producer in its
+    epilogue: returns ((da_codes, da_scales), (db_codes, db_scales),
+    (dat_codes, dat_scales), (dbt_codes, dbt_scales)), the bytes of fp4_gemm
+    followed by fp4_swiglu_backward_producer, without dH in memory."""
+    _u8_2d(dy_codes, "dy_codes")
+    _u8_2d(w2c_codes, "w2c_codes")
+    t, d2 = dy_codes.shape
+    f, wd2 = w2c_codes.shape
+    d = 2 * d2
+    if wd2 != d2:
+        raise Fp4Error(f"w2c_codes has {2 * wd2} values per row, dy_codes {d}")
+    _u8_2d(dy_scales, "dy_scales", (t, d // 32))
+    _u8_2d(w2c_scales, "w2c_scales", (f, d // 32))
+    _bf16_tf(a, "a", (t, f))
+    _bf16_tf(b, "b", (t, f))
+    dev = a.device
+    shapes = [(t, f // 2), (t, f // 32), (t, f // 2), (t, f // 32),
+              (f, t // 2), (f, t // 32), (f, t // 2), (f, t // 32)]
+    names = ["da_codes", "da_scales", "db_codes", "db_scales", "dat_codes", "dat_scales", "dbt_codes", "dbt_scales"]
+    out = list(out) if out is not None else [None] * 8
+    bufs = [_out(o, shp, torch.uint8, dev, nm) for o, shp, nm in zip(out, shapes, names)]
+    _check(load().fp4_gemm_swiglu_backward_producer(t, f, d, _p(dy_codes), _p(dy_scales), _p(w2c_codes),
+                                                    _p(w2c_scales), _p(a), _p(b), int(seed), int(offset_a),
+                                                    int(offset_b), int(sign_mask16), *[_p(x) for x in bufs],
+                                                    _stream()))
     return (bufs[0], bufs[1]), (bufs[2], bufs[3]), (bufs[4], bufs[5]), (bufs[6], bufs[7])
 
 

@@ -79,6 +79,13 @@ int main() {
   expect("bwd producer empty", fp4_swiglu_backward_producer(64, 0, nullptr, 0, nullptr, nullptr, 0, 0, 1, 0, nullptr,
                                                             nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                                             nullptr, nullptr), FP4_OK);
+  expect("dgrad+bwd short k", fp4_gemm_swiglu_backward_producer(32, 32, 288, b, b, b, b, h, h, 0, 0, 1, 0, b, b, b, b,
+                                                               b, b, b, b, nullptr), FP4_ESHAPE);
+  expect("dgrad+bwd tiles", fp4_gemm_swiglu_backward_producer(big, 1 << 21, 256, b, b, b, b, h, h, 0, 0, 1, 0, b, b,
+                                                             b, b, b, b, b, b, nullptr), FP4_ESHAPE);
+  expect("dgrad+bwd empty", fp4_gemm_swiglu_backward_producer(0, 64, 256, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                             nullptr, 0, 0, 1, 0, nullptr, nullptr, nullptr, nullptr,
+                                                             nullptr, nullptr, nullptr, nullptr, nullptr), FP4_OK);
   // the host-side generator: every seed, including ones whose halves carry
   for (uint64_t s : {0ull, 1ull, 0xFFFFFFFFull, 0x100000000ull, 0xFFFFFFFFFFFFFFFFull})
     if (fp4_sign_mask_from_seed(s) > 0xFFFFu) {

@@ -26,7 +26,8 @@ def test_header_declares_the_hot_path_calls():
     names = declared_functions()
     for n in ("fp4_quantize_rows", "fp4_quantize_cols", "fp4_quantize_dual", "fp4_quantize_w2d32", "fp4_gemm",
               "fp4_gemm_pair",
-              "fp4_swiglu_producer", "fp4_swiglu_backward", "fp4_swiglu_backward_producer"):
+              "fp4_swiglu_producer", "fp4_swiglu_backward", "fp4_swiglu_backward_producer",
+              "fp4_gemm_swiglu_backward_producer"):
         assert n in names
 
 
@@ -119,6 +120,17 @@ def test_size_limit_errors_are_reported_without_gpu_work():
     assert lib.fp4_gemm(huge, huge, 32, v(4096), v(4096), v(4096), v(4096), v(4096), huge, 0, None) == 2
     assert lib.fp4_gemm_pair(huge, huge, 256, *([v(4096)] * 8), v(4096), huge, 0, None) == 2
     assert lib.fp4_swiglu_producer(huge, huge, 32, *([v(4096)] * 10), 0, None) == 2
+    fb = [v(4096)] * 8
+    assert lib.fp4_gemm_swiglu_backward_producer(32, 32, 288, *([v(4096)] * 6), u64(0), u64(0), u64(1), 0, *fb,
+                                                 None) == 2                     # d not a multiple of 256
+    assert lib.fp4_gemm_swiglu_backward_producer(32, 1 << 22, 256, *([v(4096)] * 6), u64(0), u64(0), u64(1), 0,
+                                                 *fb, None) == 2                # f beyond the 32-bit panel offsets
+    assert lib.fp4_gemm_swiglu_backward_producer(32, 32, 256, *([v(4096)] * 5), None, u64(0), u64(0), u64(1), 0,
+                                                 *fb, None) == 1
+    assert lib.fp4_gemm_swiglu_backward_producer(32, 32, 256, *([v(4096)] * 6), u64(0), u64(0), u64(1), 0,
+                                                 *fb[:6], v(4100), fb[7], None) == 3   # misaligned dbt_codes
+    assert lib.fp4_gemm_swiglu_backward_producer(0, 64, 256, *([None] * 6), u64(0), u64(0), u64(1), 0,
+                                                 *([None] * 8), None) == 0      # empty
     # just inside the limits the checks pass on to the (here absent) alignment check
     assert lib.fp4_quantize_cols(v(4098), big_rows - 128, 32, 32, v(4096), v(4096), 32, 0, None) == 3
     assert lib.fp4_quantize_w2d32(v(4098), 32, 32, (1 << 22) - 8, v(4096), v(4096), v(4096), v(4096),

@@ -279,6 +279,11 @@ def test_ffn_step(gpu_lib, name):
     for got, want, nm in zip(fused, (dar, dbr, dac, dbc), ("dA rows", "dB rows", "dA cols", "dB cols")):
         assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1]), "fused " + nm
     del fused
+    # W2 Dgrad with the backward producer in its epilogue: the same bytes again
+    fused = gpu_lib.fp4_gemm_swiglu_backward_producer(dyr[0], dyr[1], w2[2], w2[3], a, b, seed, 1, 2, mask)
+    for got, want, nm in zip(fused, (dar, dbr, dac, dbc), ("dA rows", "dB rows", "dA cols", "dB cols")):
+        assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1]), "Dgrad epilogue " + nm
+    del fused
 
     # the seven contractions
     check_gemm(y, (hrc, hrs), w2[:2], rng, "W2 Fprop")

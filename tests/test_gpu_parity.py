@@ -422,6 +422,53 @@ def test_swiglu_backward_producer_strided_dh(gpu_lib, tfp):
         assert_same(g[1], w[1], nm + " scales")
 
 
+@pytest.mark.parametrize("tfd", [(256, 256, 256), (288, 160, 512), (512, 384, 256), (32, 32, 256), (96, 416, 768),
+                                 (320, 288, 512)])
+def test_gemm_swiglu_backward_producer(gpu_lib, tfd):
+    """W2 Dgrad with the SwiGLU backward producer in its epilogue, ragged
+    tiles included: every output byte equals fp4_gemm followed by
+    fp4_swiglu_backward_producer, and the oracle's SwiGLU backward and
+    quantizers on the GPU's dH (itself within the GEMM bound) give the same
+    bytes.  Outputs start as sentinels, so every byte is written."""
+    t, f, d = tfd
+    dy = synthetic.tensor((t, d), std=1e-3, seed=50)
+    w2 = synthetic.tensor((d, f), std=0.02, seed=51)
+    a = synthetic.tensor((t, f), std=1.3, seed=52)
+    b = synthetic.tensor((t, f), std=1.3, seed=53)
+    seed, oa, ob, mask = 2 ** 33 + 5, 1, 2, P.sign_mask_from_seed(6)
+    dyr = gpu_lib.fp4_quantize_rows(dev16(dy), gpu_lib.FP4_SR, seed, 0)
+    w2q = gpu_lib.fp4_quantize_w2d32(dev16(w2), 0.87)
+    ad, bd = dev16(a), dev16(b)
+    shapes = [(t, f // 2), (t, f // 32), (t, f // 2), (t, f // 32), (f, t // 2), (f, t // 32), (f, t // 2),
+              (f, t // 32)]
+    outs = [torch.full(shp, 0xAB if i % 2 == 0 else 0xFF, dtype=torch.uint8, device="cuda")
+            for i, shp in enumerate(shapes)]
+    got = gpu_lib.fp4_gemm_swiglu_backward_producer(dyr[0], dyr[1], w2q[2], w2q[3], ad, bd, seed, oa, ob, mask, outs)
+    dh = gpu_lib.fp4_gemm(dyr[0], dyr[1], w2q[2], w2q[3])
+    check_gemm(dh, dyr, w2q[2:], what="W2 Dgrad dH")
+    ref = gpu_lib.fp4_swiglu_backward_producer(dh, ad, bd, seed, oa, ob, mask)
+    for g, r, nm in zip(got, ref, ("dA rows", "dB rows", "dA cols", "dB cols")):
+        assert torch.equal(g[0], r[0]) and torch.equal(g[1], r[1]), nm
+    da, db = S.swiglu_backward(host(dh), a, b)
+    want = (Q.quantize_rows(da, Q.SR, seed, oa), Q.quantize_rows(db, Q.SR, seed, ob),
+            Q.quantize_cols(da, 32, mask), Q.quantize_cols(db, 32, mask))
+    for g, w, nm in zip(got, want, ("dA rows", "dB rows", "dA cols", "dB cols")):
+        assert_same(g[0], w[0], nm + " codes")
+        assert_same(g[1], w[1], nm + " scales")
+
+
+def test_gemm_swiglu_backward_producer_rejects_short_k(gpu_lib):
+    """The fused kernel runs the fast main loop only: d not a multiple of 256
+    is refused before any launch."""
+    t, f, d = 64, 64, 288
+    dyr = gpu_lib.fp4_quantize_rows(dev16(synthetic.tensor((t, d), std=1e-3, seed=54)), gpu_lib.FP4_SR, 0, 0)
+    w2q = gpu_lib.fp4_quantize_w2d32(dev16(synthetic.tensor((d, f), std=0.02, seed=55)), 0.87)
+    ab = dev16(synthetic.tensor((t, f), std=1.0, seed=56))
+    with pytest.raises(gpu_lib.Fp4Error):
+        gpu_lib.fp4_gemm_swiglu_backward_producer(dyr[0], dyr[1], w2q[2], w2q[3], ab, ab, 0, 1, 2, 0)
+    torch.cuda.synchronize()
+
+
 def test_empty_tensors(gpu_lib):
     """Empty inputs give empty outputs (no launch)."""
     x = torch.empty((0, 64), dtype=torch.int16, device="cuda")
