@@ -24,6 +24,8 @@ hadamard  Fixed-sign H32 transform (signs, Sylvester butterfly, 2^-2.5).
 quant     Row-facing, column-facing (optionally H32) and 2D32 producers.
 gemm      Decode-then-contract reference and the per-element error bound.
 swiglu    The exp used by both sides, SwiGLU forward/backward in fp32.
+nvfp4     CTA-local NVFP4: E4M3 16-value block scales with per-panel fp32
+          outer factors, the 2D16 weight producer, and its contraction.
 """
 
-from . import formats, philox, hadamard, quant, gemm, swiglu  # noqa: F401
+from . import formats, philox, hadamard, quant, gemm, swiglu, nvfp4  # noqa: F401
