@@ -303,6 +303,84 @@ fp4_status fp4_gemm_swiglu_backward_producer(int64_t t, int64_t f, int64_t d,
                                              uint8_t* dbt_codes, uint8_t* dbt_scales, void* stream);
 
 /*
+ * CTA-local NVFP4 (§2.2 Eq. 1 with §2.2.2 and §2.4): a value is
+ * S * delta * q with q an E2M1 code, delta an OCP E4M3FN scale byte shared by
+ * 16 values along K, and S an fp32 outer factor owned by one 256-row panel
+ * (the rows one 256 x 256 output tile of fp4_nv_gemm reads), or one factor
+ * for a whole weight.  The pages fix the roles, not the arithmetic; this
+ * library takes, in single fp32 roundings:
+ *   S = amax_panel / 2688 (2688 = 6 * 448; S = 1 for an all-zero panel),
+ *   inv6 = 1 / (6 S), delta = E4M3(amax_block * inv6) (nearest, ties to the
+ *   even mantissa, saturating at 448; 0x7F is never written),
+ *   r = 1 / (delta * S) (r = 0 when delta = 0: the block vanishes),
+ *   y = |x| * r, then RTN E2M1 (saturating at 6) or, for FP4_SR, the
+ *   adjacent-bin rule of §2.5 Eq. 9 on min(y, 6) with the draws of
+ *   fp4_quantize_rows (same Philox counters for the same (seed, offset)).
+ * "nv scales" hold one E4M3 byte per 16 values.  Every panel maximum must be 0
+ * or at least 2^-100 (below that the reciprocals overflow and codes are
+ * unspecified).
+ */
+
+/*
+ * Row-facing CTA-local NVFP4 of an activation or gradient X [rows][cols]
+ * along cols (the consuming GEMM's K).  Writes the panel maxima (fp32, one per
+ * 256 rows, the last panel may be short), the factors S and the codes.
+ *   x          [rows][ldx] bf16
+ *   codes      [rows][cols/2] u8, scales [rows][cols/16] u8 (E4M3)
+ *   factors    [ceil(rows/256)] fp32,  panel_amax [ceil(rows/256)] fp32
+ * Three kernels: zero the maxima, reduce them (atomic max), quantize.
+ * Errors: FP4_EINVAL bad mode or null pointer; FP4_ESHAPE rows < 0, cols not a
+ * non-negative multiple of 32, ldx < cols, or rows > 2097120 (65535 groups of
+ * 32 rows); FP4_EALIGN x or codes not 16-byte aligned, or ldx not a multiple
+ * of 8.
+ */
+fp4_status fp4_nv_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t* codes, uint8_t* scales, float* factors,
+                                float* panel_amax, int mode, uint64_t seed, uint64_t offset,
+                                void* stream);
+
+/*
+ * CTA-local 2D16 weight producer (§2.4 with §2.2.2): one E4M3 scale per 16x16
+ * tile of W [n][k], one fp32 outer factor S_W = amax_W / 2688 for the whole
+ * tensor, RTN codes, one encoding in both layouts (col codes at (j, i) hold the
+ * nibble of row codes at (i, j); each 1x16 scale byte is its tile's byte).
+ *   w          [n][ldw] bf16
+ *   row_codes  [n][k/2],  row_scales [n][k/16]   (Fprop view)
+ *   col_codes  [k][n/2],  col_scales [k][n/16]   (Dgrad view)
+ *   factor     [1] fp32 (S_W),  amax_out [1] fp32 (amax_W)
+ * Errors: FP4_EINVAL null pointer; FP4_ESHAPE n or k not a non-negative
+ * multiple of 32, ldw < k, or n > 2097120; FP4_EALIGN w, row_codes or
+ * col_codes not 16-byte aligned, or ldw not a multiple of 8.
+ */
+fp4_status fp4_nv_quantize_w2d16(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
+                                 uint8_t* row_codes, uint8_t* row_scales,
+                                 uint8_t* col_codes, uint8_t* col_scales,
+                                 float* factor, float* amax_out, void* stream);
+
+/*
+ * Contraction of two CTA-local NVFP4 operands, NT form:
+ *   C[m][n] (+)= RN(S_A(m) * S_B(n)) * sum_k (delta_a q_a)(delta_b q_b)
+ * with S_A(m) = a_factors[(m / 256) * a_factor_stride] and likewise for B
+ * (stride 1: one factor per 256-row panel, as fp4_nv_quantize_rows writes;
+ * stride 0: one factor, as fp4_nv_quantize_w2d16 writes).  Each product
+ * delta * q is exact in bf16; the sum runs on the bf16 matrix cores in fp32;
+ * the factor product is applied once per output in the epilogue.
+ *   a_codes [m][k/2], a_scales [m][k/16]; b_codes [n][k/2], b_scales [n][k/16]
+ *   c       [m][ldc] fp32
+ * Errors: FP4_EINVAL accumulate not 0 or 1, negative stride or null pointer;
+ * FP4_ESHAPE m or n not a non-negative multiple of 32, k not a non-negative
+ * multiple of 64, ldc < n, k >= 2^24, or more than 2^31 - 1 output tiles;
+ * FP4_EALIGN a code buffer or c not 16-byte aligned, or ldc not a multiple
+ * of 4.  k = 0 writes C = 0 (unchanged when accumulating).
+ */
+fp4_status fp4_nv_gemm(int64_t m, int64_t n, int64_t k,
+                       const uint8_t* a_codes, const uint8_t* a_scales,
+                       const float* a_factors, int64_t a_factor_stride,
+                       const uint8_t* b_codes, const uint8_t* b_scales,
+                       const float* b_factors, int64_t b_factor_stride,
+                       float* c, int64_t ldc, int accumulate, void* stream);
+
+/*
  * Fixed 16-entry sign vector for H32 as a bit mask (bit j set => d_j = -1).
  * App. A.1 fixes one 16-entry sign vector, shared by both Wgrad operands and
  * repeated over the two halves of each 32-value block, but its literal

@@ -35,6 +35,9 @@ _SIGS = {
     "fp4_swiglu_backward": [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp],
     "fp4_swiglu_backward_producer": [_i64, _i64, _vp, _i64, _vp, _vp, _u64, _u64, _u64, _u32] + [_vp] * 9,
     "fp4_gemm_swiglu_backward_producer": [_i64, _i64, _i64] + [_vp] * 6 + [_u64, _u64, _u64, _u32] + [_vp] * 9,
+    "fp4_nv_quantize_rows": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _int, _u64, _u64, _vp],
+    "fp4_nv_quantize_w2d16": [_vp, _i64, _i64, _i64] + [_vp] * 7,
+    "fp4_nv_gemm": [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _int, _vp],
     "fp4_sign_mask_from_seed": [_u64],
     "fp4_last_hip_error": [],
     "fp4_abi_version": [],
@@ -315,6 +318,73 @@ def fp4_gemm_swiglu_backward_producer(dy_codes, dy_scales, w2c_codes, w2c_scales
                                                     int(offset_b), int(sign_mask16), *[_p(x) for x in bufs],
                                                     _stream()))
     return (bufs[0], bufs[1]), (bufs[2], bufs[3]), (bufs[4], bufs[5]), (bufs[6], bufs[7])
+
+
+def fp4_nv_quantize_rows(x, mode=FP4_RTN, seed=0, offset=0, out=None):
+    """CTA-local NVFP4 of x along its columns: returns (codes [r][c/2],
+    scales [r][c/16] E4M3 bytes, factors [ceil(r/256)] fp32, panel maxima
+    [ceil(r/256)] fp32)."""
+    x = _bf16_2d(x, "x")
+    rows, cols = x.shape
+    panels = (rows + 255) // 256
+    out = list(out) if out is not None else [None] * 4
+    codes = _out(out[0], (rows, cols // 2), torch.uint8, x.device, "codes")
+    scales = _out(out[1], (rows, cols // 16), torch.uint8, x.device, "scales")
+    factors = _out(out[2], (panels,), torch.float32, x.device, "factors")
+    amax = _out(out[3], (panels,), torch.float32, x.device, "panel_amax")
+    _check(load().fp4_nv_quantize_rows(_p(x), rows, cols, x.stride(0), _p(codes), _p(scales), _p(factors),
+                                       _p(amax), int(mode), int(seed), int(offset), _stream()))
+    return codes, scales, factors, amax
+
+
+def fp4_nv_quantize_w2d16(w, out=None):
+    """CTA-local 2D16 weight encoding: returns (row_codes, row_scales,
+    col_codes, col_scales, factor [1], amax [1])."""
+    w = _bf16_2d(w, "w")
+    n, k = w.shape
+    shapes = [(n, k // 2), (n, k // 16), (k, n // 2), (k, n // 16)]
+    names = ["row_codes", "row_scales", "col_codes", "col_scales"]
+    out = list(out) if out is not None else [None] * 6
+    bufs = [_out(o, shp, torch.uint8, w.device, nm) for o, shp, nm in zip(out[:4], shapes, names)]
+    factor = _out(out[4], (1,), torch.float32, w.device, "factor")
+    amax = _out(out[5], (1,), torch.float32, w.device, "amax")
+    _check(load().fp4_nv_quantize_w2d16(_p(w), n, k, w.stride(0), *[_p(b) for b in bufs], _p(factor), _p(amax),
+                                        _stream()))
+    return (*bufs, factor, amax)
+
+
+def fp4_nv_gemm(a_codes, a_scales, a_factors, b_codes, b_scales, b_factors, c=None, accumulate=False):
+    """C (+)= RN(S_A S_B) * sum_k dec(A) dec(B) over CTA-local NVFP4 operands.
+    A factor vector of one element is shared by all rows (stride 0); otherwise
+    it holds one factor per 256-row panel."""
+    _u8_2d(a_codes, "a_codes")
+    _u8_2d(b_codes, "b_codes")
+    m, k2 = a_codes.shape
+    n = b_codes.shape[0]
+    k = 2 * k2
+    if b_codes.shape[1] != k2:
+        raise Fp4Error("operand shapes disagree")
+    _u8_2d(a_scales, "a_scales", (m, k // 16))
+    _u8_2d(b_scales, "b_scales", (n, k // 16))
+    strides = []
+    for fac, rows, nm in ((a_factors, m, "a_factors"), (b_factors, n, "b_factors")):
+        _dev(fac, nm)
+        panels = (rows + 255) // 256
+        if fac.dtype != torch.float32 or fac.dim() != 1 or not fac.is_contiguous() or fac.numel() not in (1, panels):
+            raise Fp4Error(f"{nm} must be a contiguous fp32 vector of 1 or {panels} elements")
+        strides.append(0 if fac.numel() == 1 else 1)
+    if c is None:
+        if accumulate:
+            raise Fp4Error("accumulate needs an output tensor")
+        c = torch.empty((m, n), dtype=torch.float32, device=a_codes.device)
+    else:
+        _dev(c, "c")
+        if c.dtype != torch.float32 or c.dim() != 2 or c.stride(1) != 1 or tuple(c.shape) != (m, n):
+            raise Fp4Error("c must be fp32 [m][n] with unit column stride")
+    _check(load().fp4_nv_gemm(m, n, k, _p(a_codes), _p(a_scales), _p(a_factors), strides[0], _p(b_codes),
+                              _p(b_scales), _p(b_factors), strides[1], _p(c), c.stride(0), 1 if accumulate else 0,
+                              _stream()))
+    return c
 
 
 def fp4_sign_mask_from_seed(seed):

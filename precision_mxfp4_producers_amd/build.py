@@ -17,7 +17,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libmxfp4.so"
-SOURCES = ["quantize.hip", "gemm.hip", "swiglu_bwd.hip", "dgrad_swiglu_bwd.hip"]
+SOURCES = ["quantize.hip", "gemm.hip", "swiglu_bwd.hip", "dgrad_swiglu_bwd.hip", "nvfp4.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -86,6 +86,39 @@ int main() {
   expect("dgrad+bwd empty", fp4_gemm_swiglu_backward_producer(0, 64, 256, nullptr, nullptr, nullptr, nullptr, nullptr,
                                                              nullptr, 0, 0, 1, 0, nullptr, nullptr, nullptr, nullptr,
                                                              nullptr, nullptr, nullptr, nullptr, nullptr), FP4_OK);
+  const int64_t i64max = INT64_MAX;
+  expect("nv rows mode", fp4_nv_quantize_rows(x, 32, 32, 32, b, b, c, c, 2, 0, 0, nullptr), FP4_EINVAL);
+  expect("nv rows shape", fp4_nv_quantize_rows(x, 32, 48, 48, b, b, c, c, 0, 0, 0, nullptr), FP4_ESHAPE);
+  expect("nv rows null", fp4_nv_quantize_rows(x, 32, 32, 32, b, b, c, nullptr, 0, 0, 0, nullptr), FP4_EINVAL);
+  expect("nv rows limit", fp4_nv_quantize_rows(x, 65536 * 32, 32, 32, b, b, c, c, 1, 0, 0, nullptr), FP4_ESHAPE);
+  expect("nv rows max", fp4_nv_quantize_rows(x, i64max, 32, 32, b, b, c, c, 1, 0, 0, nullptr), FP4_ESHAPE);
+  expect("nv rows huge cols", fp4_nv_quantize_rows(x, 32, big * 32, big * 32, b, b, c, c, 0, 0, 0, nullptr),
+         FP4_ESHAPE);
+  expect("nv rows align", fp4_nv_quantize_rows(x, 32, 32, 36, b, b, c, c, 0, 0, 0, nullptr), FP4_EALIGN);
+  expect("nv rows empty", fp4_nv_quantize_rows(nullptr, 0, 64, 64, nullptr, nullptr, nullptr, nullptr, 1, 0, 0,
+                                               nullptr), FP4_OK);
+  expect("nv w2d16 shape", fp4_nv_quantize_w2d16(x, 48, 32, 32, b, b, b, b, c, c, nullptr), FP4_ESHAPE);
+  expect("nv w2d16 null", fp4_nv_quantize_w2d16(x, 32, 32, 32, b, b, b, nullptr, c, c, nullptr), FP4_EINVAL);
+  expect("nv w2d16 limit", fp4_nv_quantize_w2d16(x, 65536 * 32, 32, 32, b, b, b, b, c, c, nullptr), FP4_ESHAPE);
+  expect("nv w2d16 huge k", fp4_nv_quantize_w2d16(x, 32, i64max - 31, i64max, b, b, b, b, c, c, nullptr),
+         FP4_ESHAPE);
+  expect("nv w2d16 align", fp4_nv_quantize_w2d16(x, 32, 32, 32, b, b, static_cast<uint8_t*>(odd), b, c, c, nullptr),
+         FP4_EALIGN);
+  expect("nv gemm k", fp4_nv_gemm(32, 32, 32, b, b, c, 1, b, b, c, 0, c, 32, 0, nullptr), FP4_ESHAPE);
+  expect("nv gemm long k", fp4_nv_gemm(32, 32, (int64_t)1 << 24, b, b, c, 1, b, b, c, 0, c, 32, 0, nullptr),
+         FP4_ESHAPE);
+  expect("nv gemm huge k", fp4_nv_gemm(32, 32, i64max - 63, b, b, c, 1, b, b, c, 0, c, 32, 0, nullptr), FP4_ESHAPE);
+  expect("nv gemm stride", fp4_nv_gemm(32, 32, 64, b, b, c, -1, b, b, c, 0, c, 32, 0, nullptr), FP4_EINVAL);
+  expect("nv gemm acc", fp4_nv_gemm(32, 32, 64, b, b, c, 1, b, b, c, 0, c, 32, 3, nullptr), FP4_EINVAL);
+  expect("nv gemm null", fp4_nv_gemm(32, 32, 64, b, b, nullptr, 1, b, b, c, 0, c, 32, 0, nullptr), FP4_EINVAL);
+  expect("nv gemm tiles", fp4_nv_gemm(big, big, 64, b, b, c, 1, b, b, c, 0, c, big, 0, nullptr), FP4_ESHAPE);
+  expect("nv gemm max", fp4_nv_gemm(i64max - 31, i64max - 31, 64, b, b, c, 1, b, b, c, 0, c, i64max, 0, nullptr),
+         FP4_ESHAPE);
+  expect("nv gemm align", fp4_nv_gemm(32, 32, 64, b, b, c, 1, b, b, c, 0, c, 34, 0, nullptr), FP4_EALIGN);
+  expect("nv gemm k0 acc", fp4_nv_gemm(64, 64, 0, nullptr, nullptr, nullptr, 1, nullptr, nullptr, nullptr, 0, c, 64,
+                                       1, nullptr), FP4_OK);
+  expect("nv gemm empty", fp4_nv_gemm(0, 64, 64, nullptr, nullptr, nullptr, 1, nullptr, nullptr, nullptr, 0, nullptr,
+                                      64, 0, nullptr), FP4_OK);
   // the host-side generator: every seed, including ones whose halves carry
   for (uint64_t s : {0ull, 1ull, 0xFFFFFFFFull, 0x100000000ull, 0xFFFFFFFFFFFFFFFFull})
     if (fp4_sign_mask_from_seed(s) > 0xFFFFu) {

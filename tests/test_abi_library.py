@@ -27,7 +27,7 @@ def test_header_declares_the_hot_path_calls():
     for n in ("fp4_quantize_rows", "fp4_quantize_cols", "fp4_quantize_dual", "fp4_quantize_w2d32", "fp4_gemm",
               "fp4_gemm_pair",
               "fp4_swiglu_producer", "fp4_swiglu_backward", "fp4_swiglu_backward_producer",
-              "fp4_gemm_swiglu_backward_producer"):
+              "fp4_gemm_swiglu_backward_producer", "fp4_nv_quantize_rows", "fp4_nv_quantize_w2d16", "fp4_nv_gemm"):
         assert n in names
 
 
@@ -50,7 +50,7 @@ def test_host_only_calls():
     from oracle import philox as P
     lib = mx.load(LIB)
     assert lib.fp4_abi_version() >> 16 == 1
-    assert lib.fp4_abi_version() & 0xFFFF >= 2      # fp4_gemm_pair, fp4_quantize_dual
+    assert lib.fp4_abi_version() & 0xFFFF >= 3      # fp4_gemm_pair, fp4_quantize_dual; the fp4_nv_* calls
     # the library's host sign-mask helper agrees with the oracle's generator
     for seed in (0, 1, 2 ** 40 + 7):
         assert mx.fp4_sign_mask_from_seed(seed) == P.sign_mask_from_seed(seed)
@@ -135,6 +135,34 @@ def test_size_limit_errors_are_reported_without_gpu_work():
     assert lib.fp4_quantize_cols(v(4098), big_rows - 128, 32, 32, v(4096), v(4096), 32, 0, None) == 3
     assert lib.fp4_quantize_w2d32(v(4098), 32, 32, (1 << 22) - 8, v(4096), v(4096), v(4096), v(4096),
                                   ctypes.c_float(0.87), None) == 3
+
+
+def test_nvfp4_argument_errors_without_gpu_work():
+    """The CTA-local NVFP4 calls: bad enums, shapes, limits, alignment, empty
+    outputs -- all answered by the host checks."""
+    import precision_mxfp4_producers_amd as mx
+    lib = mx.load(LIB)
+    v, u64 = ctypes.c_void_p, ctypes.c_uint64
+    p = v(4096)
+    assert lib.fp4_nv_quantize_rows(p, 32, 32, 32, p, p, p, p, 2, u64(0), u64(0), None) == 1
+    assert lib.fp4_nv_quantize_rows(p, 32, 48, 48, p, p, p, p, 0, u64(0), u64(0), None) == 2
+    assert lib.fp4_nv_quantize_rows(p, 65536 * 32, 32, 32, p, p, p, p, 0, u64(0), u64(0), None) == 2
+    assert lib.fp4_nv_quantize_rows(p, 65535 * 32, 32, 32, v(4098), p, p, p, 0, u64(0), u64(0), None) == 3
+    assert lib.fp4_nv_quantize_rows(p, 32, 32, 32, p, p, None, p, 0, u64(0), u64(0), None) == 1
+    assert lib.fp4_nv_quantize_rows(None, 0, 64, 64, None, None, None, None, 1, u64(0), u64(0), None) == 0
+    assert lib.fp4_nv_quantize_w2d16(p, 32, 48, 48, p, p, p, p, p, p, None) == 2
+    assert lib.fp4_nv_quantize_w2d16(p, 32, 32, 32, p, p, p, p, None, p, None) == 1
+    assert lib.fp4_nv_quantize_w2d16(p, 32, 32, 32, p, p, v(4100), p, p, p, None) == 3
+    assert lib.fp4_nv_quantize_w2d16(None, 0, 32, 32, None, None, None, None, None, None, None) == 0
+    assert lib.fp4_nv_gemm(32, 32, 32, p, p, p, 1, p, p, p, 0, p, 32, 0, None) == 2          # k % 64
+    assert lib.fp4_nv_gemm(32, 32, 1 << 24, p, p, p, 1, p, p, p, 0, p, 32, 0, None) == 2
+    assert lib.fp4_nv_gemm(32, 32, 64, p, p, p, -1, p, p, p, 0, p, 32, 0, None) == 1
+    assert lib.fp4_nv_gemm(32, 32, 64, p, p, p, 1, p, p, p, 0, p, 32, 2, None) == 1
+    assert lib.fp4_nv_gemm(32, 32, 64, p, p, p, 1, p, p, None, 0, p, 32, 0, None) == 1
+    assert lib.fp4_nv_gemm(1 << 40, 1 << 40, 64, p, p, p, 1, p, p, p, 0, p, 1 << 40, 0, None) == 2
+    assert lib.fp4_nv_gemm(32, 32, 64, p, p, p, 1, p, p, p, 0, p, 34, 0, None) == 3
+    assert lib.fp4_nv_gemm(64, 64, 0, None, None, None, 1, None, None, None, 0, p, 64, 1, None) == 0
+    assert lib.fp4_nv_gemm(0, 64, 64, None, None, None, 1, None, None, None, 0, None, 64, 0, None) == 0
 
 
 def test_empty_calls_are_noops_without_gpu_work():
