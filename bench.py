@@ -2,7 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--eager] [--unfused-backward] [--quality] [--copy-calibration]
-                    [--quantizer-sweep]
+                    [--quantizer-sweep] [--nvfp4-dgrad]
 
 A step is one pass of the whole hot path over one batch of synthetic input.
 The default workload is the full Llama-3-8B SwiGLU FFN step (T 8192, D 4096,
@@ -68,6 +68,9 @@ def parse():
     p.add_argument("--quantizer-sweep", action="store_true",
                    help="each producer alone at the FFN step's shapes after a read-only cache flush, beside a plain "
                         "streaming kernel with the same bytes read and written per element")
+    p.add_argument("--nvfp4-dgrad", action="store_true",
+                   help="the CTA-local NVFP4 Dgrad of the FFN workload (producers, bf16-MFMA contraction) call by "
+                        "call")
     return p.parse_args()
 
 
@@ -531,6 +534,22 @@ def quality_report(mx, torch):
                     c = mx.fp4_gemm(dyr[0], dyr[1], wq[2], wq[3])
                     acc = c if acc is None else acc.add_(c)
                 score("Dgrad", f"dY SR, mean of {SR_DRAWS} draws, W 2D32 columns", acc.div_(SR_DRAWS))
+        # CTA-local NVFP4 Dgrad (E4M3 16-value scales, 256-row panel factors,
+        # 2D16 weight with one factor) beside the MXFP4 Dgrad on the same
+        # tensors and draws; the error energy is the squared L2 error
+        wq = mx.fp4_quantize_w2d32(W, 0.87)
+        wn = mx.fp4_nv_quantize_w2d16(W)
+        for mode, mtag in ((mx.FP4_SR, "SR"), (mx.FP4_RTN, "RTN")):
+            dyr = mx.fp4_quantize_rows(dY, mode, seed, 0)
+            c_mx = mx.fp4_gemm(dyr[0], dyr[1], wq[2], wq[3])
+            dyn = mx.fp4_nv_quantize_rows(dY, mode, seed, 0)
+            c_nv = mx.fp4_nv_gemm(dyn[0], dyn[1], dyn[2], wn[2], wn[3], wn[4])
+            score("Dgrad", f"CTA-local NVFP4: dY {mtag}, W 2D16 columns", c_nv)
+            e_mx = float(((c_mx.double() - refs["Dgrad"].double()) ** 2).sum())
+            e_nv = float(((c_nv.double() - refs["Dgrad"].double()) ** 2).sum())
+            out.append({"workload": name, "contraction": "Dgrad", "variant": f"error energy ratio E_MX / E_NV, dY {mtag}",
+                        "e_mx": e_mx, "e_nv": e_nv, "ratio": round(e_mx / e_nv, 4)})
+            del c_mx, c_nv
         wr = mx.fp4_quantize_rows(W)
         score("Fprop", "1x32 weight blocks", mx.fp4_gemm(xr[0], xr[1], wr[0], wr[1]))
         for had, tag in ((32, "paired fixed-sign H32"), (0, "no Hadamard")):
@@ -540,6 +559,83 @@ def quality_report(mx, torch):
         del refs
         torch.cuda.empty_cache()
     return out
+
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+B_NV_ROWS = 2 + 0.5 + 1 / 16     # bf16 in, codes and E4M3 scales out
+B_NV_W2D16 = 2 + 2 * (0.5 + 1 / 16)
+
+
+def nvfp4_dgrad(mx, torch, name, reps=7):
+    """The CTA-local NVFP4 Dgrad of the gated FFN at full size, call by call
+    (eager, HIP events, median of `reps` after two untimed passes): row SR of
+    dY and 2D16 of W2, dH = dY W2, the SwiGLU backward to bf16 dA and dB, their
+    row SR, 2D16 of W1 and W3, dX = dA W1 + dB W3 (second product accumulating).
+    a, b come from the MXFP4 forward producer.  GEMMs against the dense bf16
+    MFMA peak (the contraction runs on the bf16 matrix cores), producers
+    against HBM."""
+    import synthetic
+    h = synthetic.workload(name)
+    seed = synthetic.WORKLOADS[name]["seed"]
+    dev = lambda k: torch.from_numpy(h[k].view(np.int16)).cuda()
+    X, W1, W3, W2, dY = (dev(k) for k in ("X", "W1", "W3", "W2", "dY"))
+    T, D = X.shape
+    F = W1.shape[0]
+    xr = mx.fp4_quantize_rows(X)
+    w13 = torch.cat([W1, W3])
+    wq = mx.fp4_quantize_w2d32(w13)
+    a, b = mx.fp4_swiglu_producer(xr[0], xr[1], wq[0], wq[1], mx.fp4_sign_mask_from_seed(seed), emit_cols=False)[:2]
+    del wq, w13
+    u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device="cuda")
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device="cuda")
+    o = {}
+    o["dy"] = [u8(T, D // 2), u8(T, D // 16), f32((T + 255) // 256), f32((T + 255) // 256)]
+    for nm, (n_, k_) in (("w2", (D, F)), ("w1", (F, D)), ("w3", (F, D))):
+        o[nm] = [u8(n_, k_ // 2), u8(n_, k_ // 16), u8(k_, n_ // 2), u8(k_, n_ // 16), f32(1), f32(1)]
+    for nm in ("da", "db"):
+        o[nm] = [u8(T, F // 2), u8(T, F // 16), f32((T + 255) // 256), f32((T + 255) // 256)]
+    dh, dx = f32(T, F), f32(T, D)
+    da, db = torch.empty((T, F), dtype=torch.int16, device="cuda"), torch.empty((T, F), dtype=torch.int16, device="cuda")
+    calls = [
+        ("nv rows SR (dY)", "producer", T * D * B_NV_ROWS, lambda: mx.fp4_nv_quantize_rows(dY, 1, seed, 0, out=o["dy"])),
+        ("nv 2D16 (W2)", "producer", D * F * B_NV_W2D16, lambda: mx.fp4_nv_quantize_w2d16(W2, out=o["w2"])),
+        ("nv GEMM dH = dY W2", "gemm", 2.0 * T * F * D,
+         lambda: mx.fp4_nv_gemm(o["dy"][0], o["dy"][1], o["dy"][2], o["w2"][2], o["w2"][3], o["w2"][4], c=dh)),
+        ("SwiGLU backward (bf16 dA, dB)", "other", T * F * 12, lambda: mx.fp4_swiglu_backward(dh, a, b, da, db)),
+        ("nv rows SR (dA)", "producer", T * F * B_NV_ROWS, lambda: mx.fp4_nv_quantize_rows(da, 1, seed, 1, out=o["da"])),
+        ("nv rows SR (dB)", "producer", T * F * B_NV_ROWS, lambda: mx.fp4_nv_quantize_rows(db, 1, seed, 2, out=o["db"])),
+        ("nv 2D16 (W1)", "producer", F * D * B_NV_W2D16, lambda: mx.fp4_nv_quantize_w2d16(W1, out=o["w1"])),
+        ("nv 2D16 (W3)", "producer", F * D * B_NV_W2D16, lambda: mx.fp4_nv_quantize_w2d16(W3, out=o["w3"])),
+        ("nv GEMM dX = dA W1", "gemm", 2.0 * T * D * F,
+         lambda: mx.fp4_nv_gemm(o["da"][0], o["da"][1], o["da"][2], o["w1"][2], o["w1"][3], o["w1"][4], c=dx)),
+        ("nv GEMM dX += dB W3", "gemm", 2.0 * T * D * F,
+         lambda: mx.fp4_nv_gemm(o["db"][0], o["db"][1], o["db"][2], o["w3"][2], o["w3"][3], o["w3"][4], c=dx,
+                                accumulate=True)),
+    ]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(reps + 2)]
+    for r in range(reps + 2):
+        for i, (_, _, _, fn) in enumerate(calls):
+            ev[r][i][0].record()
+            fn()
+            ev[r][i][1].record()
+        print(f"[bench] nvfp4 dgrad pass {r + 1}/{reps + 2}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    rows, total = [], 0.0
+    for i, (label, kind, units, _) in enumerate(calls):
+        ms = float(np.median([ev[r][i][0].elapsed_time(ev[r][i][1]) for r in range(2, reps + 2)]))
+        total += ms
+        e = {"call": label, "us": round(ms * 1e3, 1)}
+        if kind == "gemm":
+            e["tflops"] = round(units / ms / 1e9, 1)
+            e["frac_bf16_mfma_peak"] = round(units / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
+        else:
+            e["gbps"] = round(units / ms / 1e6, 1)
+            e["frac_hbm_peak"] = round(units / ms / 1e6 / PEAK_HBM_GBPS, 4)
+        rows.append(e)
+    flops = sum(c[2] for c in calls if c[1] == "gemm")
+    return {"workload": name, "calls": rows, "total_us": round(total * 1e3, 1),
+            "dgrad_tflop": round(flops / 1e12, 4), "quantize_gemm_tflops": round(flops / (total * 1e-3) / 1e12, 1)}
+
 
 def main():
     args = parse()
@@ -561,6 +657,9 @@ def main():
         return
     if args.quantizer_sweep:
         print(json.dumps({"quantizer_sweep": quantizer_sweep(mx, torch)}), flush=True)
+        return
+    if args.nvfp4_dgrad:
+        print(json.dumps({"nvfp4_dgrad": nvfp4_dgrad(mx, torch, args.workload)}), flush=True)
         return
     print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
     step = Step(args.workload, args.seed, mx, torch, fused_backward=not args.unfused_backward,

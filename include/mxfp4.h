@@ -349,8 +349,9 @@ fp4_status fp4_nv_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
  *   col_codes  [k][n/2],  col_scales [k][n/16]   (Dgrad view)
  *   factor     [1] fp32 (S_W),  amax_out [1] fp32 (amax_W)
  * Errors: FP4_EINVAL null pointer; FP4_ESHAPE n or k not a non-negative
- * multiple of 32, ldw < k, or n > 2097120; FP4_EALIGN w, row_codes or
- * col_codes not 16-byte aligned, or ldw not a multiple of 8.
+ * multiple of 32, ldw < k, n > 2097120, or ldw >= 2^22 (a 128-row strip is
+ * addressed with 32-bit byte offsets); FP4_EALIGN w, row_codes or col_codes
+ * not 16-byte aligned, or ldw not a multiple of 8.
  */
 fp4_status fp4_nv_quantize_w2d16(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
                                  uint8_t* row_codes, uint8_t* row_scales,
