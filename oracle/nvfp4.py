@@ -114,13 +114,15 @@ def _encode(x64, delta, S, mode, u=None):
     return F.sign_nibble(x64, code)
 
 
-def quantize_rows(x_bits, mode=RTN, seed=0, offset=0):
+def quantize_rows(x_bits, mode=RTN, seed=0, offset=0, row0=0):
     """CTA-local NVFP4 of a bf16 tensor [R][C] along C (the consumer's K):
     returns (codes [R][C/2], scales [R][C/16] E4M3 bytes, factors [ceil(R/256)]
     fp32, panel maxima [ceil(R/256)] fp32).  SR draws as MX rows: Philox at
-    (seed, offset), element index r*C + c."""
+    (seed, offset), element index (row0 + r)*C + c.  A slice of whole panels
+    of a larger tensor (row0 a multiple of 256) gives that tensor's rows."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     R, C = x_bits.shape
+    assert row0 % PANEL == 0
     assert C % BLOCK == 0
     x = F.bf16_bits_to_f64(x_bits)
     npan = (R + PANEL - 1) // PANEL
@@ -132,16 +134,20 @@ def quantize_rows(x_bits, mode=RTN, seed=0, offset=0):
     byte, delta = block_scales(amax_b, S_row[:, None])
     u = None
     if mode == SR:
-        idx = np.arange(R, dtype=np.uint64)[:, None] * np.uint64(C) + np.arange(C, dtype=np.uint64)[None, :]
+        idx = (np.arange(R, dtype=np.uint64)[:, None] + np.uint64(row0)) * np.uint64(C) + \
+            np.arange(C, dtype=np.uint64)[None, :]
         u = P.draws(seed, offset, idx).reshape(R, C // BLOCK, BLOCK)
     nib = _encode(xb, delta, S_row[:, None], mode, u).reshape(R, C)
     return F.pack_nibbles(nib), byte.astype(np.uint8), S, amax_p
 
 
-def quantize_w2d16(w_bits):
+def quantize_w2d16(w_bits, factor=None):
     """2D16 CTA-local weight producer for W [N][K]: one E4M3 scale per 16x16
     tile, one common outer factor.  Returns (row_codes [N][K/2], row_scales
-    [N][K/16], col_codes [K][N/2], col_scales [K][N/16], factor S_W, amax_W)."""
+    [N][K/16], col_codes [K][N/2], col_scales [K][N/16], factor S_W, amax_W).
+    `factor` supplies S_W for a strip of whole 16-row tiles of a larger
+    weight (its amax_W comes from the whole tensor); amax_W is then the
+    strip's own maximum."""
     w_bits = np.asarray(w_bits, dtype=np.uint16)
     N, K = w_bits.shape
     assert N % BLOCK == 0 and K % BLOCK == 0
@@ -149,7 +155,7 @@ def quantize_w2d16(w_bits):
     tiles = w.reshape(N // BLOCK, BLOCK, K // BLOCK, BLOCK)
     amax_t = np.abs(tiles).max(axis=(1, 3))                              # [N/16][K/16]
     amax_w = np.float32(amax_t.max(initial=0.0))
-    S = outer_factor(amax_w)
+    S = outer_factor(amax_w) if factor is None else np.float32(factor)
     byte_t, delta_t = block_scales(amax_t, S)
     d_elem = np.repeat(delta_t, BLOCK, axis=0)                           # [N][K/16]
     nib = _encode(w.reshape(N, K // BLOCK, BLOCK), d_elem, S, RTN).reshape(N, K)
@@ -175,16 +181,15 @@ def decode_full(codes, scales, factors):
     return inner * S[:, None]
 
 
-def gemm_ref(a_codes, a_scales, a_factors, b_codes, b_scales, b_factors, rows=None):
+def gemm_ref(a_codes, a_scales, a_factors, b_codes, b_scales, b_factors, rows=None, cols=None):
     """C_ref[m][n] = S_A(m) S_B(n) sum_k dec(A)[m,k] dec(B)[n,k] in float64 and
-    its magnitude sum E (same factors), as (C_ref, E).  `rows` selects rows of A
-    (with their global indices, for the panel factors)."""
-    A = decode(a_codes, a_scales)
-    ia = np.arange(A.shape[0]) if rows is None else np.asarray(rows)
-    if rows is not None:
-        A = A[ia]
-    B = decode(b_codes, b_scales)
+    its magnitude sum E (same factors), as (C_ref, E).  `rows` / `cols` select
+    rows of A / B by their global indices (which pick the panel factors)."""
+    ia = np.arange(np.asarray(a_codes).shape[0]) if rows is None else np.asarray(rows)
+    ib = np.arange(np.asarray(b_codes).shape[0]) if cols is None else np.asarray(cols)
+    A = decode(np.asarray(a_codes)[ia], np.asarray(a_scales)[ia])
+    B = decode(np.asarray(b_codes)[ib], np.asarray(b_scales)[ib])
     sa = np.asarray(a_factors, dtype=np.float64)[ia // PANEL]
-    sb = np.asarray(b_factors, dtype=np.float64)[np.arange(B.shape[0]) // PANEL]
+    sb = np.asarray(b_factors, dtype=np.float64)[ib // PANEL]
     f = sa[:, None] * sb[None, :]
     return f * (A @ B.T), f * (np.abs(A) @ np.abs(B).T)

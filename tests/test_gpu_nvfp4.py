@@ -237,3 +237,63 @@ def test_nv_outputs_fully_written(gpu_lib):
     c = torch.full((320, 96), float("nan"), device="cuda")
     gpu_lib.fp4_nv_gemm(*a, *b, c=c)
     check_nv_gemm(c, a, b, 512)
+
+
+def pick(n, k, rng, step=1):
+    groups = n // step
+    idx = rng.choice(groups, size=min(k, groups), replace=False)
+    return (np.unique(np.concatenate([idx, [0, groups - 1]])) * step).astype(np.int64)
+
+
+def test_nv_dgrad_route_full_size(gpu_lib):
+    """The CTA-local Dgrad of the FFN step at full size (T 8192, D 4096,
+    F 14336), with the calls and shapes `bench.py --nvfp4-dgrad` times:
+    row SR of dY and of a dA-shaped gradient, 2D16 of W2 and W1, dH = dY W2
+    (K 4096) and dX = dA W1 (K 14336).  Whole sampled panels (row producer)
+    and 32-row strips (2D16, with the tensor's factor) bit-exact; sampled
+    outputs of both contractions within the GEMM bound."""
+    h = synthetic.workload("ffn_step_8192x4096x14336")
+    rng = np.random.default_rng(7)
+    seed = 0
+    dY, W2, W1 = h["dY"], h["W2"], h["W1"]
+    T, D = dY.shape
+    F_ = W1.shape[0]
+    dA = synthetic.tensor((T, F_), std=1e-3, seed=48, outlier_rate=0.001, outlier_scale=20.0)
+    # row producer: three whole panels (first, last, one between) per tensor
+    q_dy = gpu_lib.fp4_nv_quantize_rows(dev16(dY), N.SR, seed, 0)
+    q_da = gpu_lib.fp4_nv_quantize_rows(dev16(dA), N.SR, seed, 1)
+    for x, q, off in ((dY, q_dy, 0), (dA, q_da, 1)):
+        panels = x.shape[0] // N.PANEL
+        for p in sorted({0, panels - 1, int(rng.integers(1, panels - 1))}):
+            r0 = p * N.PANEL
+            want = N.quantize_rows(x[r0:r0 + N.PANEL], N.SR, seed, off, row0=r0)
+            assert_same(q[0][r0:r0 + N.PANEL], want[0], f"codes panel {p}")
+            assert_same(q[1][r0:r0 + N.PANEL], want[1], f"scales panel {p}")
+            assert_same(q[2][p:p + 1], want[2], f"factor panel {p}")
+            assert_same(q[3][p:p + 1], want[3], f"panel max {p}")
+    # 2D16 weights: the whole-tensor maximum and factor, then sampled strips
+    q_w2 = gpu_lib.fp4_nv_quantize_w2d16(dev16(W2))
+    q_w1 = gpu_lib.fp4_nv_quantize_w2d16(dev16(W1))
+    for w, q in ((W2, q_w2), (W1, q_w1)):
+        amax = np.float32(np.abs(F.bf16_bits_to_f64(w)).max())
+        assert host(q[5])[0] == amax
+        S = N.outer_factor(amax)
+        assert host(q[4])[0] == S
+        for n0 in pick(w.shape[0], 3, rng, step=32):
+            want = N.quantize_w2d16(w[n0:n0 + 32], factor=S)
+            assert_same(q[0][n0:n0 + 32], want[0], f"row codes strip {n0}")
+            assert_same(q[1][n0:n0 + 32], want[1], f"row scales strip {n0}")
+            assert_same(q[2][:, n0 // 2:n0 // 2 + 16], want[2], f"col codes strip {n0}")
+            assert_same(q[3][:, n0 // 16:n0 // 16 + 2], want[3], f"col scales strip {n0}")
+    # contractions, sampled outputs against the exact reference on the GPU's codes
+    for a, b, k in ((q_dy, q_w2, D), (q_da, q_w1, F_)):
+        c = gpu_lib.fp4_nv_gemm(a[0], a[1], a[2], b[2], b[3], b[4])
+        m, n = c.shape
+        rows, cols = pick(m, 96, rng), pick(n, 1024, rng)
+        fb = panel_factors(host(b[4]), n)
+        ref, e = N.gemm_ref(host(a[0]), host(a[1]), host(a[2]), host(b[2]), host(b[3]), fb, rows=rows, cols=cols)
+        got = host(c)[np.ix_(rows, cols)]
+        ok = G.within_bound(got, ref, e, k=k)
+        assert ok.all(), f"k={k}: {np.count_nonzero(~ok)} sampled outputs outside the bound"
+        del c
+        torch.cuda.empty_cache()

@@ -156,3 +156,24 @@ def test_sr_unbiased_and_bracketed():
     hi = g[np.clip(np.searchsorted(g, y * (1 + 2.0 ** -20), side="left"), 0, 7)]
     q = np.abs(r / unit)
     assert np.all((q >= lo[None, :] - 1e-12) & (q <= hi[None, :] + 1e-12))
+
+
+def test_sampling_hooks_equal_the_whole_computation():
+    """row0, factor and rows/cols only select: slices of whole panels, strips
+    of whole tiles with the tensor's factor and sampled rows/columns give the
+    whole computation's values."""
+    x = synthetic.tensor((768, 64), std=1.0, seed=8)
+    whole = N.quantize_rows(x, N.SR, 3, 5)
+    part = N.quantize_rows(x[256:512], N.SR, 3, 5, row0=256)
+    assert np.array_equal(part[0], whole[0][256:512]) and np.array_equal(part[1], whole[1][256:512])
+    assert part[2][0] == whole[2][1] and part[3][0] == whole[3][1]
+    w = synthetic.tensor((96, 64), std=0.1, seed=9)
+    rc, rs, cc, cs, S, _ = N.quantize_w2d16(w)
+    src, srs, scc, scs, sS, _ = N.quantize_w2d16(w[32:64], factor=S)
+    assert sS == S and np.array_equal(src, rc[32:64]) and np.array_equal(srs, rs[32:64])
+    assert np.array_equal(scc, cc[:, 16:32]) and np.array_equal(scs, cs[:, 2:4])
+    b = N.quantize_rows(synthetic.tensor((320, 64), std=1.0, seed=10))
+    ref, e = N.gemm_ref(whole[0], whole[1], whole[2], b[0], b[1], b[2])
+    rows, cols = np.array([0, 300, 767]), np.array([5, 256, 319])
+    sref, se = N.gemm_ref(whole[0], whole[1], whole[2], b[0], b[1], b[2], rows=rows, cols=cols)
+    assert np.array_equal(sref, ref[np.ix_(rows, cols)]) and np.array_equal(se, e[np.ix_(rows, cols)])
