@@ -363,8 +363,8 @@ fp4_status fp4_nv_quantize_w2d16(const uint16_t* w, int64_t n, int64_t k, int64_
  *   C[m][n] (+)= RN(S_A(m) * S_B(n)) * sum_k (delta_a q_a)(delta_b q_b)
  * with S_A(m) = a_factors[(m / 256) * a_factor_stride] and likewise for B
  * (stride 1: one factor per 256-row panel, as fp4_nv_quantize_rows writes;
- * stride 0: one factor, as fp4_nv_quantize_w2d16 writes).  Each product
- * delta * q is exact in bf16; the sum runs on the bf16 matrix cores in fp32;
+ * stride 0: one factor, as fp4_nv_quantize_w2d16 writes).  Each inner value
+ * delta * q is exact in f16; the sum runs on the f16 matrix cores in fp32;
  * the factor product is applied once per output in the epilogue.
  *   a_codes [m][k/2], a_scales [m][k/16]; b_codes [n][k/2], b_scales [n][k/16]
  *   c       [m][ldc] fp32

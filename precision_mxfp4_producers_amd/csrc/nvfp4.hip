@@ -14,11 +14,11 @@
 // The contraction: CDNA4's block-scaled MFMA takes only E8M0 (power-of-two)
 // scales over 32 values, while an NVFP4 value carries a 16-value E4M3 scale
 // with three fraction bits; delta_b * q has at most six significant bits and
-// lies in [2^-10, 2688], so it is exact in bf16.  The GEMM decodes each K step
-// of codes and scales into bf16 in LDS and runs the bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16) with fp32 accumulation; the epilogue multiplies by
-// RN(S_A * S_B), one product per 256 x 256 output tile (the tile is one panel
-// of each operand).
+// lies in [2^-10, 2688], so it is exact (and normal) in f16.  The GEMM decodes
+// each K step of codes and scales into f16 in LDS and runs the f16 MFMA
+// (v_mfma_f32_32x32x16_f16, the dense 16-bit rate) with fp32 accumulation; the
+// epilogue multiplies by RN(S_A * S_B), one product per 256 x 256 output tile
+// (the tile is one panel of each operand).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -336,10 +336,9 @@ __global__ __launch_bounds__(256) void nv_w2d16_kernel(const uint16_t* __restric
 // ------------------------------------------------------------------ GEMM
 // 256 x 256 output tile, 8 waves of 128 x 64 (as the MXFP4 fast kernel), K in
 // steps of 64 values.  Per step, lane t decodes 32 values of row t/2 of each
-// operand (16 code bytes + 2 E4M3 scale bytes) into bf16 and writes them to
+// operand (16 code bytes + 2 E4M3 scale bytes) into f16 and writes them to
 // the LDS stage (128 bytes per row, 16-byte chunks XOR-swizzled per row).
-// Sub-step s of a step reads chunk 2s + lane/32 (8 bf16 = k 8(lane/32) ..).
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+// Sub-step s of a step reads chunk 2s + lane/32 (8 f16 = k 16s + 8(lane/32) ..).
 constexpr int kNvStage = 2 * 256 * 128;                // A and B rows of one step, bytes
 static_assert(2 * kNvStage <= kSmemBytes, "two stages fit");
 
@@ -359,28 +358,26 @@ __device__ __forceinline__ void nv_load(NvLoad& x, __amdgpu_buffer_rsrc_t rca, _
   x.sb = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsb, so, 0, 0);
 }
 
-// One code word (8 values) times block scale d -> four bf16 words (exact).
+// One code word (8 values) times block scale dd -> four packed f16 words.
 // gfx950's fp4 converters scale by the exponent of their fp32 scale operand
 // only (an E8M0 reading: checked on every code byte and every E4M3 value), so
-// the E4M3 scale's mantissa is applied with a plain fp32 multiply; q * d has
-// at most six significant bits and is finite, so the bf16 conversion is exact
-// and needs no NaN handling.
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t nv_dec2(f32x2_t q, float d) {
-  const bf16x2_t v = {(__bf16)__fmul_rn(q.x, d), (__bf16)__fmul_rn(q.y, d)};
-  return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ void nv_decode8(uint32_t w, float d, uint32_t* o) {
-  o[0] = nv_dec2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0), d);
-  o[1] = nv_dec2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1), d);
-  o[2] = nv_dec2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2), d);
-  o[3] = nv_dec2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3), d);
+// the codes are converted at scale 1 and the E4M3 scale (exact in f16) is
+// applied with one packed f16 multiply per two values.  q * delta has at most
+// six significant bits and lies in [2^-10, 2688]: exact and normal in f16.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ uint32_t nv_dec2(f16x2_t q, f16x2_t dd) { return __builtin_bit_cast(uint32_t, q * dd); }
+__device__ __forceinline__ void nv_decode8(uint32_t w, f16x2_t dd, uint32_t* o) {
+  o[0] = nv_dec2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0), dd);
+  o[1] = nv_dec2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1), dd);
+  o[2] = nv_dec2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2), dd);
+  o[3] = nv_dec2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3), dd);
 }
 
 // Chunk q (values 8q..8q+7 of this lane's 32) of the A and B rows in x,
 // decoded with block scales da, db and written to the stage.
 template <int Q>
-__device__ __forceinline__ void nv_stage_chunk(uint8_t* stage, const NvLoad& x, float da, float db, int row,
+__device__ __forceinline__ void nv_stage_chunk(uint8_t* stage, const NvLoad& x, f16x2_t da, f16x2_t db, int row,
                                                int half) {
   const uint32_t wa = Q == 0 ? x.ca.x : Q == 1 ? x.ca.y : Q == 2 ? x.ca.z : x.ca.w;
   const uint32_t wb = Q == 0 ? x.cb.x : Q == 1 ? x.cb.y : Q == 2 ? x.cb.z : x.cb.w;
@@ -393,11 +390,17 @@ __device__ __forceinline__ void nv_stage_chunk(uint8_t* stage, const NvLoad& x, 
 }
 
 struct NvScales {
-  float a0, a1, b0, b1;                                // E4M3 values of the lane's two A and two B blocks
+  f16x2_t a0, a1, b0, b1;                              // E4M3 values of the lane's two A and two B blocks
 };
 
+__device__ __forceinline__ f16x2_t nv_splat(float d) {
+  const _Float16 h = (_Float16)d;                      // exact: every E4M3 value is an f16 value
+  return f16x2_t{h, h};
+}
+
 __device__ __forceinline__ NvScales nv_scales(const NvLoad& x) {
-  return {e4m3_value(x.sa & 0xFFu), e4m3_value(x.sa >> 8), e4m3_value(x.sb & 0xFFu), e4m3_value(x.sb >> 8)};
+  return {nv_splat(e4m3_value(x.sa & 0xFFu)), nv_splat(e4m3_value(x.sa >> 8)), nv_splat(e4m3_value(x.sb & 0xFFu)),
+          nv_splat(e4m3_value(x.sb >> 8))};
 }
 
 template <int Q>
@@ -406,7 +409,7 @@ __device__ __forceinline__ void nv_stage_q(uint8_t* stage, const NvLoad& x, cons
 }
 
 struct NvFrag {
-  bf16x8_t a[4], b[2];
+  f16x8_t a[4], b[2];
 };
 
 // Fragments of sub-step ss (k 16ss .. 16ss+15) of the stage for this lane.
@@ -417,12 +420,12 @@ __device__ __forceinline__ void nv_frag(NvFrag& f, const uint8_t* stage, int ss,
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ar = wm * 128 + 32 * i + r;
-    f.a[i] = *reinterpret_cast<const bf16x8_t*>(la + ar * 128 + swz(ar, ch) * 16);
+    f.a[i] = *reinterpret_cast<const f16x8_t*>(la + ar * 128 + swz(ar, ch) * 16);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int br = wn * 64 + 32 * j + r;
-    f.b[j] = *reinterpret_cast<const bf16x8_t*>(lb + br * 128 + swz(br, ch) * 16);
+    f.b[j] = *reinterpret_cast<const f16x8_t*>(lb + br * 128 + swz(br, ch) * 16);
   }
 }
 
@@ -430,7 +433,7 @@ __device__ __forceinline__ void nv_mfma(v16f (&acc)[4][2], const NvFrag& f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
 // One K step: the MFMAs of the step held in `cur`, with the decode of the
