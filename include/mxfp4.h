@@ -46,7 +46,7 @@
  *     guarantees; a block beyond that has no upward scale and unspecified
  *     codes.
  *   - Each call validates its arguments on the host, enqueues its kernels on
- *     `stream` (a hipStream_t; NULL = default stream) and returns without
+ *     `stream` (NULL = the default stream) and returns without
  *     synchronising.  Results are valid once the stream has reached them.
  *   - Errors: FP4_EINVAL (null pointer or bad enum), FP4_ESHAPE (negative
  *     dimension, dimension not a multiple of 32, or ld smaller than the row
@@ -61,6 +61,8 @@
 
 #include <stdint.h>
 
+#include <hip/hip_runtime_api.h>   /* hipStream_t */
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -73,8 +75,14 @@ typedef enum {
   FP4_EHIP = 4
 } fp4_status;
 
-/* Rounding of row-facing producers. */
-enum { FP4_RTN = 0, FP4_SR = 1 };
+/* Rounding of row-facing producers.  An int-sized enumeration; any other
+ * value is rejected with FP4_EINVAL (C++ gives it int as its fixed underlying
+ * type so that such a value is representable). */
+#ifdef __cplusplus
+enum fp4_round : int { FP4_RTN = 0, FP4_SR = 1 };
+#else
+typedef enum { FP4_RTN = 0, FP4_SR = 1 } fp4_round;
+#endif
 
 /*
  * Row-facing MXFP4 (Q_r): blocks of 32 consecutive values along `cols`, the
@@ -96,7 +104,7 @@ enum { FP4_RTN = 0, FP4_SR = 1 };
  */
 fp4_status fp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* codes, uint8_t* scales,
-                             int mode, uint64_t seed, uint64_t offset, void* stream);
+                             fp4_round mode, uint64_t seed, uint64_t offset, hipStream_t stream);
 
 /*
  * Column-facing MXFP4 (Q_c) for the Wgrad operands: blocks of 32 consecutive
@@ -116,7 +124,7 @@ fp4_status fp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
  */
 fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* codes_t, uint8_t* scales_t,
-                             int hadamard, uint32_t sign_mask16, void* stream);
+                             int hadamard, uint32_t sign_mask16, hipStream_t stream);
 
 /*
  * Both activation-gradient views from one read (§2.3 Eq. 5-6 with §2.5: the
@@ -134,9 +142,9 @@ fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int6
  */
 fp4_status fp4_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* row_codes, uint8_t* row_scales,
-                             int mode, uint64_t seed, uint64_t offset,
+                             fp4_round mode, uint64_t seed, uint64_t offset,
                              uint8_t* codes_t, uint8_t* scales_t,
-                             int hadamard, uint32_t sign_mask16, void* stream);
+                             int hadamard, uint32_t sign_mask16, hipStream_t stream);
 
 /*
  * 2D32 weight producer (§2.4, Eq. 7-8; adaptive rule of §2.2.1).  One
@@ -158,7 +166,7 @@ fp4_status fp4_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
 fp4_status fp4_quantize_w2d32(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
                               uint8_t* row_codes, uint8_t* row_scales,
                               uint8_t* col_codes, uint8_t* col_scales,
-                              float finer_ratio, void* stream);
+                              float finer_ratio, hipStream_t stream);
 
 /*
  * Block-scaled E2M1 GEMM, NT form (§2.3 Eq. 4-6): with both operands stored
@@ -177,7 +185,7 @@ fp4_status fp4_quantize_w2d32(const uint16_t* w, int64_t n, int64_t k, int64_t l
 fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k,
                     const uint8_t* a_codes, const uint8_t* a_scales,
                     const uint8_t* b_codes, const uint8_t* b_scales,
-                    float* c, int64_t ldc, int accumulate, void* stream);
+                    float* c, int64_t ldc, int accumulate, hipStream_t stream);
 
 /*
  * Two block-scaled products summed in one fp32 accumulation:
@@ -195,7 +203,7 @@ fp4_status fp4_gemm_pair(int64_t m, int64_t n, int64_t k,
                          const uint8_t* b1_codes, const uint8_t* b1_scales,
                          const uint8_t* a2_codes, const uint8_t* a2_scales,
                          const uint8_t* b2_codes, const uint8_t* b2_scales,
-                         float* c, int64_t ldc, int accumulate, void* stream);
+                         float* c, int64_t ldc, int accumulate, hipStream_t stream);
 
 /*
  * Fused gated-FFN producer (§3.2): a = X W1^T and b = X W3^T computed together
@@ -226,7 +234,7 @@ fp4_status fp4_swiglu_producer(int64_t t, int64_t f, int64_t d,
                                uint16_t* a_bf16, uint16_t* b_bf16,
                                uint8_t* h_codes, uint8_t* h_scales,
                                uint8_t* ht_codes, uint8_t* ht_scales,
-                               uint32_t sign_mask16, void* stream);
+                               uint32_t sign_mask16, hipStream_t stream);
 
 /*
  * SwiGLU backward, elementwise (§3.2), from the fp32 W2 Dgrad output dH and
@@ -240,7 +248,7 @@ fp4_status fp4_swiglu_producer(int64_t t, int64_t f, int64_t d,
  */
 fp4_status fp4_swiglu_backward(int64_t t, int64_t f, const float* dh, int64_t lddh,
                                const uint16_t* a_bf16, const uint16_t* b_bf16,
-                               uint16_t* da_bf16, uint16_t* db_bf16, void* stream);
+                               uint16_t* da_bf16, uint16_t* db_bf16, hipStream_t stream);
 
 /*
  * Fused SwiGLU backward producer (§3.1-§3.2: the producer completes every
@@ -269,7 +277,7 @@ fp4_status fp4_swiglu_backward_producer(int64_t t, int64_t f, const float* dh, i
                                         uint8_t* da_codes, uint8_t* da_scales,
                                         uint8_t* db_codes, uint8_t* db_scales,
                                         uint8_t* dat_codes, uint8_t* dat_scales,
-                                        uint8_t* dbt_codes, uint8_t* dbt_scales, void* stream);
+                                        uint8_t* dbt_codes, uint8_t* dbt_scales, hipStream_t stream);
 
 /*
  * W2 data gradient with the fused SwiGLU backward producer in its epilogue
@@ -300,7 +308,7 @@ fp4_status fp4_gemm_swiglu_backward_producer(int64_t t, int64_t f, int64_t d,
                                              uint8_t* da_codes, uint8_t* da_scales,
                                              uint8_t* db_codes, uint8_t* db_scales,
                                              uint8_t* dat_codes, uint8_t* dat_scales,
-                                             uint8_t* dbt_codes, uint8_t* dbt_scales, void* stream);
+                                             uint8_t* dbt_codes, uint8_t* dbt_scales, hipStream_t stream);
 
 /*
  * CTA-local NVFP4 (§2.2 Eq. 1 with §2.2.2 and §2.4): a value is
@@ -336,8 +344,8 @@ fp4_status fp4_gemm_swiglu_backward_producer(int64_t t, int64_t f, int64_t d,
  */
 fp4_status fp4_nv_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                 uint8_t* codes, uint8_t* scales, float* factors,
-                                float* panel_amax, int mode, uint64_t seed, uint64_t offset,
-                                void* stream);
+                                float* panel_amax, fp4_round mode, uint64_t seed, uint64_t offset,
+                                hipStream_t stream);
 
 /*
  * CTA-local 2D16 weight producer (§2.4 with §2.2.2): one E4M3 scale per 16x16
@@ -356,7 +364,7 @@ fp4_status fp4_nv_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
 fp4_status fp4_nv_quantize_w2d16(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
                                  uint8_t* row_codes, uint8_t* row_scales,
                                  uint8_t* col_codes, uint8_t* col_scales,
-                                 float* factor, float* amax_out, void* stream);
+                                 float* factor, float* amax_out, hipStream_t stream);
 
 /*
  * Contraction of two CTA-local NVFP4 operands, NT form:
@@ -379,7 +387,7 @@ fp4_status fp4_nv_gemm(int64_t m, int64_t n, int64_t k,
                        const float* a_factors, int64_t a_factor_stride,
                        const uint8_t* b_codes, const uint8_t* b_scales,
                        const float* b_factors, int64_t b_factor_stride,
-                       float* c, int64_t ldc, int accumulate, void* stream);
+                       float* c, int64_t ldc, int accumulate, hipStream_t stream);
 
 /*
  * Fixed 16-entry sign vector for H32 as a bit mask (bit j set => d_j = -1).

@@ -23,6 +23,6 @@ inline fp4_status launch_status() {
   return FP4_OK;
 }
 
-inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline hipStream_t as_stream(hipStream_t s) { return s; }
 
 }  // namespace mx

@@ -230,7 +230,7 @@ extern "C" fp4_status fp4_gemm_swiglu_backward_producer(
     const uint8_t* w2c_scales, const uint16_t* a_bf16, const uint16_t* b_bf16, uint64_t seed, uint64_t offset_a,
     uint64_t offset_b, uint32_t sign_mask16, uint8_t* da_codes, uint8_t* da_scales, uint8_t* db_codes,
     uint8_t* db_scales, uint8_t* dat_codes, uint8_t* dat_scales, uint8_t* dbt_codes, uint8_t* dbt_scales,
-    void* stream) {
+    hipStream_t stream) {
   if (!mult32z(t) || !mult32z(f) || !mult32z(d)) return FP4_ESHAPE;
   if (t == 0 || f == 0) return FP4_OK;                                  // empty outputs
   if ((d % 256) != 0 || d == 0) return FP4_ESHAPE;                      // the fast main loop's K steps

@@ -466,7 +466,7 @@ extern "C" {
 
 fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                     const uint8_t* b_codes, const uint8_t* b_scales, float* c, int64_t ldc, int accumulate,
-                    void* stream) {
+                    hipStream_t stream) {
   if (accumulate != 0 && accumulate != 1) return FP4_EINVAL;
   if (!mult32z(m) || !mult32z(n) || !mult32z(k) || ldc < n) return FP4_ESHAPE;
   if (m == 0 || n == 0) return FP4_OK;                    // empty C
@@ -499,7 +499,7 @@ fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, con
 fp4_status fp4_gemm_pair(int64_t m, int64_t n, int64_t k, const uint8_t* a1_codes, const uint8_t* a1_scales,
                          const uint8_t* b1_codes, const uint8_t* b1_scales, const uint8_t* a2_codes,
                          const uint8_t* a2_scales, const uint8_t* b2_codes, const uint8_t* b2_scales, float* c,
-                         int64_t ldc, int accumulate, void* stream) {
+                         int64_t ldc, int accumulate, hipStream_t stream) {
   if (accumulate != 0 && accumulate != 1) return FP4_EINVAL;
   if (!mult32z(m) || !mult32z(n) || !mult32z(k) || ldc < n) return FP4_ESHAPE;
   if (m == 0 || n == 0) return FP4_OK;
@@ -528,7 +528,7 @@ fp4_status fp4_gemm_pair(int64_t m, int64_t n, int64_t k, const uint8_t* a1_code
 fp4_status fp4_swiglu_producer(int64_t t, int64_t f, int64_t d, const uint8_t* x_codes, const uint8_t* x_scales,
                                const uint8_t* w13_codes, const uint8_t* w13_scales, uint16_t* a_bf16,
                                uint16_t* b_bf16, uint8_t* h_codes, uint8_t* h_scales, uint8_t* ht_codes,
-                               uint8_t* ht_scales, uint32_t sign_mask16, void* stream) {
+                               uint8_t* ht_scales, uint32_t sign_mask16, hipStream_t stream) {
   if ((ht_codes == nullptr) != (ht_scales == nullptr)) return FP4_EINVAL;
   if (!mult32z(t) || !mult32z(f) || !mult32z(d)) return FP4_ESHAPE;
   if (t == 0 || f == 0) return FP4_OK;                    // empty outputs

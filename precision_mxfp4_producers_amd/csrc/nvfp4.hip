@@ -553,8 +553,8 @@ static int nv_amax_batches(int64_t gx, int64_t rows) {
 }
 
 fp4_status fp4_nv_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
-                                uint8_t* scales, float* factors, float* panel_amax, int mode, uint64_t seed,
-                                uint64_t offset, void* stream) {
+                                uint8_t* scales, float* factors, float* panel_amax, fp4_round mode, uint64_t seed,
+                                uint64_t offset, hipStream_t stream) {
   if (mode != FP4_RTN && mode != FP4_SR) return FP4_EINVAL;
   if (rows < 0 || !mult32z(cols) || ldx < cols) return FP4_ESHAPE;
   if (rows == 0 || cols == 0) return FP4_OK;
@@ -583,7 +583,7 @@ fp4_status fp4_nv_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
 
 fp4_status fp4_nv_quantize_w2d16(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, uint8_t* row_codes,
                                  uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, float* factor,
-                                 float* amax_out, void* stream) {
+                                 float* amax_out, hipStream_t stream) {
   if (!mult32z(n) || !mult32z(k) || ldw < k) return FP4_ESHAPE;
   if (n == 0 || k == 0) return FP4_OK;
   if (!w || !row_codes || !row_scales || !col_codes || !col_scales || !factor || !amax_out) return FP4_EINVAL;
@@ -609,7 +609,7 @@ fp4_status fp4_nv_quantize_w2d16(const uint16_t* w, int64_t n, int64_t k, int64_
 fp4_status fp4_nv_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                        const float* a_factors, int64_t a_factor_stride, const uint8_t* b_codes,
                        const uint8_t* b_scales, const float* b_factors, int64_t b_factor_stride, float* c,
-                       int64_t ldc, int accumulate, void* stream) {
+                       int64_t ldc, int accumulate, hipStream_t stream) {
   if (accumulate != 0 && accumulate != 1) return FP4_EINVAL;
   if (a_factor_stride < 0 || b_factor_stride < 0) return FP4_EINVAL;
   if (!mult32z(m) || !mult32z(n) || k < 0 || (k % 64) != 0 || ldc < n || k >= ((int64_t)1 << 24)) return FP4_ESHAPE;

@@ -459,8 +459,8 @@ using namespace mx;
 extern "C" {
 
 fp4_status fp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
-                             uint8_t* codes, uint8_t* scales, int mode, uint64_t seed,
-                             uint64_t offset, void* stream) {
+                             uint8_t* codes, uint8_t* scales, fp4_round mode, uint64_t seed,
+                             uint64_t offset, hipStream_t stream) {
   if (mode != FP4_RTN && mode != FP4_SR) return FP4_EINVAL;
   if (rows < 0 || !mult32z(cols) || ldx < cols) return FP4_ESHAPE;
   if (rows == 0 || cols == 0) return FP4_OK;             // empty: nothing to write
@@ -486,7 +486,7 @@ fp4_status fp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
 
 fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* codes_t, uint8_t* scales_t, int hadamard,
-                             uint32_t sign_mask16, void* stream) {
+                             uint32_t sign_mask16, hipStream_t stream) {
   if (hadamard != 0 && hadamard != 32) return FP4_EINVAL;
   if (!mult32z(rows) || !mult32z(cols) || ldx < cols) return FP4_ESHAPE;
   if (rows == 0 || cols == 0) return FP4_OK;
@@ -506,9 +506,9 @@ fp4_status fp4_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, int6
 }
 
 fp4_status fp4_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
-                             uint8_t* row_codes, uint8_t* row_scales, int mode, uint64_t seed, uint64_t offset,
+                             uint8_t* row_codes, uint8_t* row_scales, fp4_round mode, uint64_t seed, uint64_t offset,
                              uint8_t* codes_t, uint8_t* scales_t, int hadamard, uint32_t sign_mask16,
-                             void* stream) {
+                             hipStream_t stream) {
   if (mode != FP4_RTN && mode != FP4_SR) return FP4_EINVAL;
   if (hadamard != 0 && hadamard != 32) return FP4_EINVAL;
   if (!mult32z(rows) || !mult32z(cols) || ldx < cols) return FP4_ESHAPE;
@@ -537,7 +537,7 @@ fp4_status fp4_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
 
 fp4_status fp4_quantize_w2d32(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
                               uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
-                              uint8_t* col_scales, float finer_ratio, void* stream) {
+                              uint8_t* col_scales, float finer_ratio, hipStream_t stream) {
   if (!(finer_ratio >= 0.0f && finer_ratio <= 1.0f)) return FP4_EINVAL;
   if (!mult32z(n) || !mult32z(k) || ldw < k) return FP4_ESHAPE;
   if (n == 0 || k == 0) return FP4_OK;

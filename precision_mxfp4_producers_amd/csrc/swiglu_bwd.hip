@@ -268,7 +268,7 @@ using namespace mx;
 
 extern "C" fp4_status fp4_swiglu_backward(int64_t t, int64_t f, const float* dh, int64_t lddh,
                                           const uint16_t* a_bf16, const uint16_t* b_bf16, uint16_t* da_bf16,
-                                          uint16_t* db_bf16, void* stream) {
+                                          uint16_t* db_bf16, hipStream_t stream) {
   if (!mult32z(t) || !mult32z(f) || lddh < f) return FP4_ESHAPE;
   if (t == 0 || f == 0) return FP4_OK;
   if (!dh || !a_bf16 || !b_bf16 || !da_bf16 || !db_bf16) return FP4_EINVAL;
@@ -288,7 +288,7 @@ extern "C" fp4_status fp4_swiglu_backward_producer(
     int64_t t, int64_t f, const float* dh, int64_t lddh, const uint16_t* a_bf16, const uint16_t* b_bf16,
     uint64_t seed, uint64_t offset_a, uint64_t offset_b, uint32_t sign_mask16,
     uint8_t* da_codes, uint8_t* da_scales, uint8_t* db_codes, uint8_t* db_scales,
-    uint8_t* dat_codes, uint8_t* dat_scales, uint8_t* dbt_codes, uint8_t* dbt_scales, void* stream) {
+    uint8_t* dat_codes, uint8_t* dat_scales, uint8_t* dbt_codes, uint8_t* dbt_scales, hipStream_t stream) {
   if (!mult32z(t) || !mult32z(f) || lddh < f) return FP4_ESHAPE;
   if (t == 0 || f == 0) return FP4_OK;
   if (!dh || !a_bf16 || !b_bf16 || !da_codes || !da_scales || !db_codes || !db_scales || !dat_codes ||

@@ -27,22 +27,22 @@ int main() {
   float* c = static_cast<float*>(p);
   const int64_t big = (int64_t)1 << 40, huge_rows = (int64_t)65536 * 128;
 
-  expect("rows null", fp4_quantize_rows(nullptr, 32, 32, 32, nullptr, nullptr, 0, 0, 0, nullptr), FP4_EINVAL);
-  expect("rows shape", fp4_quantize_rows(x, 32, 33, 40, b, b, 0, 0, 0, nullptr), FP4_ESHAPE);
-  expect("rows align", fp4_quantize_rows(static_cast<uint16_t*>(odd), 32, 32, 32, b, b, 0, 0, 0, nullptr), FP4_EALIGN);
-  expect("rows mode", fp4_quantize_rows(x, 32, 32, 32, b, b, 7, 0, 0, nullptr), FP4_EINVAL);
-  expect("rows negative", fp4_quantize_rows(nullptr, -1, 64, 64, nullptr, nullptr, 0, 0, 0, nullptr), FP4_ESHAPE);
-  expect("rows empty", fp4_quantize_rows(nullptr, 0, 64, 64, nullptr, nullptr, 1, 0, 0, nullptr), FP4_OK);
-  expect("rows huge cols", fp4_quantize_rows(x, 32, big * 32, big * 32, b, b, 0, 0, 0, nullptr), FP4_ESHAPE);
+  expect("rows null", fp4_quantize_rows(nullptr, 32, 32, 32, nullptr, nullptr, static_cast<fp4_round>(0), 0, 0, nullptr), FP4_EINVAL);
+  expect("rows shape", fp4_quantize_rows(x, 32, 33, 40, b, b, static_cast<fp4_round>(0), 0, 0, nullptr), FP4_ESHAPE);
+  expect("rows align", fp4_quantize_rows(static_cast<uint16_t*>(odd), 32, 32, 32, b, b, static_cast<fp4_round>(0), 0, 0, nullptr), FP4_EALIGN);
+  expect("rows mode", fp4_quantize_rows(x, 32, 32, 32, b, b, static_cast<fp4_round>(7), 0, 0, nullptr), FP4_EINVAL);
+  expect("rows negative", fp4_quantize_rows(nullptr, -1, 64, 64, nullptr, nullptr, static_cast<fp4_round>(0), 0, 0, nullptr), FP4_ESHAPE);
+  expect("rows empty", fp4_quantize_rows(nullptr, 0, 64, 64, nullptr, nullptr, static_cast<fp4_round>(1), 0, 0, nullptr), FP4_OK);
+  expect("rows huge cols", fp4_quantize_rows(x, 32, big * 32, big * 32, b, b, static_cast<fp4_round>(0), 0, 0, nullptr), FP4_ESHAPE);
   expect("cols shape", fp4_quantize_cols(x, 48, 32, 32, b, b, 0, 0, nullptr), FP4_ESHAPE);
   expect("cols hadamard", fp4_quantize_cols(x, 32, 32, 32, b, b, 16, 0, nullptr), FP4_EINVAL);
   expect("cols limit", fp4_quantize_cols(x, huge_rows, 32, 32, b, b, 32, 0, nullptr), FP4_ESHAPE);
   expect("cols huge cols", fp4_quantize_cols(x, 32, big * 512, big * 512, b, b, 32, 0, nullptr), FP4_ESHAPE);
   expect("cols empty", fp4_quantize_cols(nullptr, 64, 0, 0, nullptr, nullptr, 0, 0, nullptr), FP4_OK);
-  expect("dual shape", fp4_quantize_dual(x, 48, 32, 32, b, b, 1, 0, 0, b, b, 32, 0, nullptr), FP4_ESHAPE);
-  expect("dual mode", fp4_quantize_dual(x, 32, 32, 32, b, b, 3, 0, 0, b, b, 32, 0, nullptr), FP4_EINVAL);
-  expect("dual null", fp4_quantize_dual(x, 32, 32, 32, b, b, 1, 0, 0, nullptr, b, 32, 0, nullptr), FP4_EINVAL);
-  expect("dual limit", fp4_quantize_dual(x, huge_rows, 32, 32, b, b, 1, 0, 0, b, b, 32, 0, nullptr), FP4_ESHAPE);
+  expect("dual shape", fp4_quantize_dual(x, 48, 32, 32, b, b, static_cast<fp4_round>(1), 0, 0, b, b, 32, 0, nullptr), FP4_ESHAPE);
+  expect("dual mode", fp4_quantize_dual(x, 32, 32, 32, b, b, static_cast<fp4_round>(3), 0, 0, b, b, 32, 0, nullptr), FP4_EINVAL);
+  expect("dual null", fp4_quantize_dual(x, 32, 32, 32, b, b, static_cast<fp4_round>(1), 0, 0, nullptr, b, 32, 0, nullptr), FP4_EINVAL);
+  expect("dual limit", fp4_quantize_dual(x, huge_rows, 32, 32, b, b, static_cast<fp4_round>(1), 0, 0, b, b, 32, 0, nullptr), FP4_ESHAPE);
   expect("w2d32 ld", fp4_quantize_w2d32(x, 32, 32, 16, b, b, b, b, 0.87f, nullptr), FP4_ESHAPE);
   expect("w2d32 ratio", fp4_quantize_w2d32(x, 32, 32, 32, b, b, b, b, 1.5f, nullptr), FP4_EINVAL);
   expect("w2d32 pitch", fp4_quantize_w2d32(x, 32, 32, (int64_t)1 << 22, b, b, b, b, 0.87f, nullptr), FP4_ESHAPE);
@@ -87,15 +87,15 @@ int main() {
                                                              nullptr, 0, 0, 1, 0, nullptr, nullptr, nullptr, nullptr,
                                                              nullptr, nullptr, nullptr, nullptr, nullptr), FP4_OK);
   const int64_t i64max = INT64_MAX;
-  expect("nv rows mode", fp4_nv_quantize_rows(x, 32, 32, 32, b, b, c, c, 2, 0, 0, nullptr), FP4_EINVAL);
-  expect("nv rows shape", fp4_nv_quantize_rows(x, 32, 48, 48, b, b, c, c, 0, 0, 0, nullptr), FP4_ESHAPE);
-  expect("nv rows null", fp4_nv_quantize_rows(x, 32, 32, 32, b, b, c, nullptr, 0, 0, 0, nullptr), FP4_EINVAL);
-  expect("nv rows limit", fp4_nv_quantize_rows(x, 65536 * 32, 32, 32, b, b, c, c, 1, 0, 0, nullptr), FP4_ESHAPE);
-  expect("nv rows max", fp4_nv_quantize_rows(x, i64max, 32, 32, b, b, c, c, 1, 0, 0, nullptr), FP4_ESHAPE);
-  expect("nv rows huge cols", fp4_nv_quantize_rows(x, 32, big * 32, big * 32, b, b, c, c, 0, 0, 0, nullptr),
+  expect("nv rows mode", fp4_nv_quantize_rows(x, 32, 32, 32, b, b, c, c, static_cast<fp4_round>(2), 0, 0, nullptr), FP4_EINVAL);
+  expect("nv rows shape", fp4_nv_quantize_rows(x, 32, 48, 48, b, b, c, c, static_cast<fp4_round>(0), 0, 0, nullptr), FP4_ESHAPE);
+  expect("nv rows null", fp4_nv_quantize_rows(x, 32, 32, 32, b, b, c, nullptr, static_cast<fp4_round>(0), 0, 0, nullptr), FP4_EINVAL);
+  expect("nv rows limit", fp4_nv_quantize_rows(x, 65536 * 32, 32, 32, b, b, c, c, static_cast<fp4_round>(1), 0, 0, nullptr), FP4_ESHAPE);
+  expect("nv rows max", fp4_nv_quantize_rows(x, i64max, 32, 32, b, b, c, c, static_cast<fp4_round>(1), 0, 0, nullptr), FP4_ESHAPE);
+  expect("nv rows huge cols", fp4_nv_quantize_rows(x, 32, big * 32, big * 32, b, b, c, c, static_cast<fp4_round>(0), 0, 0, nullptr),
          FP4_ESHAPE);
-  expect("nv rows align", fp4_nv_quantize_rows(x, 32, 32, 36, b, b, c, c, 0, 0, 0, nullptr), FP4_EALIGN);
-  expect("nv rows empty", fp4_nv_quantize_rows(nullptr, 0, 64, 64, nullptr, nullptr, nullptr, nullptr, 1, 0, 0,
+  expect("nv rows align", fp4_nv_quantize_rows(x, 32, 32, 36, b, b, c, c, static_cast<fp4_round>(0), 0, 0, nullptr), FP4_EALIGN);
+  expect("nv rows empty", fp4_nv_quantize_rows(nullptr, 0, 64, 64, nullptr, nullptr, nullptr, nullptr, static_cast<fp4_round>(1), 0, 0,
                                                nullptr), FP4_OK);
   expect("nv w2d16 shape", fp4_nv_quantize_w2d16(x, 48, 32, 32, b, b, b, b, c, c, nullptr), FP4_ESHAPE);
   expect("nv w2d16 null", fp4_nv_quantize_w2d16(x, 32, 32, 32, b, b, b, nullptr, c, c, nullptr), FP4_EINVAL);

@@ -189,3 +189,38 @@ def test_empty_calls_are_noops_without_gpu_work():
     assert lib.fp4_quantize_rows(None, -1, 64, 64, None, None, 0, 0, 0, None) == 2
     assert lib.fp4_quantize_rows(None, 0, 64, 64, None, None, 5, 0, 0, None) == 1
     assert lib.fp4_gemm(-32, 64, 64, None, None, None, None, None, 64, 0, None) == 2
+
+
+def test_header_compiles_and_links_as_plain_c(tmp_path):
+    """include/mxfp4.h is a C header: a C11 program built with gcc against it
+    links to the library and gets the documented host-check answers."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "c_abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "mxfp4.h"
+int main(void) {
+  int fails = 0;
+  if (fp4_abi_version() >> 16 != 1) ++fails;
+  if (fp4_sign_mask_from_seed(7) > 0xFFFFu) ++fails;
+  /* a bad rounding mode and an empty call, answered on the host */
+  if (fp4_quantize_rows((const uint16_t*)4096, 32, 32, 32, (uint8_t*)4096, (uint8_t*)4096, (fp4_round)5, 0, 0, NULL)
+      != FP4_EINVAL) ++fails;
+  if (fp4_nv_gemm(0, 64, 64, NULL, NULL, NULL, 1, NULL, NULL, NULL, 0, NULL, 64, 0, NULL) != FP4_OK) ++fails;
+  printf("c_abi: %d failure(s)\n", fails);
+  return fails;
+}
+''')
+    exe = tmp_path / "c_abi"
+    libdir = os.path.dirname(LIB)
+    cmd = [gcc, "-std=c11", "-Wall", "-Werror=implicit-function-declaration", "-I", os.path.join(ROOT, "include"),
+           "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", str(src), "-L", libdir, "-lmxfp4",
+           "-Wl,-rpath," + libdir, "-o", str(exe)]
+    b = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, timeout=120)
+    assert b.returncode == 0, b.stdout.decode()[-3000:]
+    r = subprocess.run([str(exe)], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, timeout=60)
+    assert r.returncode == 0 and b"0 failure(s)" in r.stdout, r.stdout.decode()[-2000:]
