@@ -297,3 +297,29 @@ def test_nv_dgrad_route_full_size(gpu_lib):
         assert ok.all(), f"k={k}: {np.count_nonzero(~ok)} sampled outputs outside the bound"
         del c
         torch.cuda.empty_cache()
+
+
+def test_nv_long_k_and_tall_tensor(gpu_lib):
+    """Size extremes: a contraction over K = 65536 (1024 steps; the bound
+    holds over the long fp32 sum) and a row producer over 131072 x 32 (the
+    grid's rows loop and the largest maxima batches), checked on panels."""
+    k = 65536
+    a_bits = synthetic.tensor((32, k), std=1.0, seed=49, outlier_rate=0.001, outlier_scale=30.0)
+    b_bits = synthetic.tensor((96, k), std=0.02, seed=50)
+    a = gpu_lib.fp4_nv_quantize_rows(dev16(a_bits), N.SR, 2, 3)[:3]
+    b = gpu_lib.fp4_nv_quantize_rows(dev16(b_bits))[:3]
+    want_a = N.quantize_rows(a_bits, N.SR, 2, 3)
+    assert_same(a[0], want_a[0], "long-k codes")
+    assert_same(a[1], want_a[1], "long-k scales")
+    c = gpu_lib.fp4_nv_gemm(*a, *b)
+    check_nv_gemm(c, a, b, k, what="nv gemm k 65536")
+    rows = 131072
+    x = synthetic.tensor((rows, 32), std=1.0, seed=51)
+    x[rows // 2: rows // 2 + 256] = 0                              # one all-zero panel in the middle
+    q = gpu_lib.fp4_nv_quantize_rows(dev16(x), N.SR, 4, 5)
+    for p in (0, 255, 256, 511):
+        r0 = p * N.PANEL
+        want = N.quantize_rows(x[r0:r0 + N.PANEL], N.SR, 4, 5, row0=r0)
+        for g, w, nm in zip(q, want, ("codes", "scales", "factor", "max")):
+            got = g[r0:r0 + N.PANEL] if nm in ("codes", "scales") else g[p:p + 1]
+            assert_same(got, w, f"tall tensor {nm} panel {p}")
