@@ -34,7 +34,12 @@ def build_step(mx, t=256, d=512, f=384, seed=3):
          "dx2": torch.empty((t, d), dtype=torch.float32, device="cuda"),
          "dyd": [u8(t, d // 2), u8(t, d // 32), u8(d, t // 2), u8(d, t // 32)],
          "dw1": torch.empty((f, d), dtype=torch.float32, device="cuda"),
-         "dw3": torch.empty((f, d), dtype=torch.float32, device="cuda")}
+         "dw3": torch.empty((f, d), dtype=torch.float32, device="cuda"),
+         # the CTA-local NVFP4 Dgrad: fill kernels (not memsets) clear its maxima
+         "nvdy": [u8(t, d // 2), u8(t, d // 16), torch.empty(1, device="cuda"), torch.empty(1, device="cuda")],
+         "nvw2": [u8(d, f // 2), u8(d, f // 16), u8(f, d // 2), u8(f, d // 16), torch.empty(1, device="cuda"),
+                  torch.empty(1, device="cuda")],
+         "nvdh": torch.empty((t, f), dtype=torch.float32, device="cuda")}
 
     def run():
         mx.fp4_quantize_rows(dv["X"], codes=o["xr"][0], scales=o["xr"][1])
@@ -57,6 +62,10 @@ def build_step(mx, t=256, d=512, f=384, seed=3):
         mx.fp4_quantize_dual(dv["dY"], mx.FP4_SR, seed, 0, 32, mask, *o["dyd"])
         mx.fp4_gemm(o["bwd"][4], o["bwd"][5], o["xc"][0], o["xc"][1], c=o["dw1"])
         mx.fp4_gemm(o["bwd"][6], o["bwd"][7], o["xc"][0], o["xc"][1], c=o["dw3"])
+        mx.fp4_nv_quantize_rows(dv["dY"], mx.FP4_SR, seed, 0, out=o["nvdy"])
+        mx.fp4_nv_quantize_w2d16(dv["W2"], out=o["nvw2"])
+        mx.fp4_nv_gemm(o["nvdy"][0], o["nvdy"][1], o["nvdy"][2], o["nvw2"][2], o["nvw2"][3], o["nvw2"][4],
+                       c=o["nvdh"])
 
     def snapshot():
         torch.cuda.synchronize()
