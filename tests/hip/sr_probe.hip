@@ -46,3 +46,21 @@ extern "C" int sr_probe(const uint32_t* w, const int32_t* e, const uint32_t* u, 
                      out, exact, n);
   return (int)hipGetLastError();
 }
+
+// The adjacent-bin rule alone on caller-chosen fp32 magnitudes y in [0, 6]
+// (any fp32, as the CTA-local NVFP4 producers form them) and draws u:
+// code[i] = mx::e2m1_sr(y[i], u[i], 0).
+__global__ __launch_bounds__(256) void sr_y_probe_kernel(const float* __restrict__ y, const uint32_t* __restrict__ u,
+                                                         uint32_t* __restrict__ code, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) code[i] = mx::e2m1_sr(y[i], u[i], 0u);
+}
+
+extern "C" int sr_y_probe(const float* y, const uint32_t* u, uint32_t* code, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  if (!y || !u || !code || n > ((int64_t)1 << 30)) return -1;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(sr_y_probe_kernel, dim3(blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), y, u, code,
+                     n);
+  return (int)hipGetLastError();
+}

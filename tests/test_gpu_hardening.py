@@ -410,3 +410,47 @@ def test_swiglu_bindings_refuse_bad_operands(gpu_lib):
         with pytest.raises(gpu_lib.Fp4Error):
             gpu_lib.fp4_swiglu_backward(dh, aa, bb)
     torch.cuda.synchronize()
+
+
+def test_sr_rule_on_fp32_magnitudes_at_the_threshold(gpu_lib):
+    """The adjacent-bin rule as the CTA-local NVFP4 producers apply it, on fp32
+    magnitudes with full 24-bit significands (y = RN(|x| r) is any fp32 in
+    [0, 6]): random values over [2^-40, 6], every grid point and its fp32
+    neighbours, and subnormals; each at the draws T - 1 and T around its
+    threshold T = ceil(frac 2^32) (exact in float64: every spacing is a power
+    of two), compared with the oracle's rule."""
+    lib = _probe()
+    lib.sr_y_probe.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_void_p]
+    lib.sr_y_probe.restype = ctypes.c_int
+    rng = np.random.default_rng(102)
+    grid = F.E2M1_GRID.astype(np.float32)
+    ys = [rng.uniform(0, 6, 40000).astype(np.float32),
+          np.exp2(rng.uniform(-40, np.log2(6), 40000)).astype(np.float32),
+          grid, np.nextafter(grid, np.float32(7)), np.nextafter(grid, np.float32(-1)),
+          np.float32([1e-45, 3e-42, 1.17e-38, 2.0 ** -33, 2.0 ** -32, 3 * 2.0 ** -34])]
+    y = np.concatenate(ys)
+    y = y[(y >= 0) & (y <= 6)].astype(np.float32)
+    y64 = y.astype(np.float64)
+    lo = np.clip(np.searchsorted(F.E2M1_GRID, y64, side="right") - 1, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    step = np.where(hi > lo, F.E2M1_GRID[hi] - F.E2M1_GRID[lo], 1.0)
+    T = np.ceil((y64 - F.E2M1_GRID[lo]) / step * 2.0 ** 32)           # exact: power-of-two step
+    cases_y, cases_u = [], []
+    for du in (-1, 0):
+        u = T + du
+        ok = (u >= 0) & (u <= 2.0 ** 32 - 1)
+        cases_y.append(y[ok])
+        cases_u.append(u[ok].astype(np.uint64).astype(np.uint32))
+    cases_y.append(y)                                               # and the extreme draws
+    cases_u.append(np.zeros(len(y), dtype=np.uint32))
+    cases_y.append(y)
+    cases_u.append(np.full(len(y), 0xFFFFFFFF, dtype=np.uint32))
+    yy, uu = np.concatenate(cases_y), np.concatenate(cases_u)
+    n = len(yy)
+    yd = torch.from_numpy(yy).cuda()
+    ud = torch.from_numpy(uu.view(np.int32)).cuda()
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    assert lib.sr_y_probe(yd.data_ptr(), ud.data_ptr(), out.data_ptr(), n, torch.cuda.current_stream().cuda_stream) == 0
+    got = host(out).view(np.uint32)
+    want = F.sr_code(yy.astype(np.float64), uu).astype(np.uint32)
+    assert_same(got, want, "SR codes on fp32 magnitudes")
