@@ -39,6 +39,13 @@ Readings where the pages leave a step open (each listed in the design doc):
   * Contraction: C[m][n] = RN32(RN32(S_A(m) S_B(n)) * acc), acc the fp32 sum of
     the exact products (delta_a q_a)(delta_b q_b); checked against the fp64
     value S_A S_B sum(...) within the GEMM bound of formats/gemm.
+
+Parity unpinned: the readings above as readings (the owning panel, the outer
+factor's formula and the order of roundings) -- the pages print no NVFP4
+worked example.  The tests pin the arithmetic as read: the E4M3 grid and its
+rounding against the OCP definition and torch's float8_e4m3fn conversion, the
+factor's closed form, vanishing blocks, the reconstruction bound, the 2D16
+orientation invariant, exact rational contractions and SR's unbiasedness.
 """
 
 import numpy as np

@@ -20,6 +20,11 @@ Layouts (readings):
 Finer-scale reading: with e_up the upward exponent of the tile maximum a_T,
 r = (a_T / 6) / 2^e_up lies in (0.5, 1]; the tile takes e_up - 1 iff
 r < finer_ratio (exact comparison) and e_up > -127.  finer_ratio = 0 disables.
+
+Parity unpinned: the normalisation in which the pages' 0.87 is compared (the
+reading above) -- the pages give the constant but no worked example, so the
+tests pin the rule's arithmetic as read (boundary cases, ratio 0 reducing to
+the upward scale), not its meaning.  Everything else here is pinned.
 """
 
 import numpy as np
