@@ -560,7 +560,7 @@ def quality_report(mx, torch):
         torch.cuda.empty_cache()
     return out
 
-PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 / f16 MFMA, published
 B_NV_ROWS = 2 + 0.5 + 1 / 16     # bf16 in, codes and E4M3 scales out
 B_NV_W2D16 = 2 + 2 * (0.5 + 1 / 16)
 
@@ -570,8 +570,8 @@ def nvfp4_dgrad(mx, torch, name, reps=7):
     (eager, HIP events, median of `reps` after two untimed passes): row SR of
     dY and 2D16 of W2, dH = dY W2, the SwiGLU backward to bf16 dA and dB, their
     row SR, 2D16 of W1 and W3, dX = dA W1 + dB W3 (second product accumulating).
-    a, b come from the MXFP4 forward producer.  GEMMs against the dense bf16
-    MFMA peak (the contraction runs on the bf16 matrix cores), producers
+    a, b come from the MXFP4 forward producer.  GEMMs against the dense 16-bit
+    MFMA peak (the contraction runs on the f16 matrix cores), producers
     against HBM."""
     import synthetic
     h = synthetic.workload(name)
@@ -627,7 +627,7 @@ def nvfp4_dgrad(mx, torch, name, reps=7):
         e = {"call": label, "us": round(ms * 1e3, 1)}
         if kind == "gemm":
             e["tflops"] = round(units / ms / 1e9, 1)
-            e["frac_bf16_mfma_peak"] = round(units / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
+            e["frac_16bit_mfma_peak"] = round(units / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
         else:
             e["gbps"] = round(units / ms / 1e6, 1)
             e["frac_hbm_peak"] = round(units / ms / 1e6 / PEAK_HBM_GBPS, 4)
