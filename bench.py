@@ -637,6 +637,52 @@ def nvfp4_dgrad(mx, torch, name, reps=7):
             "dgrad_tflop": round(flops / 1e12, 4), "quantize_gemm_tflops": round(flops / (total * 1e-3) / 1e12, 1)}
 
 
+def cpu_baseline_nv(name, seed=None):
+    """Time the CPU oracle's CTA-local NVFP4 Dgrad route (the calls of
+    nvfp4_dgrad) on a reduced instance of the FFN workload (T 256, F 6144,
+    same laws); a, b come from the oracle's MXFP4 forward outside the timed
+    region.  Reported as contraction FLOPs per second."""
+    import threadpoolctl
+    import synthetic
+    from oracle import gemm as G
+    from oracle import nvfp4 as NV
+    from oracle import quant as Q
+    from oracle import swiglu as S
+    red = CPU_SAMPLE_SHAPES["ffn"]
+    T, F = red["T"], red["F"]
+    spec = synthetic.WORKLOADS[name]["tensors"]
+    D = spec["X"][1]
+    shapes = {"X": (T, D), "dY": (T, D), "W1": (F, D), "W3": (F, D), "W2": (D, F)}
+    seed = synthetic.WORKLOADS[name]["seed"] if seed is None else seed
+    h = synthetic.workload(name, seed=seed, shapes=shapes)
+    xr = Q.quantize_rows(h["X"])
+    w1, w3 = Q.quantize_w2d32(h["W1"]), Q.quantize_w2d32(h["W3"])
+    ab = G.gemm_ref(xr[0], xr[1], np.concatenate([w1[0], w3[0]]), np.concatenate([w1[1], w3[1]]))[0]
+    a = S.f32_to_bf16_rne(ab[:, :F].astype(np.float32))
+    b = S.f32_to_bf16_rne(ab[:, F:].astype(np.float32))
+
+    def one(w):                                          # a weight's 2D16 column view with its factor
+        q = NV.quantize_w2d16(w)
+        return q[2], q[3], np.repeat(np.float32(q[4]), (q[2].shape[0] + NV.PANEL - 1) // NV.PANEL)
+
+    t0 = time.perf_counter()
+    dyq = NV.quantize_rows(h["dY"], NV.SR, seed, 0)
+    w2c = one(h["W2"])
+    dh = NV.gemm_ref(dyq[0], dyq[1], dyq[2], *w2c)[0]
+    da, db = S.swiglu_backward(dh.astype(np.float32), a, b)
+    daq, dbq = NV.quantize_rows(da, NV.SR, seed, 1), NV.quantize_rows(db, NV.SR, seed, 2)
+    w1c, w3c = one(h["W1"]), one(h["W3"])
+    dx = NV.gemm_ref(daq[0], daq[1], daq[2], *w1c)[0] + NV.gemm_ref(dbq[0], dbq[1], dbq[2], *w3c)[0]
+    dt = time.perf_counter() - t0
+    del dx
+    flops = 3 * 2.0 * T * F * D
+    info = threadpoolctl.threadpool_info()
+    blas_threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"the NVFP4 Dgrad route on a reduced FFN instance (T {T}, D {D}, F {F}), "
+                      f"{flops / 1e9:.2f} GFLOP in {dt:.1f} s", "host_cpus": os.cpu_count()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -659,7 +705,11 @@ def main():
         print(json.dumps({"quantizer_sweep": quantizer_sweep(mx, torch)}), flush=True)
         return
     if args.nvfp4_dgrad:
-        print(json.dumps({"nvfp4_dgrad": nvfp4_dgrad(mx, torch, args.workload)}), flush=True)
+        res = nvfp4_dgrad(mx, torch, args.workload)
+        if not args.no_cpu_baseline:
+            print("[bench] timing the CPU oracle's NVFP4 route on a sample", file=sys.stderr, flush=True)
+            res["cpu_baseline"] = cpu_baseline_nv(args.workload)
+        print(json.dumps({"nvfp4_dgrad": res}), flush=True)
         return
     print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
     step = Step(args.workload, args.seed, mx, torch, fused_backward=not args.unfused_backward,
