@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--quantizer-sweep", action="store_true",
                    help="each producer alone at the FFN step's shapes after a read-only cache flush, beside a plain "
                         "streaming kernel with the same bytes read and written per element")
+    p.add_argument("--hybrid-dgrad", action="store_true",
+                   help="FFN step as the operand-wise hybrid: MXFP4 forward and Wgrads, CTA-local NVFP4 Dgrads")
     p.add_argument("--nvfp4-dgrad", action="store_true",
                    help="the CTA-local NVFP4 Dgrad of the FFN workload (producers, bf16-MFMA contraction) call by "
                         "call")
@@ -186,9 +188,10 @@ def quantizer_sweep(mx, torch, reps=9):
 class Step:
     """Holds device inputs/outputs and enqueues one step as a list of named calls."""
 
-    def __init__(self, name, seed, mx, torch, fused_backward=True, dgrad_epilogue=False):
+    def __init__(self, name, seed, mx, torch, fused_backward=True, dgrad_epilogue=False, nvfp4_dgrad=False):
         self.fused_backward = fused_backward
         self.dgrad_epilogue = dgrad_epilogue and fused_backward
+        self.nvfp4_dgrad = nvfp4_dgrad
         import synthetic
         self.mx, self.torch = mx, torch
         self.name = name
@@ -200,7 +203,8 @@ class Step:
         self.o = {}
         self.calls = []          # (label, kind, units, fn, algorithmic bytes of a GEMM)
         self.charge = {}         # contraction label -> producer calls charged to it (each charged once)
-        getattr(self, "_build_" + name.split("_")[0])()
+        kind = name.split("_")[0]
+        getattr(self, "_build_ffn_hybrid" if (kind == "ffn" and nvfp4_dgrad) else "_build_" + kind)()
         charged = sorted(q for v in self.charge.values() for q in v)
         producers = sorted(c[0] for c in self.calls if c[1] == "quant")
         assert charged == producers, f"every producer call is charged to exactly one contraction: {charged} {producers}"
@@ -263,6 +267,31 @@ class Step:
         self.calls.append((label, "gemm", 2.0 * m * n * 2 * k,
                            lambda: mx.fp4_gemm_pair(a1[0], a1[1], b1[0], b1[1], a2[0], a2[1], b2[0], b2[1], c=c),
                            alg_bytes))
+        return c
+
+    # CTA-local NVFP4 calls (the operand-wise hybrid's Dgrads)
+    def nv_rows(self, label, x, offset):
+        mx, torch, (R, C) = self.mx, self.torch, x.shape
+        p = (R + 255) // 256
+        out = [self.u8(R, C // 2), self.u8(R, C // 16), self.e((p,), torch.float32), self.e((p,), torch.float32)]
+        self.calls.append((label, "quant", R * C * B_NV_ROWS,
+                           lambda: mx.fp4_nv_quantize_rows(x, 1, self.seed, offset, out=out), 0))
+        return out
+
+    def nv_w(self, label, w):
+        mx, torch, (N, K) = self.mx, self.torch, w.shape
+        out = [self.u8(N, K // 2), self.u8(N, K // 16), self.u8(K, N // 2), self.u8(K, N // 16),
+               self.e((1,), torch.float32), self.e((1,), torch.float32)]
+        self.calls.append((label, "quant", N * K * B_NV_W2D16, lambda: mx.fp4_nv_quantize_w2d16(w, out=out), 0))
+        return out
+
+    def nv_gemm(self, label, a, b, c=None, accumulate=False):
+        mx = self.mx
+        m, n, k = a[0].shape[0], b[0].shape[0], 2 * a[0].shape[1]
+        if c is None:
+            c = self.e((m, n), self.torch.float32)
+        self.calls.append((label, "nvgemm", 2.0 * m * n * k,
+                           lambda: mx.fp4_nv_gemm(a[0], a[1], a[2], b[0], b[1], b[2], c=c, accumulate=accumulate), 0))
         return c
 
     # -------------------------------------------------------------- workloads
@@ -375,6 +404,54 @@ class Step:
             self.charge["W1+W3 Dgrad"] = ["swiglu_backward", "rows(dA,SR)", "rows(dB,SR)"]
             self.charge["W1|W3 Wgrad"] += ["cols(dA,H32)", "cols(dB,H32)"]
 
+    def _build_ffn_hybrid(self):
+        """The operand-wise hybrid (FAF §3.3): the forward and both Wgrads in
+        MXFP4 as in the default step, both Dgrads in CTA-local NVFP4 (row SR of
+        dY, dA and dB with panel factors; 2D16 column views of W2, W1 and W3;
+        the contraction on the f16 matrix cores).  dY and dA/dB are quantized
+        twice (NVFP4 rows for Dgrad, MXFP4 H32 columns for Wgrad)."""
+        torch, mx = self.torch, self.mx
+        X, W1, W3, W2, dY = (self.d[k] for k in ("X", "W1", "W3", "W2", "dY"))
+        T, D = X.shape
+        F = W1.shape[0]
+        xr, xc = self.q_dual("dual(X: RTN rows, H32 cols)", X, 0)
+        w13_rc, w13_rs = self.u8(2 * F, D // 2), self.u8(2 * F, D // 32)
+        self.q_w("w2d32(W1)", W1, w13_rc[:F], w13_rs[:F])
+        self.q_w("w2d32(W3)", W3, w13_rc[F:], w13_rs[F:])
+        a, b = self.e((T, F), torch.int16), self.e((T, F), torch.int16)
+        hr = (self.u8(T, F // 2), self.u8(T, F // 32))
+        hc = (self.u8(F, T // 2), self.u8(F, T // 32))
+        self.calls.append(("swiglu_producer", "producer", 2.0 * T * 2 * F * D,
+                           lambda: mx.fp4_swiglu_producer(xr[0], xr[1], w13_rc, w13_rs, self.mask, True,
+                                                          a, b, hr[0], hr[1], hc[0], hc[1]), 0))
+        w2 = self.q_w("w2d32(W2)", W2)
+        self.gemm("W2 Fprop", hr, w2[:2])
+        dyc = self.q_cols("cols(dY,H32)", dY)
+        dyn = self.nv_rows("nv rows(dY,SR)", dY, 0)
+        w2n = self.nv_w("nv 2D16(W2)", W2)
+        dh = self.nv_gemm("W2 Dgrad (NVFP4)", dyn[:3], w2n[2:5])
+        self.gemm("W2 Wgrad", dyc, hc)
+        da, db = self.e((T, F), torch.int16), self.e((T, F), torch.int16)
+        self.calls.append(("swiglu_backward", "quant", T * F * B_SWIGLU_BWD,
+                           lambda: mx.fp4_swiglu_backward(dh, a, b, da, db), 0))
+        dabc = (self.u8(2 * F, T // 2), self.u8(2 * F, T // 32))
+        self.q_cols("cols(dA,H32)", da, out=(dabc[0][:F], dabc[1][:F]))
+        self.q_cols("cols(dB,H32)", db, out=(dabc[0][F:], dabc[1][F:]))
+        self.gemm("W1|W3 Wgrad", dabc, xc)
+        dan = self.nv_rows("nv rows(dA,SR)", da, 1)
+        dbn = self.nv_rows("nv rows(dB,SR)", db, 2)
+        w1n = self.nv_w("nv 2D16(W1)", W1)
+        w3n = self.nv_w("nv 2D16(W3)", W3)
+        dx = self.nv_gemm("W1 Dgrad (NVFP4)", dan[:3], w1n[2:5])
+        self.nv_gemm("W3 Dgrad (NVFP4)", dbn[:3], w3n[2:5], c=dx, accumulate=True)
+        self.charge = {"swiglu_producer": ["w2d32(W1)", "w2d32(W3)", "dual(X: RTN rows, H32 cols)"],
+                       "W2 Fprop": ["w2d32(W2)"],
+                       "W2 Dgrad (NVFP4)": ["nv rows(dY,SR)", "nv 2D16(W2)"],
+                       "W2 Wgrad": ["cols(dY,H32)"],
+                       "W1|W3 Wgrad": ["swiglu_backward", "cols(dA,H32)", "cols(dB,H32)"],
+                       "W1 Dgrad (NVFP4)": ["nv rows(dA,SR)", "nv 2D16(W1)"],
+                       "W3 Dgrad (NVFP4)": ["nv rows(dB,SR)", "nv 2D16(W3)"]}
+
     def run(self, events=None):
         for i, (_, _, _, fn, _) in enumerate(self.calls):
             if events is not None:
@@ -384,7 +461,7 @@ class Step:
                 events[i][1].record()
 
     def gemm_flops(self):
-        return sum(c[2] for c in self.calls if c[1] in ("gemm", "producer"))
+        return sum(c[2] for c in self.calls if c[1] in ("gemm", "producer", "nvgemm"))
 
 
 CPU_SAMPLE_SHAPES = {
@@ -713,7 +790,7 @@ def main():
         return
     print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
     step = Step(args.workload, args.seed, mx, torch, fused_backward=not args.unfused_backward,
-                dgrad_epilogue=args.dgrad_epilogue)
+                dgrad_epilogue=args.dgrad_epilogue, nvfp4_dgrad=args.hybrid_dgrad)
     ncalls = len(step.calls)
     print(f"[bench] warmup {args.warmup} steps, {ncalls} calls per step", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -760,6 +837,9 @@ def main():
         if kind in ("gemm", "producer"):
             entry["tflops"] = round(units / ms / 1e9, 1)
             entry["frac_mfma_peak"] = round(units / ms / 1e9 / PEAK_MXFP4_TFLOPS, 4)
+        elif kind == "nvgemm":
+            entry["tflops"] = round(units / ms / 1e9, 1)
+            entry["frac_16bit_mfma_peak"] = round(units / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
         else:
             entry["gbps"] = round(units / ms / 1e6, 1)
             entry["frac_hbm_peak"] = round(units / ms / 1e6 / PEAK_HBM_GBPS, 4)
@@ -770,7 +850,7 @@ def main():
     ms_of = {e["call"]: e["ms"] for e in per}
     contractions = []
     for label, kind, units, _, _ in step.calls:
-        if kind not in ("gemm", "producer"):
+        if kind not in ("gemm", "producer", "nvgemm"):
             continue
         prod_ms = sum(ms_of[p] for p in step.charge.get(label, []))
         contractions.append({"contraction": label, "tflop": round(units / 1e12, 4), "gemm_ms": ms_of[label],
@@ -799,8 +879,9 @@ def main():
         "dtype": "e2m1/e8m0 operands, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": args.workload, "gemm_tflop_per_step": round(flops / 1e12, 3),
-                   "swiglu_backward": ("unfused" if args.unfused_backward else
+                   "swiglu_backward": ("unfused" if (args.unfused_backward or step.nvfp4_dgrad) else
                                        "in the W2 Dgrad epilogue" if step.dgrad_epilogue else "fused producer"),
+                   "dgrad": "CTA-local NVFP4 (operand-wise hybrid)" if step.nvfp4_dgrad else "MXFP4",
                    "launch": mode,
                    "quantizer_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1) if q_ms > 0 else None,
                    "quantizer_frac_hbm_peak": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if q_ms > 0 else None},
@@ -812,7 +893,9 @@ def main():
         "breakdown": per,
         "contractions": contractions,
     }
-    if not args.no_cpu_baseline:
+    if step.nvfp4_dgrad:
+        out["cpu_baseline"] = None                         # the oracle step is the MXFP4 one: see --nvfp4-dgrad
+    elif not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(step)
     print(json.dumps(out), flush=True)
