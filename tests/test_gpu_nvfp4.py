@@ -323,3 +323,20 @@ def test_nv_long_k_and_tall_tensor(gpu_lib):
         for g, w, nm in zip(q, want, ("codes", "scales", "factor", "max")):
             got = g[r0:r0 + N.PANEL] if nm in ("codes", "scales") else g[p:p + 1]
             assert_same(got, w, f"tall tensor {nm} panel {p}")
+
+
+def test_nv_gemm_strided_c(gpu_lib):
+    """C as a column slice of a wider fp32 tensor (ldc > n): the columns
+    outside the slice keep their values, with and without accumulation."""
+    m, n, k = 288, 160, 192
+    a = gpu_lib.fp4_nv_quantize_rows(dev16(synthetic.tensor((m, k), std=1.0, seed=52)))[:3]
+    b = gpu_lib.fp4_nv_quantize_rows(dev16(synthetic.tensor((n, k), std=0.1, seed=53)))[:3]
+    wide = torch.full((m, n + 96), 7.0, device="cuda")
+    view = wide[:, 32:32 + n]
+    gpu_lib.fp4_nv_gemm(*a, *b, c=view)
+    check_nv_gemm(view, a, b, k)
+    prev = host(view).copy()
+    gpu_lib.fp4_nv_gemm(*a, *b, c=view, accumulate=True)
+    check_nv_gemm(view, a, b, k, c_prev=prev, what="strided accumulate")
+    w = host(wide)
+    assert np.all(w[:, :32] == 7.0) and np.all(w[:, 32 + n:] == 7.0)
