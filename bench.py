@@ -59,6 +59,8 @@ def parse():
     p.add_argument("--dgrad-epilogue", action="store_true",
                    help="FFN step: W2 Dgrad with the SwiGLU backward producer in its epilogue (one launch; dH never "
                         "in memory) instead of W2 Dgrad followed by the backward producer")
+    p.add_argument("--separate-gemms", action="store_true",
+                   help="FFN step: W2 Dgrad and W2 Wgrad as two launches instead of one fp4_gemm_grouped")
     p.add_argument("--eager", action="store_true",
                    help="time the step as eager launches instead of one captured HIP graph")
     p.add_argument("--quality", action="store_true",
@@ -185,10 +187,15 @@ def quantizer_sweep(mx, torch, reps=9):
     return rows
 
 
+W2_GROUP = "W2 Wgrad | W2 Dgrad"          # label of the FFN backward's grouped launch
+
+
 class Step:
     """Holds device inputs/outputs and enqueues one step as a list of named calls."""
 
-    def __init__(self, name, seed, mx, torch, fused_backward=True, dgrad_epilogue=False, nvfp4_dgrad=False):
+    def __init__(self, name, seed, mx, torch, fused_backward=True, dgrad_epilogue=False, nvfp4_dgrad=False,
+                 grouped=True):
+        self.grouped = grouped
         self.fused_backward = fused_backward
         self.dgrad_epilogue = dgrad_epilogue and fused_backward
         self.nvfp4_dgrad = nvfp4_dgrad
@@ -268,6 +275,23 @@ class Step:
                            lambda: mx.fp4_gemm_pair(a1[0], a1[1], b1[0], b1[1], a2[0], a2[1], b2[0], b2[1], c=c),
                            alg_bytes))
         return c
+
+    def gemm_group(self, label, probs):
+        """Independent contractions in one launch (fp4_gemm_grouped).  probs:
+        (a, b, a2, b2, c) with a2 = b2 = None for the plain form."""
+        mx, torch = self.mx, self.torch
+        flops = alg_bytes = 0
+        args = []
+        for a, b, a2, b2, c in probs:
+            m, n, k = a[0].shape[0], b[0].shape[0], 2 * a[0].shape[1]
+            npair = 1 if a2 is None else 2
+            flops += 2.0 * m * n * k * npair
+            alg_bytes += npair * (m + n) * k * (0.5 + 1 / 32) + 4 * m * n
+            d = dict(a_codes=a[0], a_scales=a[1], b_codes=b[0], b_scales=b[1], c=c)
+            if a2 is not None:
+                d.update(a2_codes=a2[0], a2_scales=a2[1], b2_codes=b2[0], b2_scales=b2[1])
+            args.append(d)
+        self.calls.append((label, "gemm", flops, lambda: mx.fp4_gemm_grouped(args), alg_bytes))
 
     # CTA-local NVFP4 calls (the operand-wise hybrid's Dgrads)
     def nv_rows(self, label, x, offset):
@@ -352,9 +376,17 @@ class Step:
             self.calls.append((label, "producer", 2.0 * T * F * D,
                                lambda: mx.fp4_gemm_swiglu_backward_producer(dyr[0], dyr[1], w2[2], w2[3], a, b,
                                                                             self.seed, 1, 2, self.mask, outs), 0))
+            self.gemm("W2 Wgrad", dyc, hc)
+        elif self.grouped:
+            # W2 Wgrad has 896 tiles of 32 K steps (3.5 rounds of 256 CUs): in
+            # one launch with W2 Dgrad's 1792 shorter tiles, those fill the CUs
+            # that its last round leaves idle
+            dh = self.e((T, F), torch.float32)
+            dw2 = self.e((D, F), torch.float32)
+            self.gemm_group(W2_GROUP, [(dyc, hc, None, None, dw2), (dyr, w2[2:], None, None, dh)])
         else:
             dh = self.gemm("W2 Dgrad", dyr, w2[2:])
-        self.gemm("W2 Wgrad", dyc, hc)
+            self.gemm("W2 Wgrad", dyc, hc)
         # column-facing dA and dB land in one stacked [2F][T/2] buffer, so that
         # the W1 and W3 Wgrads (same B operand, X column-facing) run as one
         # contraction with M = 2F: 2x896 256x256 tiles (3.5 rounds of 256 CUs
@@ -381,28 +413,31 @@ class Step:
         xc = xc_dual if self.fused_backward else self.q_cols("cols(X,H32)", X)
         # the stacked Wgrad reads the column-facing dA, dB just written; then
         # dX = dA W1 + dB W3 as one contraction over K = 2F (no fp32 read-back of dX)
+        # (these two stay separate launches: grouped, with the longer Dgrad tiles
+        # first, they saved about 3 us themselves but the next step's SwiGLU
+        # producer ran about 22 us slower after them, on four alternating runs)
         self.gemm("W1|W3 Wgrad", dabc, xc)
         self.gemm_pair("W1+W3 Dgrad", dar, w1[2:], dbr, w3[2:])
         # each producer is charged to the first contraction that reads it
         self.charge = {"swiglu_producer": ["w2d32(W1)", "w2d32(W3)"], "W2 Fprop": ["w2d32(W2)"]}
-        if self.dgrad_epilogue:
+        w2dg = "W2 Dgrad + swiglu_bwd_producer" if self.dgrad_epilogue else W2_GROUP if self.grouped else "W2 Dgrad"
+        w2wg = W2_GROUP if self.grouped and not self.dgrad_epilogue else "W2 Wgrad"
+        w13wg, w13dg = "W1|W3 Wgrad", "W1+W3 Dgrad"
+        if self.fused_backward:
             self.charge["swiglu_producer"].append("dual(X: RTN rows, H32 cols)")
-            self.charge["W2 Dgrad + swiglu_bwd_producer"] = ["dual(dY: SR rows, H32 cols)"]
-        elif self.fused_backward:
-            self.charge["swiglu_producer"].append("dual(X: RTN rows, H32 cols)")
-            self.charge["W2 Dgrad"] = ["dual(dY: SR rows, H32 cols)"]
+            self.charge[w2dg] = ["dual(dY: SR rows, H32 cols)"]
         else:
             self.charge["swiglu_producer"].append("rows(X)")
-            self.charge["W2 Dgrad"] = ["rows(dY,SR)"]
-            self.charge["W2 Wgrad"] = ["cols(dY,H32)"]
-            self.charge["W1|W3 Wgrad"] = ["cols(X,H32)"]
+            self.charge[w2dg] = ["rows(dY,SR)"]
+            self.charge.setdefault(w2wg, []).append("cols(dY,H32)")
+            self.charge.setdefault(w13wg, []).append("cols(X,H32)")
         if self.dgrad_epilogue:
             pass
         elif self.fused_backward:
-            self.charge["W1+W3 Dgrad"] = ["swiglu_bwd_producer"]
+            self.charge.setdefault(w13dg, []).append("swiglu_bwd_producer")
         else:
-            self.charge["W1+W3 Dgrad"] = ["swiglu_backward", "rows(dA,SR)", "rows(dB,SR)"]
-            self.charge["W1|W3 Wgrad"] += ["cols(dA,H32)", "cols(dB,H32)"]
+            self.charge.setdefault(w13dg, []).extend(["swiglu_backward", "rows(dA,SR)", "rows(dB,SR)"])
+            self.charge[w13wg] += ["cols(dA,H32)", "cols(dB,H32)"]
 
     def _build_ffn_hybrid(self):
         """The operand-wise hybrid (FAF §3.3): the forward and both Wgrads in
@@ -790,7 +825,8 @@ def main():
         return
     print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
     step = Step(args.workload, args.seed, mx, torch, fused_backward=not args.unfused_backward,
-                dgrad_epilogue=args.dgrad_epilogue, nvfp4_dgrad=args.hybrid_dgrad)
+                dgrad_epilogue=args.dgrad_epilogue, nvfp4_dgrad=args.hybrid_dgrad,
+                grouped=not args.separate_gemms)
     ncalls = len(step.calls)
     print(f"[bench] warmup {args.warmup} steps, {ncalls} calls per step", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

@@ -206,6 +206,47 @@ fp4_status fp4_gemm_pair(int64_t m, int64_t n, int64_t k,
                          float* c, int64_t ldc, int accumulate, hipStream_t stream);
 
 /*
+ * Independent block-scaled products in one launch (§2.3 Eq. 4-6: the FFN
+ * backward's contractions that read the same producers' outputs, e.g. the
+ * W2 Dgrad and the W2 Wgrad of one step).  Problem q computes what
+ *   fp4_gemm(m, n, k, a, b, c, ldc, accumulate)            (a2_codes NULL)
+ *   fp4_gemm_pair(m, n, k, a, b, a2, b2, c, ldc, accumulate) (otherwise)
+ * computes, with the same bytes.  When every k is a multiple of 256 the
+ * problems share one launch of the GEMM kernel, longest K per tile first, so
+ * the tiles of one problem fill the CUs that another problem's last round of
+ * tiles leaves idle; a problem with k = 0 or k % 256 != 0 runs as its own
+ * call, after the shared launch.  No order holds between the problems: no
+ * problem's c may overlap another problem's c or any operand.
+ *   problems  host array of `count` descriptors, read during the call only
+ *   count     0 .. FP4_GEMM_GROUP_MAX
+ * Errors: FP4_EINVAL count outside 0 .. FP4_GEMM_GROUP_MAX, problems NULL
+ * with count > 0, or a problem that fp4_gemm / fp4_gemm_pair would reject
+ * with FP4_EINVAL (for the pair form all four of a2_codes, a2_scales,
+ * b2_codes, b2_scales must be non-NULL, otherwise all four NULL); FP4_ESHAPE,
+ * FP4_EALIGN as those calls, and FP4_ESHAPE when the problems together have
+ * more than 2^31 - 1 tiles.  Every problem is checked before anything is
+ * enqueued.
+ */
+#define FP4_GEMM_GROUP_MAX 4
+
+typedef struct fp4_gemm_problem {
+  int64_t m, n, k;
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  const uint8_t* a2_codes;
+  const uint8_t* a2_scales;
+  const uint8_t* b2_codes;
+  const uint8_t* b2_scales;
+  float* c;
+  int64_t ldc;
+  int accumulate;
+} fp4_gemm_problem;
+
+fp4_status fp4_gemm_grouped(const fp4_gemm_problem* problems, int count, hipStream_t stream);
+
+/*
  * Fused gated-FFN producer (§3.2): a = X W1^T and b = X W3^T computed together
  * on the block-scaled MFMA, rounded to bf16 (RNE) and saved for backward; then
  *   sig = 1/(1 + exp(-a)), s = a*sig, h = bf16(s*b)

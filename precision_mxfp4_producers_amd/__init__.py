@@ -31,6 +31,7 @@ _SIGS = {
     "fp4_quantize_w2d32": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.c_float, _vp],
     "fp4_gemm": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _int, _vp],
     "fp4_gemm_pair": [_i64, _i64, _i64] + [_vp] * 9 + [_i64, _int, _vp],
+    "fp4_gemm_grouped": [_vp, _int, _vp],
     "fp4_swiglu_producer": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u32, _vp],
     "fp4_swiglu_backward": [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp],
     "fp4_swiglu_backward_producer": [_i64, _i64, _vp, _i64, _vp, _vp, _u64, _u64, _u64, _u32] + [_vp] * 9,
@@ -156,24 +157,40 @@ def fp4_quantize_w2d32(w, finer_ratio=0.87, row_codes=None, row_scales=None, col
     return row_codes, row_scales, col_codes, col_scales
 
 
-def fp4_gemm(a_codes, a_scales, b_codes, b_scales, c=None, accumulate=False):
-    for t, nm in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
-        _dev(t, nm)
-        if t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 2:
-            raise Fp4Error(f"{nm} must be a contiguous 2-D uint8 tensor")
-    m, k2 = a_codes.shape
-    n = b_codes.shape[0]
+def _gemm_shapes(pairs):
+    """(m, n, k) of the products C (+)= sum of A B^T over `pairs` of
+    (a_codes, a_scales, b_codes, b_scales) with names; all pairs alike."""
+    for quad in pairs:
+        for t, nm in quad:
+            _dev(t, nm)
+            if t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 2:
+                raise Fp4Error(f"{nm} must be a contiguous 2-D uint8 tensor")
+    (ac, _), _, (bc, _), _ = pairs[0]
+    m, k2 = ac.shape
+    n = bc.shape[0]
     k = 2 * k2
-    if b_codes.shape[1] != k2 or tuple(a_scales.shape) != (m, k // 32) or tuple(b_scales.shape) != (n, k // 32):
-        raise Fp4Error("operand shapes disagree")
+    for (ac, _), (asc, _), (bc, _), (bsc, _) in pairs:
+        if (tuple(ac.shape) != (m, k2) or tuple(bc.shape) != (n, k2) or tuple(asc.shape) != (m, k // 32)
+                or tuple(bsc.shape) != (n, k // 32)):
+            raise Fp4Error("operand shapes disagree")
+    return m, n, k
+
+
+def _gemm_out(c, m, n, accumulate, device):
     if c is None:
         if accumulate:
             raise Fp4Error("accumulate needs an output tensor")
-        c = torch.empty((m, n), dtype=torch.float32, device=a_codes.device)
-    else:
-        _dev(c, "c")
-        if c.dtype != torch.float32 or c.dim() != 2 or c.stride(1) != 1 or tuple(c.shape) != (m, n):
-            raise Fp4Error("c must be fp32 [m][n] with unit column stride")
+        return torch.empty((m, n), dtype=torch.float32, device=device)
+    _dev(c, "c")
+    if c.dtype != torch.float32 or c.dim() != 2 or c.stride(1) != 1 or tuple(c.shape) != (m, n):
+        raise Fp4Error("c must be fp32 [m][n] with unit column stride")
+    return c
+
+
+def fp4_gemm(a_codes, a_scales, b_codes, b_scales, c=None, accumulate=False):
+    m, n, k = _gemm_shapes([((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"),
+                             (b_scales, "b_scales"))])
+    c = _gemm_out(c, m, n, accumulate, a_codes.device)
     _check(load().fp4_gemm(m, n, k, _p(a_codes), _p(a_scales), _p(b_codes), _p(b_scales), _p(c), c.stride(0),
                            1 if accumulate else 0, _stream()))
     return c
@@ -184,28 +201,46 @@ def fp4_gemm_pair(a1_codes, a1_scales, b1_codes, b1_scales, a2_codes, a2_scales,
     """C (+)= A1 B1^T + A2 B2^T, one fp32 sum over both K ranges (same shapes)."""
     ops = ((a1_codes, "a1_codes"), (a1_scales, "a1_scales"), (b1_codes, "b1_codes"), (b1_scales, "b1_scales"),
            (a2_codes, "a2_codes"), (a2_scales, "a2_scales"), (b2_codes, "b2_codes"), (b2_scales, "b2_scales"))
-    for t, nm in ops:
-        _dev(t, nm)
-        if t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 2:
-            raise Fp4Error(f"{nm} must be a contiguous 2-D uint8 tensor")
-    m, k2 = a1_codes.shape
-    n = b1_codes.shape[0]
-    k = 2 * k2
-    for (ac, asc, bc, bsc) in ((a1_codes, a1_scales, b1_codes, b1_scales), (a2_codes, a2_scales, b2_codes, b2_scales)):
-        if (tuple(ac.shape) != (m, k2) or tuple(bc.shape) != (n, k2) or tuple(asc.shape) != (m, k // 32)
-                or tuple(bsc.shape) != (n, k // 32)):
-            raise Fp4Error("operand shapes disagree")
-    if c is None:
-        if accumulate:
-            raise Fp4Error("accumulate needs an output tensor")
-        c = torch.empty((m, n), dtype=torch.float32, device=a1_codes.device)
-    else:
-        _dev(c, "c")
-        if c.dtype != torch.float32 or c.dim() != 2 or c.stride(1) != 1 or tuple(c.shape) != (m, n):
-            raise Fp4Error("c must be fp32 [m][n] with unit column stride")
+    m, n, k = _gemm_shapes([ops[:4], ops[4:]])
+    c = _gemm_out(c, m, n, accumulate, a1_codes.device)
     _check(load().fp4_gemm_pair(m, n, k, *(_p(t) for t, _ in ops), _p(c), c.stride(0), 1 if accumulate else 0,
                                 _stream()))
     return c
+
+
+class _GemmProblem(ctypes.Structure):
+    _fields_ = [("m", _i64), ("n", _i64), ("k", _i64), ("a_codes", _vp), ("a_scales", _vp), ("b_codes", _vp),
+                ("b_scales", _vp), ("a2_codes", _vp), ("a2_scales", _vp), ("b2_codes", _vp), ("b2_scales", _vp),
+                ("c", _vp), ("ldc", _i64), ("accumulate", _int)]
+
+
+GEMM_GROUP_MAX = 4
+_GEMM_KEYS = ("a_codes", "a_scales", "b_codes", "b_scales")
+_GEMM2_KEYS = ("a2_codes", "a2_scales", "b2_codes", "b2_scales")
+
+
+def fp4_gemm_grouped(problems):
+    """Independent products in one launch.  Each problem is a dict with
+    a_codes, a_scales, b_codes, b_scales, optionally a2_codes, a2_scales,
+    b2_codes, b2_scales (the fp4_gemm_pair form), c and accumulate; returns the
+    list of C tensors (allocated where c is missing)."""
+    if len(problems) > GEMM_GROUP_MAX:
+        raise Fp4Error(f"at most {GEMM_GROUP_MAX} problems per call")
+    arr = (_GemmProblem * max(1, len(problems)))()
+    outs = []
+    for q, pr in enumerate(problems):
+        quads = [tuple((pr[key], f"problems[{q}].{key}") for key in _GEMM_KEYS)]
+        pair = any(pr.get(key) is not None for key in _GEMM2_KEYS)
+        if pair:
+            quads.append(tuple((pr.get(key), f"problems[{q}].{key}") for key in _GEMM2_KEYS))
+        m, n, k = _gemm_shapes(quads)
+        acc = bool(pr.get("accumulate", False))
+        c = _gemm_out(pr.get("c"), m, n, acc, pr["a_codes"].device)
+        outs.append(c)
+        ptrs = [_p(pr[key]) for key in _GEMM_KEYS] + [_p(pr[key]) if pair else None for key in _GEMM2_KEYS]
+        arr[q] = _GemmProblem(m, n, k, *ptrs, _p(c), c.stride(0), 1 if acc else 0)
+    _check(load().fp4_gemm_grouped(ctypes.cast(arr, _vp), len(problems), _stream()))
+    return outs
 
 
 def _u8_2d(t, name, shape=None):

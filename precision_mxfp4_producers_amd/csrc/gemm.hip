@@ -354,26 +354,56 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_generic_kernel(
   }
 }
 
-// a2_codes == nullptr: C (+)= A B^T.  Otherwise C (+)= A B^T + A2 B2^T as one
-// fp32 accumulation over both K ranges (each K long).  `flags`: bit 0
+// One product of a launch: C (+)= A B^T, or with a2c set C (+)= A B^T + A2 B2^T
+// as one fp32 accumulation over both K ranges (each K long).  `flags`: bit 0
 // accumulate, bit 1 write C with non-temporal (streaming) stores.
-__global__ __launch_bounds__(kFastThreads) void gemm_fast_kernel(
-    int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
-    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, const uint8_t* __restrict__ a2_codes,
-    const uint8_t* __restrict__ a2_scales, const uint8_t* __restrict__ b2_codes,
-    const uint8_t* __restrict__ b2_scales, float* __restrict__ c, int64_t ldc, int flags) {
+struct GemmJob {
+  const uint8_t* ac;
+  const uint8_t* as;
+  const uint8_t* bc;
+  const uint8_t* bs;
+  const uint8_t* a2c;
+  const uint8_t* a2s;
+  const uint8_t* b2c;
+  const uint8_t* b2s;
+  float* c;
+  int64_t M, N, K, ldc;
+  int64_t tiles;                            // 256 x 256 output tiles of this product
+  int flags;
+};
+constexpr int kMaxGemmJobs = 4;
+struct GemmGroup {
+  GemmJob job[kMaxGemmJobs];
+  int count;
+};
+
+// Up to kMaxGemmJobs independent products in one launch: job q owns the
+// workgroups after those of jobs 0 .. q-1, and the workgroup dispatcher hands
+// them out in that order, so a job that leaves the last round of tiles part
+// empty is followed at once by the next job's tiles on the idle CUs.  Every
+// tile runs the same loop and epilogue as in a launch of its own.
+__global__ __launch_bounds__(kFastThreads) void gemm_fast_kernel(const GemmGroup g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  GemmJob J = g.job[0];
+  int64_t pid = blockIdx.x;
+#pragma unroll
+  for (int q = 1; q < kMaxGemmJobs; ++q) {
+    if (q < g.count && pid >= J.tiles) {
+      pid -= J.tiles;
+      J = g.job[q];
+    }
+  }
   int64_t tm, tn;
-  tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  tile_coords_of(pid, J.tiles, (J.M + BM - 1) / BM, (J.N + BN - 1) / BN, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3, hl = lane >> 5;
-  Operand A{a_codes, a_scales, M}, B{b_codes, b_scales, N};
-  Operand A2{a2_codes, a2_scales, M}, B2{b2_codes, b2_scales, N};
+  Operand A{J.ac, J.as, J.M}, B{J.bc, J.bs, J.N};
+  Operand A2{J.a2c, J.a2s, J.M}, B2{J.b2c, J.b2s, J.N};
   v16f acc[4][2];
-  main_loop_fast<false>(smem, A, B, m0, n0, 0, K, acc, wm, wn, &A2, &B2);
-  store_c_tile_wave(smem, acc, c, ldc, M, N, m0, n0, wave, lane, wm, wn, hl, (flags & 1) != 0,
-                    (flags & 2) != 0);
+  main_loop_fast<false>(smem, A, B, m0, n0, 0, J.K, acc, wm, wn, &A2, &B2);
+  store_c_tile_wave(smem, acc, J.c, J.ldc, J.M, J.N, m0, n0, wave, lane, wm, wn, hl, (J.flags & 1) != 0,
+                    (J.flags & 2) != 0);
 }
 
 // SwiGLU producer output tile: 256 tokens x 128 FFN columns.
@@ -462,67 +492,151 @@ static int fast_flags(int64_t m, int64_t n, int accumulate) {
   return accumulate | (m * n * 4 > kStreamCBytes ? 2 : 0);
 }
 
+// The fast kernel needs K % 256 == 0 and buffer offsets below 2^31 per tile.
+static bool fast_k(int64_t k) { return k > 0 && (k % 256) == 0 && 256 * (k / 2) < 0x7FFFFFFF; }
+
+static GemmJob make_job(const fp4_gemm_problem& p, int64_t tiles) {
+  GemmJob j{};
+  j.ac = p.a_codes;
+  j.as = p.a_scales;
+  j.bc = p.b_codes;
+  j.bs = p.b_scales;
+  j.a2c = p.a2_codes;
+  j.a2s = p.a2_scales;
+  j.b2c = p.b2_codes;
+  j.b2s = p.b2_scales;
+  j.c = p.c;
+  j.M = p.m;
+  j.N = p.n;
+  j.K = p.k;
+  j.ldc = p.ldc;
+  j.tiles = tiles;
+  j.flags = fast_flags(p.m, p.n, p.accumulate);
+  return j;
+}
+
+// Argument checks of one product (plain or pair form); `tiles` gets its
+// number of 256 x 256 output tiles (0 when C is empty).
+static fp4_status check_problem(const fp4_gemm_problem& p, int64_t& tiles) {
+  tiles = 0;
+  if (p.accumulate != 0 && p.accumulate != 1) return FP4_EINVAL;
+  if (!mult32z(p.m) || !mult32z(p.n) || !mult32z(p.k) || p.ldc < p.n) return FP4_ESHAPE;
+  if (p.m == 0 || p.n == 0) return FP4_OK;                // empty C
+  if (!p.c) return FP4_EINVAL;
+  if (p.k == 0) {                                         // C = 0, or unchanged when accumulating
+    if (!p.accumulate && (p.n + 255) / 256 > 0x7FFFFFFF) return FP4_ESHAPE;
+    return FP4_OK;
+  }
+  const bool pair = p.a2_codes || p.a2_scales || p.b2_codes || p.b2_scales;
+  if (!p.a_codes || !p.a_scales || !p.b_codes || !p.b_scales) return FP4_EINVAL;
+  if (pair && !(p.a2_codes && p.a2_scales && p.b2_codes && p.b2_scales)) return FP4_EINVAL;
+  if (!aligned16(p.a_codes) || !aligned16(p.b_codes) || !aligned16(p.a_scales) || !aligned16(p.b_scales) ||
+      !aligned16(p.c) || (p.ldc % 4) != 0)
+    return FP4_EALIGN;
+  if (pair && (!aligned16(p.a2_codes) || !aligned16(p.b2_codes) || !aligned16(p.a2_scales) ||
+               !aligned16(p.b2_scales)))
+    return FP4_EALIGN;
+  tiles = grid_tiles(p.m, BM, p.n, BN);
+  if (tiles < 0) return FP4_ESHAPE;
+  return FP4_OK;
+}
+
+static fp4_status launch_fast(const GemmGroup& g, int64_t total_tiles, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_fast_kernel, dim3((unsigned)total_tiles), dim3(kFastThreads), 0, s, g);
+  return launch_status();
+}
+
+// One checked product on its own: the fill kernel for K = 0, the fast kernel,
+// or the generic kernel(s).
+static fp4_status run_problem(const fp4_gemm_problem& p, int64_t tiles, hipStream_t s) {
+  if (p.m == 0 || p.n == 0) return FP4_OK;
+  if (p.k == 0) {
+    if (p.accumulate) return FP4_OK;
+    const int64_t gx = (p.n + 255) / 256, gy = std::min<int64_t>(p.m, 65535);
+    hipLaunchKernelGGL(fill_rows_f32_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, p.c, p.m, p.n,
+                       p.ldc);
+    return launch_status();
+  }
+  if (fast_k(p.k)) {
+    GemmGroup g{};
+    g.job[0] = make_job(p, tiles);
+    g.count = 1;
+    return launch_fast(g, tiles, s);
+  }
+  hipLaunchKernelGGL(gemm_generic_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, p.m, p.n, p.k,
+                     p.a_codes, p.a_scales, p.b_codes, p.b_scales, p.c, p.ldc, p.accumulate);
+  fp4_status st = launch_status();
+  if (st != FP4_OK || !p.a2_codes) return st;
+  // pair form with K not a multiple of 256: the second product is added to the first's result
+  hipLaunchKernelGGL(gemm_generic_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, p.m, p.n, p.k,
+                     p.a2_codes, p.a2_scales, p.b2_codes, p.b2_scales, p.c, p.ldc, 1);
+  return launch_status();
+}
+
 extern "C" {
 
 fp4_status fp4_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                     const uint8_t* b_codes, const uint8_t* b_scales, float* c, int64_t ldc, int accumulate,
                     hipStream_t stream) {
-  if (accumulate != 0 && accumulate != 1) return FP4_EINVAL;
-  if (!mult32z(m) || !mult32z(n) || !mult32z(k) || ldc < n) return FP4_ESHAPE;
-  if (m == 0 || n == 0) return FP4_OK;                    // empty C
-  if (!c) return FP4_EINVAL;
-  if (k == 0) {                                           // empty sums: C = 0, or C unchanged when accumulating
-    if (accumulate) return FP4_OK;
-    const int64_t gx = (n + 255) / 256, gy = std::min<int64_t>(m, 65535);
-    if (gx > 0x7FFFFFFF) return FP4_ESHAPE;
-    hipLaunchKernelGGL(fill_rows_f32_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
-                       as_stream(stream), c, m, n, ldc);
-    return launch_status();
-  }
-  if (!a_codes || !a_scales || !b_codes || !b_scales) return FP4_EINVAL;
-  if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned16(a_scales) || !aligned16(b_scales) ||
-      !aligned16(c) || (ldc % 4) != 0)
-    return FP4_EALIGN;
-  const int64_t tiles = grid_tiles(m, BM, n, BN);
-  if (tiles < 0) return FP4_ESHAPE;
-  hipStream_t s = as_stream(stream);
-  // the fast path needs K % 256 == 0 and buffer offsets below 2^31 per tile
-  if ((k % 256) == 0 && 256 * (k / 2) < 0x7FFFFFFF)
-    hipLaunchKernelGGL(gemm_fast_kernel, dim3((unsigned)tiles), dim3(kFastThreads), 0, s, m, n, k, a_codes, a_scales,
-                       b_codes, b_scales, nullptr, nullptr, nullptr, nullptr, c, ldc, fast_flags(m, n, accumulate));
-  else
-    hipLaunchKernelGGL(gemm_generic_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, m, n, k, a_codes,
-                       a_scales, b_codes, b_scales, c, ldc, accumulate);
-  return launch_status();
+  const fp4_gemm_problem p{m, n, k, a_codes, a_scales, b_codes, b_scales, nullptr, nullptr, nullptr, nullptr,
+                           c, ldc, accumulate};
+  int64_t tiles;
+  const fp4_status st = check_problem(p, tiles);
+  if (st != FP4_OK) return st;
+  return run_problem(p, tiles, as_stream(stream));
 }
 
 fp4_status fp4_gemm_pair(int64_t m, int64_t n, int64_t k, const uint8_t* a1_codes, const uint8_t* a1_scales,
                          const uint8_t* b1_codes, const uint8_t* b1_scales, const uint8_t* a2_codes,
                          const uint8_t* a2_scales, const uint8_t* b2_codes, const uint8_t* b2_scales, float* c,
                          int64_t ldc, int accumulate, hipStream_t stream) {
-  if (accumulate != 0 && accumulate != 1) return FP4_EINVAL;
-  if (!mult32z(m) || !mult32z(n) || !mult32z(k) || ldc < n) return FP4_ESHAPE;
-  if (m == 0 || n == 0) return FP4_OK;
-  if (k == 0) return fp4_gemm(m, n, 0, nullptr, nullptr, nullptr, nullptr, c, ldc, accumulate, stream);
-  if (!c || !a1_codes || !a1_scales || !b1_codes || !b1_scales || !a2_codes || !a2_scales || !b2_codes ||
-      !b2_scales)
+  // with all four second operands NULL the checks below would take the plain
+  // form; here that is a missing operand
+  if (!a2_codes && !a2_scales && !b2_codes && !b2_scales && mult32z(m) && mult32z(n) && mult32z(k) && k > 0 &&
+      ldc >= n && m > 0 && n > 0)
     return FP4_EINVAL;
-  if (!aligned16(a1_codes) || !aligned16(b1_codes) || !aligned16(a1_scales) || !aligned16(b1_scales) ||
-      !aligned16(a2_codes) || !aligned16(b2_codes) || !aligned16(a2_scales) || !aligned16(b2_scales) ||
-      !aligned16(c) || (ldc % 4) != 0)
-    return FP4_EALIGN;
-  const int64_t tiles = grid_tiles(m, BM, n, BN);
-  if (tiles < 0) return FP4_ESHAPE;
-  if ((k % 256) == 0 && 256 * (k / 2) < 0x7FFFFFFF) {
-    hipLaunchKernelGGL(gemm_fast_kernel, dim3((unsigned)tiles), dim3(kFastThreads), 0, as_stream(stream), m, n, k,
-                       a1_codes, a1_scales, b1_codes, b1_scales, a2_codes, a2_scales, b2_codes, b2_scales, c, ldc,
-                       fast_flags(m, n, accumulate));
-    return launch_status();
-  }
-  // K not a multiple of 256: the second product is added to the first's result
-  const fp4_status st = fp4_gemm(m, n, k, a1_codes, a1_scales, b1_codes, b1_scales, c, ldc, accumulate, stream);
+  const fp4_gemm_problem p{m, n, k, a1_codes, a1_scales, b1_codes, b1_scales, a2_codes, a2_scales, b2_codes,
+                           b2_scales, c, ldc, accumulate};
+  int64_t tiles;
+  const fp4_status st = check_problem(p, tiles);
   if (st != FP4_OK) return st;
-  return fp4_gemm(m, n, k, a2_codes, a2_scales, b2_codes, b2_scales, c, ldc, 1, stream);
+  return run_problem(p, tiles, as_stream(stream));
+}
+
+fp4_status fp4_gemm_grouped(const fp4_gemm_problem* problems, int count, hipStream_t stream) {
+  if (count < 0 || count > FP4_GEMM_GROUP_MAX) return FP4_EINVAL;
+  if (count == 0) return FP4_OK;
+  if (!problems) return FP4_EINVAL;
+  int64_t tiles[FP4_GEMM_GROUP_MAX];
+  int64_t total = 0;
+  for (int q = 0; q < count; ++q) {
+    const fp4_status st = check_problem(problems[q], tiles[q]);
+    if (st != FP4_OK) return st;
+    if (fast_k(problems[q].k)) total += tiles[q];
+  }
+  if (total > 0x7FFFFFFF) return FP4_ESHAPE;
+  hipStream_t s = as_stream(stream);
+  // the shared launch: longest K per tile first (pair form: both K ranges)
+  int order[FP4_GEMM_GROUP_MAX];
+  int nfast = 0;
+  for (int q = 0; q < count; ++q)
+    if (fast_k(problems[q].k) && tiles[q] > 0) order[nfast++] = q;
+  auto steps = [&](int q) { return problems[q].k * (problems[q].a2_codes ? 2 : 1); };
+  for (int i = 1; i < nfast; ++i)                         // stable insertion sort, descending
+    for (int j = i; j > 0 && steps(order[j]) > steps(order[j - 1]); --j) std::swap(order[j], order[j - 1]);
+  if (nfast > 0) {
+    GemmGroup g{};
+    for (int i = 0; i < nfast; ++i) g.job[i] = make_job(problems[order[i]], tiles[order[i]]);
+    g.count = nfast;
+    const fp4_status st = launch_fast(g, total, s);
+    if (st != FP4_OK) return st;
+  }
+  for (int q = 0; q < count; ++q) {
+    if (fast_k(problems[q].k)) continue;
+    const fp4_status st = run_problem(problems[q], tiles[q], s);
+    if (st != FP4_OK) return st;
+  }
+  return FP4_OK;
 }
 
 fp4_status fp4_swiglu_producer(int64_t t, int64_t f, int64_t d, const uint8_t* x_codes, const uint8_t* x_scales,

@@ -186,10 +186,10 @@ __device__ __forceinline__ void compute_stage(const uint8_t* stage, v16f (&acc)[
 
 // Tile order: XCD-aware (the hardware deals workgroups round-robin to 8 XCDs;
 // remap so that consecutive logical tiles share an XCD and its L2), then
-// grouped along M so neighbouring tiles reuse A rows and B columns.
-__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
-  int64_t pid = blockIdx.x;
-  const int64_t num = gridDim.x;
+// grouped along M so neighbouring tiles reuse A rows and B columns.  `pid` is
+// the workgroup's index among the `num` workgroups of its product.
+__device__ __forceinline__ void tile_coords_of(int64_t pid, int64_t num, int64_t tiles_m, int64_t tiles_n,
+                                               int64_t& tm, int64_t& tn) {
   if ((num & 7) == 0) pid = (pid & 7) * (num >> 3) + (pid >> 3);
   const int64_t GM = 8;
   const int64_t width = GM * tiles_n;
@@ -199,6 +199,10 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
   const int64_t in_group = pid - group * width;
   tm = first_m + in_group % gsz;
   tn = in_group / gsz;
+}
+
+__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  tile_coords_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
 }
 
 // Generic main loop (any K that is a multiple of 32): global -> registers ->

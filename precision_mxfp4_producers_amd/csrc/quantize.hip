@@ -575,6 +575,6 @@ uint32_t fp4_sign_mask_from_seed(uint64_t seed) {
 
 int fp4_last_hip_error(void) { return g_last_hip_error; }
 
-int fp4_abi_version(void) { return (1 << 16) | 3; }
+int fp4_abi_version(void) { return (1 << 16) | 4; }
 
 }  // extern "C"

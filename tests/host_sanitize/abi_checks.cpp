@@ -62,6 +62,26 @@ int main() {
   expect("pair tiles", fp4_gemm_pair(big, big, 256, b, b, b, b, b, b, b, b, c, big, 0, nullptr), FP4_ESHAPE);
   expect("pair k0 acc", fp4_gemm_pair(64, 64, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                       nullptr, c, 64, 1, nullptr), FP4_OK);
+  {
+    const fp4_gemm_problem ok{256, 256, 256, b, b, b, b, nullptr, nullptr, nullptr, nullptr, c, 256, 0};
+    fp4_gemm_problem g[2] = {ok, ok};
+    g[1].ldc = 255;
+    expect("grouped ldc", fp4_gemm_grouped(g, 2, nullptr), FP4_ESHAPE);
+    g[1] = ok;
+    g[1].b2_codes = b;
+    expect("grouped partial pair", fp4_gemm_grouped(g, 2, nullptr), FP4_EINVAL);
+    expect("grouped count", fp4_gemm_grouped(g, FP4_GEMM_GROUP_MAX + 1, nullptr), FP4_EINVAL);
+    expect("grouped null", fp4_gemm_grouped(nullptr, 1, nullptr), FP4_EINVAL);
+    const int64_t half = (int64_t)256 * 32768;               // 2^30 tiles each, 2^31 together
+    const fp4_gemm_problem wide{half, half, 256, b, b, b, b, nullptr, nullptr, nullptr, nullptr, c, half, 0};
+    fp4_gemm_problem w[2] = {wide, wide};
+    expect("grouped total tiles", fp4_gemm_grouped(w, 2, nullptr), FP4_ESHAPE);
+    fp4_gemm_problem e[2] = {ok, ok};
+    e[0].m = 0;
+    e[1].k = 0;
+    e[1].accumulate = 1;
+    expect("grouped empty", fp4_gemm_grouped(e, 2, nullptr), FP4_OK);
+  }
   uint16_t* h = static_cast<uint16_t*>(p);
   expect("swiglu ht pair", fp4_swiglu_producer(32, 32, 32, b, b, b, b, h, h, b, b, b, nullptr, 0, nullptr), FP4_EINVAL);
   expect("swiglu tiles", fp4_swiglu_producer(big, big, 32, b, b, b, b, h, h, b, b, b, b, 0, nullptr), FP4_ESHAPE);

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_hot_path_calls():
     names = declared_functions()
     for n in ("fp4_quantize_rows", "fp4_quantize_cols", "fp4_quantize_dual", "fp4_quantize_w2d32", "fp4_gemm",
-              "fp4_gemm_pair",
+              "fp4_gemm_pair", "fp4_gemm_grouped",
               "fp4_swiglu_producer", "fp4_swiglu_backward", "fp4_swiglu_backward_producer",
               "fp4_gemm_swiglu_backward_producer", "fp4_nv_quantize_rows", "fp4_nv_quantize_w2d16", "fp4_nv_gemm"):
         assert n in names
@@ -50,7 +50,7 @@ def test_host_only_calls():
     from oracle import philox as P
     lib = mx.load(LIB)
     assert lib.fp4_abi_version() >> 16 == 1
-    assert lib.fp4_abi_version() & 0xFFFF >= 3      # fp4_gemm_pair, fp4_quantize_dual; the fp4_nv_* calls
+    assert lib.fp4_abi_version() & 0xFFFF >= 4      # fp4_gemm_pair, fp4_quantize_dual, the fp4_nv_* calls, fp4_gemm_grouped
     # the library's host sign-mask helper agrees with the oracle's generator
     for seed in (0, 1, 2 ** 40 + 7):
         assert mx.fp4_sign_mask_from_seed(seed) == P.sign_mask_from_seed(seed)
@@ -191,6 +191,44 @@ def test_empty_calls_are_noops_without_gpu_work():
     assert lib.fp4_gemm(-32, 64, 64, None, None, None, None, None, 64, 0, None) == 2
 
 
+def test_grouped_gemm_checks_every_problem_before_any_launch():
+    """fp4_gemm_grouped answers bad counts and each problem's errors on the
+    host, and checks all problems before it enqueues anything: a valid first
+    problem beside an invalid second one gives the second one's error, not a
+    launch failure (there is no GPU here)."""
+    import precision_mxfp4_producers_amd as mx
+    lib = mx.load(LIB)
+    P = mx._GemmProblem
+    v = ctypes.c_void_p
+    p = v(4096)
+
+    def call(*probs, count=None):
+        arr = (P * max(1, len(probs)))(*probs)
+        return lib.fp4_gemm_grouped(ctypes.cast(arr, v), len(probs) if count is None else count, None)
+
+    good = P(256, 256, 256, p, p, p, p, None, None, None, None, p, 256, 0)
+    assert lib.fp4_gemm_grouped(None, 0, None) == 0
+    assert lib.fp4_gemm_grouped(None, 1, None) == 1
+    assert call(good, count=-1) == 1
+    assert call(good, count=5) == 1
+    assert call(good, P(256, 256, 48, p, p, p, p, None, None, None, None, p, 256, 0)) == 2       # k % 32
+    assert call(good, P(256, 256, 256, p, p, p, p, None, None, None, None, p, 255, 0)) == 2      # ldc < n
+    assert call(good, P(256, 256, 256, p, p, p, p, None, None, None, None, p, 256, 2)) == 1      # accumulate
+    assert call(good, P(256, 256, 256, p, p, p, None, None, None, None, None, p, 256, 0)) == 1   # b_scales
+    assert call(good, P(256, 256, 256, p, p, p, p, p, p, p, None, p, 256, 0)) == 1               # pair, 3 of 4
+    assert call(good, P(256, 256, 256, p, p, p, p, p, p, p, v(4100), p, 256, 0)) == 3            # pair alignment
+    assert call(good, P(256, 256, 256, p, p, p, p, None, None, None, None, v(4100), 256, 0)) == 3
+    huge = 1 << 40
+    assert call(good, P(huge, huge, 256, p, p, p, p, None, None, None, None, p, huge, 0)) == 2
+    # together above 2^31 - 1 tiles, each alone below
+    half = 256 * 32768                                     # 2^30 tiles each
+    big = P(half, half, 256, p, p, p, p, None, None, None, None, p, half, 0)
+    assert call(big, big) == 2
+    # empty products, and K = 0 accumulating, need no device work
+    assert call(P(0, 256, 256, None, None, None, None, None, None, None, None, None, 256, 0),
+                P(256, 256, 0, None, None, None, None, None, None, None, None, p, 256, 1)) == 0
+
+
 def test_header_compiles_and_links_as_plain_c(tmp_path):
     """include/mxfp4.h is a C header: a C11 program built with gcc against it
     links to the library and gets the documented host-check answers."""
@@ -211,6 +249,12 @@ int main(void) {
   if (fp4_quantize_rows((const uint16_t*)4096, 32, 32, 32, (uint8_t*)4096, (uint8_t*)4096, (fp4_round)5, 0, 0, NULL)
       != FP4_EINVAL) ++fails;
   if (fp4_nv_gemm(0, 64, 64, NULL, NULL, NULL, 1, NULL, NULL, NULL, 0, NULL, 64, 0, NULL) != FP4_OK) ++fails;
+  {
+    fp4_gemm_problem g[2] = {{0, 64, 64, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 64, 0},
+                             {64, 64, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, (float*)4096, 64, 1}};
+    if (fp4_gemm_grouped(g, 2, NULL) != FP4_OK) ++fails;
+    if (fp4_gemm_grouped(g, FP4_GEMM_GROUP_MAX + 1, NULL) != FP4_EINVAL) ++fails;
+  }
   printf("c_abi: %d failure(s)\n", fails);
   return fails;
 }

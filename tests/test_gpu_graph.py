@@ -39,7 +39,11 @@ def build_step(mx, t=256, d=512, f=384, seed=3):
          "nvdy": [u8(t, d // 2), u8(t, d // 16), torch.empty(1, device="cuda"), torch.empty(1, device="cuda")],
          "nvw2": [u8(d, f // 2), u8(d, f // 16), u8(f, d // 2), u8(f, d // 16), torch.empty(1, device="cuda"),
                   torch.empty(1, device="cuda")],
-         "nvdh": torch.empty((t, f), dtype=torch.float32, device="cuda")}
+         "nvdh": torch.empty((t, f), dtype=torch.float32, device="cuda"),
+         # the backward contractions again, as one grouped launch
+         "dhg": torch.empty((t, f), dtype=torch.float32, device="cuda"),
+         "dw2g": torch.empty((d, f), dtype=torch.float32, device="cuda"),
+         "dxg": torch.empty((t, d), dtype=torch.float32, device="cuda")}
 
     def run():
         mx.fp4_quantize_rows(dv["X"], codes=o["xr"][0], scales=o["xr"][1])
@@ -66,6 +70,12 @@ def build_step(mx, t=256, d=512, f=384, seed=3):
         mx.fp4_nv_quantize_w2d16(dv["W2"], out=o["nvw2"])
         mx.fp4_nv_gemm(o["nvdy"][0], o["nvdy"][1], o["nvdy"][2], o["nvw2"][2], o["nvw2"][3], o["nvw2"][4],
                        c=o["nvdh"])
+        mx.fp4_gemm_grouped([
+            dict(a_codes=o["dyc"][0], a_scales=o["dyc"][1], b_codes=o["hc"][0], b_scales=o["hc"][1], c=o["dw2g"]),
+            dict(a_codes=o["dyr"][0], a_scales=o["dyr"][1], b_codes=o["w2"][2], b_scales=o["w2"][3], c=o["dhg"]),
+            dict(a_codes=o["bwd"][0], a_scales=o["bwd"][1], b_codes=o["w1c"][0], b_scales=o["w1c"][1],
+                 a2_codes=o["bwd"][2], a2_scales=o["bwd"][3], b2_codes=o["w3c"][0], b2_scales=o["w3c"][1],
+                 c=o["dxg"])])
 
     def snapshot():
         torch.cuda.synchronize()
@@ -83,6 +93,8 @@ def test_captured_step_replays_match_eager(gpu_lib, f):
     run, snapshot, o = build_step(gpu_lib, f=f)
     run()
     eager = snapshot()
+    for grouped, alone in (("dhg", "dh"), ("dw2g", "dw2"), ("dxg", "dx2")):
+        assert torch.equal(o[grouped], o[alone]), f"grouped {grouped} differs from its separate call"
     # poison every output, then capture
     for v in o.values():
         for x in (v if isinstance(v, (list, tuple)) else [v]):
