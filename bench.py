@@ -79,12 +79,17 @@ def parse():
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_fast_kernel_ffn_step_8192x4096x14336_traffic.md")
-GEMM_SOURCE = os.path.join(ROOT, "precision_mxfp4_producers_amd", "csrc", "gemm.hip")
+# the sources gemm_fast_kernel is built from (its epilogue, main loop and helpers)
+GEMM_SOURCES = [os.path.join(ROOT, "precision_mxfp4_producers_amd", "csrc", f)
+                for f in ("gemm.hip", "gemm_core.h", "mx_device.h")]
 
 
 def gemm_source_hash():
     import hashlib
-    return hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, launches):
@@ -98,7 +103,7 @@ def measured_traffic(workload, launches):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    if (fields.get("gemm.hip sha256 (first 16 hex)") != gemm_source_hash() or fields.get("workload") != workload
+    if (fields.get("gemm kernel sources sha256 (first 16 hex)") != gemm_source_hash() or fields.get("workload") != workload
             or fields.get("gemm launches per step") != str(launches)):
         return None
     try:
