@@ -18,15 +18,26 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
-// Two fp32 -> packed bf16 (x low), round to nearest even, NaN -> 0x7FC0.
-// gfx950's v_cvt_pk_bf16_f32 rounds to nearest even on every non-NaN fp32
-// pattern (checked against the integer rounding on all 2^32 inputs); a NaN
-// keeps its sign and upper payload bits there, so NaN inputs are first
-// replaced by the canonical fp32 quiet NaN 0x7FC00000, which converts to
-// 0x7FC0 (one compare and one select per value).
+// maxNum against the canonical fp32 quiet NaN 0x7FC00000 (first operand):
+// gfx950's v_max_f32 returns x for every non-NaN x and 0x7FC00000 for every
+// quiet NaN x (checked over all 2^32 patterns in the kernels' IEEE mode with
+// fp32 denormals kept); a signalling NaN keeps its payload, but the callers
+// only pass results of arithmetic, which are never signalling.  The asm keeps
+// the compiler from folding maxNum(NaN, x) to x.
+__device__ __forceinline__ float canon_qnan(float x) {
+  float r;
+  asm("v_max_f32 %0, 0x7fc00000, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// Two fp32 arithmetic results -> packed bf16 (x low), round to nearest even,
+// NaN -> 0x7FC0.  gfx950's v_cvt_pk_bf16_f32 rounds to nearest even on every
+// non-NaN fp32 pattern (checked against the integer rounding on all 2^32
+// inputs); a NaN keeps its sign and upper payload bits there, so NaNs are
+// first made the canonical quiet NaN, which converts to 0x7FC0 (one v_max per
+// value; a compare and a select before).
 __device__ __forceinline__ uint32_t bf16_pack2_rne(float x, float y) {
-  const float qnan = __uint_as_float(0x7FC00000u);
-  const bf16x2_t v = {(__bf16)((x != x) ? qnan : x), (__bf16)((y != y) ? qnan : y)};
+  const bf16x2_t v = {(__bf16)canon_qnan(x), (__bf16)canon_qnan(y)};
   return __builtin_bit_cast(uint32_t, v);
 }
 

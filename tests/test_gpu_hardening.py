@@ -454,3 +454,43 @@ def test_sr_rule_on_fp32_magnitudes_at_the_threshold(gpu_lib):
     got = host(out).view(np.uint32)
     want = F.sr_code(yy.astype(np.float64), uu).astype(np.uint32)
     assert_same(got, want, "SR codes on fp32 magnitudes")
+
+
+def test_bf16_rounding_of_arithmetic_results(gpu_lib):
+    """The bf16 rounding the SwiGLU producer and the backward producers apply to
+    their fp32 results (hardware RNE after a maxNum against the canonical quiet
+    NaN), on every quiet NaN pattern of both signs, on NaNs that GPU arithmetic
+    produces (inf - inf, 0 * inf, NaN inputs carried through a product), and on
+    finite values around every bf16 rounding boundary, subnormals, the overflow
+    threshold and the infinities: equal to the oracle's RNE with NaN -> 0x7FC0."""
+    from precision_mxfp4_producers_amd.build import probe_path
+    path = probe_path("bf16_probe")
+    if not os.path.exists(path):
+        pytest.fail(f"{path} missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.bf16_pack_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.bf16_pack_probe.restype = ctypes.c_int
+    rng = np.random.default_rng(103)
+    qnan = (np.arange(1 << 22, dtype=np.uint32) | np.uint32(0x7FC00000))          # every quiet NaN, + sign
+    hi16 = np.arange(1 << 16, dtype=np.uint32) << 16                                  # every bf16 pattern ...
+    lows = np.uint32([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF])                          # ... with the tie cases
+    fin = (hi16[:, None] | lows[None, :]).reshape(-1)
+    fin = fin[(fin & 0x7FFFFFFF) <= 0x7F800000]                                       # finite and infinities
+    rnd = rng.integers(0, 1 << 32, size=1 << 21, dtype=np.uint64).astype(np.uint32)
+    rnd = rnd[(rnd & 0x7FFFFFFF) <= 0x7F800000]
+    bits = np.concatenate([qnan, qnan | np.uint32(0x80000000), fin, rnd])
+    if len(bits) % 2:
+        bits = np.append(bits, np.uint32(0))
+    x = torch.from_numpy(bits.view(np.float32)).cuda()
+    # NaNs made by arithmetic on the GPU: inf - inf, 0 * inf, and payload NaNs through a product
+    inf = torch.full((4096,), float("inf"), device="cuda")
+    made = torch.cat([inf - inf, torch.zeros_like(inf) * inf, x[: 1 << 20] * 1.5, -x[: 1 << 20]])
+    x = torch.cat([x, made])
+    n = x.numel() // 2
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    assert lib.bf16_pack_probe(x.data_ptr(), out.data_ptr(), n, torch.cuda.current_stream().cuda_stream) == 0
+    got = host(out).view(np.uint32)
+    xs = host(x)
+    want16 = S.f32_to_bf16_rne(xs).astype(np.uint32)
+    want = want16[0::2] | (want16[1::2] << 16)
+    assert_same(got, want, "bf16 rounding with NaN -> 0x7FC0")
