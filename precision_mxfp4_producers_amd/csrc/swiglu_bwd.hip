@@ -223,13 +223,23 @@ __global__ __launch_bounds__(kFbThreads) void swiglu_bwd_producer_kernel(
     {
       const int k = tid >> 8, c = (tid >> 7) & 1, tb = (tid >> 6) & 1, cp = tid & 63;
       if (32 * tb < nrow && 2 * cp < ncol) {
+        // value i of column 2cp+c as fp32 with the fixed sign d_(i mod 16):
+        // the low half by a shift and an add of the sign bit (adding bit 31
+        // flips it), the high half by one and-xor; c is uniform over the wave
         float f[32];
+        const uint8_t* src = gs[k] + (32 * tb) * kFbPitch + cp * 4;
+        if (__builtin_amdgcn_readfirstlane(c) == 0) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const uint32_t v = *reinterpret_cast<const uint32_t*>(gs[k] + (32 * tb + i) * kFbPitch + cp * 4);
-          uint32_t bb = (v >> (16 * c)) & 0xFFFFu;
-          bb ^= ((sign_mask16 >> (i & 15)) & 1u) << 15;   // d_(i mod 16)
-          f[i] = bf16_bits_to_f32(bb);
+          for (int i = 0; i < 32; ++i) {
+            const uint32_t v = *reinterpret_cast<const uint32_t*>(src + i * kFbPitch);
+            f[i] = __uint_as_float((v << 16) + (((sign_mask16 >> (i & 15)) & 1u) << 31));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const uint32_t v = *reinterpret_cast<const uint32_t*>(src + i * kFbPitch);
+            f[i] = __uint_as_float((v & 0xFFFF0000u) ^ (((sign_mask16 >> (i & 15)) & 1u) << 31));
+          }
         }
         h32_fp32(f);
         int e;
