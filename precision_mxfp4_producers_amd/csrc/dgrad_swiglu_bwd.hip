@@ -201,12 +201,11 @@ __global__ __launch_bounds__(kFastThreads) void dgrad_swiglu_bwd_kernel(
 #pragma unroll
       for (int i = 0; i < 32; ++i)
         v[i] = *reinterpret_cast<const uint32_t*>(smem + db_chunk(32 * tb + i, cp >> 2) + 16 * k + 4 * (cp & 3));
-      h32_sign_words(v, sign_mask16);
       const int64_t t0 = m0 + 32 * tb;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         float f[32];
-        h32_half(v, c, f);
+        h32_column(v, c, sign_mask16, f);
         h32_fp32(f);
         int e;
         const uint4 code = encode32_rtn(f, e);

@@ -89,9 +89,11 @@ __device__ __forceinline__ void swiglu_quad(const v16f& acc_a, const v16f& acc_b
 
 // RTN MXFP4 of one 32-value bf16 block given as 16 packed words.
 __device__ __forceinline__ uint4 encode_block_bf16(const uint32_t (&w)[16], int& e_out) {
-  uint32_t m = 0;
+  // largest 15-bit magnitude pattern: packed 16-bit maxima, one final pair
+  u16x2_t mm = {0, 0};
 #pragma unroll
-  for (int j = 0; j < 16; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+  for (int j = 0; j < 16; ++j) mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2_t, w[j] & 0x7FFF7FFFu));
+  const uint32_t m = max((uint32_t)mm[0], (uint32_t)mm[1]);
   const int e = upward_exp(m << 16);
   const float sc = pow2_scale(e);
   e_out = e;
@@ -130,13 +132,12 @@ __device__ __forceinline__ void quantize_h_tile(const uint8_t* smem, int64_t m0,
     uint32_t v[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) v[i] = *reinterpret_cast<const uint32_t*>(smem + (32 * tb + i) * kHPitch + cp * 4);
-    h32_sign_words(v, sign_mask16);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int64_t col = n0 + 2 * cp + c;
       if (col >= Fdim) continue;
       float fv[32];
-      h32_half(v, c, fv);
+      h32_column(v, c, sign_mask16, fv);
       h32_fp32(fv);
       int e;
       const uint4 code = encode32_rtn(fv, e);
@@ -291,12 +292,11 @@ __device__ __forceinline__ void swiglu_epilogue_staged(
     uint32_t v[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) v[i] = *reinterpret_cast<const uint32_t*>(hs + (32 * tb + i) * kHPitch + 4 * (cp ^ (tb << 3)));
-    h32_sign_words(v, sign_mask16);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int64_t col = n0 + 2 * cp + c;
       float fv[32];
-      h32_half(v, c, fv);
+      h32_column(v, c, sign_mask16, fv);
       h32_fp32(fv);
       int e;
       const uint4 code = encode32_rtn(fv, e);

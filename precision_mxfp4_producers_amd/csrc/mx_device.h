@@ -237,17 +237,17 @@ __device__ __forceinline__ void h32_fp32(float (&f)[32]) {
   for (int j = 0; j < 32; ++j) f[j] = __fmul_rn(f[j], c);
 }
 
-// Fixed-sign H32 inputs of a column pair: word k holds token k of two
-// columns (low and high bf16); the sign d_(k mod 16) flips both halves at
-// once, and h32_half then unpacks the values of one column as fp32.
-__device__ __forceinline__ void h32_sign_words(uint32_t (&v)[32], uint32_t sign_mask16) {
+// Fixed-sign H32 inputs of one column of a pair: word k holds token k of two
+// columns (low and high bf16).  Value k of column c as fp32 with the sign
+// d_(k mod 16) applied, one instruction per value: the low half by a shift
+// and an add of the sign bit (adding bit 31 flips it), the high half by one
+// and-xor.  sign_mask16 = 0 unpacks without signs.
+__device__ __forceinline__ void h32_column(const uint32_t (&v)[32], int c, uint32_t sign_mask16, float (&f)[32]) {
 #pragma unroll
-  for (int k = 0; k < 32; ++k) v[k] ^= ((sign_mask16 >> (k & 15)) & 1u) * 0x80008000u;
-}
-
-__device__ __forceinline__ void h32_half(const uint32_t (&v)[32], int c, float (&f)[32]) {
-#pragma unroll
-  for (int k = 0; k < 32; ++k) f[k] = __uint_as_float(c ? (v[k] & 0xFFFF0000u) : (v[k] << 16));
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t s = ((sign_mask16 >> (k & 15)) & 1u) << 31;
+    f[k] = __uint_as_float(c ? ((v[k] & 0xFFFF0000u) ^ s) : ((v[k] << 16) + s));
+  }
 }
 
 // RTN MXFP4 of one 32-value fp32 block: upward scale of its maximum, codes.

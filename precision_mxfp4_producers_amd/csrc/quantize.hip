@@ -152,11 +152,10 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     uint32_t v[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) v[k] = *reinterpret_cast<const uint32_t*>(tile + (32 * tb + k) * kColPitch + cp * 4);
-    if constexpr (kH32) h32_sign_words(v, sign_mask16);                // d_(k mod 16)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float f[32];
-      h32_half(v, c, f);
+      h32_column(v, c, kH32 ? sign_mask16 : 0u, f);     // d_(k mod 16) with H32
       if constexpr (kH32) h32_fp32(f);
       code[c] = encode32_rtn(f, ex[c]);
     }
@@ -276,11 +275,10 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     uint32_t v[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) v[k] = *reinterpret_cast<const uint32_t*>(tile + (32 * tb + k) * kDualPitch + cp * 4);
-    if constexpr (kH32) h32_sign_words(v, sign_mask16);                // d_(k mod 16)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float f[32];
-      h32_half(v, c, f);
+      h32_column(v, c, kH32 ? sign_mask16 : 0u, f);     // d_(k mod 16) with H32
       if constexpr (kH32) h32_fp32(f);
       code[u][c] = encode32_rtn(f, ex[u][c]);
     }
