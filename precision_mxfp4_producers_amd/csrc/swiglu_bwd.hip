@@ -125,6 +125,9 @@ __device__ __forceinline__ void fb_load(FbIn& in, const float* dh, int64_t lddh,
   }
 }
 
+// kIdx32: the tensors hold at most 2^34 elements, so every Philox counter's
+// second word is 0 (sr_words32).
+template <bool kIdx32>
 __global__ __launch_bounds__(kFbThreads) void swiglu_bwd_producer_kernel(
     int64_t T, int64_t Fdim, const float* __restrict__ dh, int64_t lddh, const uint16_t* __restrict__ a,
     const uint16_t* __restrict__ b, FbOut oa, FbOut ob, uint64_t seed, uint32_t sign_mask16) {
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(kFbThreads) void swiglu_bwd_producer_kernel(
     // the tensor is uniform over each wave
     {
       const int k = tid >> 8, r = (tid >> 2) & 63, blk = tid & 3;
-      const FbOut& o = k ? ob : oa;
+      const FbOut& o = __builtin_amdgcn_readfirstlane(k) ? ob : oa;       // wave-uniform
       const int64_t row = r0 + r, col0 = c0 + 32 * blk;
       const bool ok = r < nrow && 32 * blk < ncol;
       uint32_t w[16];
@@ -208,7 +211,14 @@ __global__ __launch_bounds__(kFbThreads) void swiglu_bwd_producer_kernel(
       const uint64_t blk0 = ((uint64_t)row * (uint64_t)Fdim + (uint64_t)col0) >> 2;   // first Philox counter
       uint32_t packed[4];
       sr_encode<16>(w, e, [&](int q, uint32_t* u) {
-        const u32x4 a = sr_words(blk0 + 2 * q, seed, o.offset), b = sr_words(blk0 + 2 * q + 1, seed, o.offset);
+        u32x4 a, b;
+        if constexpr (kIdx32) {
+          a = sr_words32((uint32_t)blk0 + 2u * q, seed, o.offset);
+          b = sr_words32((uint32_t)blk0 + 2u * q + 1u, seed, o.offset);
+        } else {
+          a = sr_words(blk0 + 2 * q, seed, o.offset);
+          b = sr_words(blk0 + 2 * q + 1, seed, o.offset);
+        }
         u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w; u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
       }, packed);
       if (ok) {
@@ -311,7 +321,11 @@ extern "C" fp4_status fp4_swiglu_backward_producer(
   if (gy > kMaxGridY || gx > kMaxGridX || lddh >= (int64_t(1) << 23)) return FP4_ESHAPE;   // 32-bit buffer offsets
   const FbOut oa{da_codes, da_scales, dat_codes, dat_scales, offset_a};
   const FbOut ob{db_codes, db_scales, dbt_codes, dbt_scales, offset_b};
-  hipLaunchKernelGGL(swiglu_bwd_producer_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kFbThreads), 0,
-                     as_stream(stream), t, f, dh, lddh, a_bf16, b_bf16, oa, ob, seed, sign_mask16 & 0xFFFFu);
+  if (t <= (int64_t(1) << 34) / f)                        // t * f <= 2^34: counters below 2^32
+    hipLaunchKernelGGL(swiglu_bwd_producer_kernel<true>, dim3((unsigned)gx, (unsigned)gy), dim3(kFbThreads), 0,
+                       as_stream(stream), t, f, dh, lddh, a_bf16, b_bf16, oa, ob, seed, sign_mask16 & 0xFFFFu);
+  else
+    hipLaunchKernelGGL(swiglu_bwd_producer_kernel<false>, dim3((unsigned)gx, (unsigned)gy), dim3(kFbThreads), 0,
+                       as_stream(stream), t, f, dh, lddh, a_bf16, b_bf16, oa, ob, seed, sign_mask16 & 0xFFFFu);
   return launch_status();
 }
