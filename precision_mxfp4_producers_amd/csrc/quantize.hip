@@ -39,7 +39,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // row loop issues the loads of kRowsPerPass rows before using any of them.
 constexpr int kRowsPerPass = 2;
 
-template <bool kSR>
+// kIdx32 (SR only): the tensor holds at most 2^34 elements, so every Philox
+// counter's second word is 0 (sr_words32).
+template <bool kSR, bool kIdx32 = false>
 __device__ __forceinline__ uint32_t encode_row_chunk(uint4 v, int e, int64_t r, int64_t cols, int64_t c8,
                                                      uint64_t seed, uint64_t offset) {
   if constexpr (kSR) {
@@ -47,7 +49,14 @@ __device__ __forceinline__ uint32_t encode_row_chunk(uint4 v, int e, int64_t r, 
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t packed;
     sr_encode<4>(w, e, [&](int, uint32_t* u) {
-      const u32x4 a = sr_words(blk0, seed, offset), b = sr_words(blk0 + 1u, seed, offset);
+      u32x4 a, b;
+      if constexpr (kIdx32) {
+        a = sr_words32((uint32_t)blk0, seed, offset);
+        b = sr_words32((uint32_t)blk0 + 1u, seed, offset);
+      } else {
+        a = sr_words(blk0, seed, offset);
+        b = sr_words(blk0 + 1u, seed, offset);
+      }
       u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w; u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
     }, &packed);
     return packed;
@@ -56,7 +65,7 @@ __device__ __forceinline__ uint32_t encode_row_chunk(uint4 v, int e, int64_t r, 
   }
 }
 
-template <bool kSR>
+template <bool kSR, bool kIdx32 = false>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint64_t seed, uint64_t offset) {
@@ -78,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
       const uint32_t m = max_quad(bf16_absmax8(v[j].x, v[j].y, v[j].z, v[j].w));
       const int e = upward_exp(m << 16);
       if (col_ok && r < rows) {
-        const uint32_t packed = encode_row_chunk<kSR>(v[j], e, r, cols, c8, seed, offset);
+        const uint32_t packed = encode_row_chunk<kSR, kIdx32>(v[j], e, r, cols, c8, seed, offset);
         *reinterpret_cast<uint32_t*>(codes + r * (cols >> 1) + c8 * 4) = packed;
         if ((c8 & 3) == 0) scales[r * (cols >> 5) + (c8 >> 2)] = (uint8_t)(e + 127);
       }
@@ -206,7 +215,7 @@ constexpr int kDualPitch = kDualW * 2 + 16;              // bytes per staged tok
 constexpr int kDualCodePitch = kDualTok / 2 + 16;        // bytes per staged column of codes
 static_assert(kDualW * kDualCodePitch <= kDualTok * kDualPitch, "column codes fit in the tile buffer");
 
-template <bool kSR, bool kH32>
+template <bool kSR, bool kH32, bool kIdx32 = false>
 __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* __restrict__ row_codes,
     uint8_t* __restrict__ row_scales, uint64_t seed, uint64_t offset, uint8_t* __restrict__ codes_t,
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
       const int e = upward_exp(m << 16);
       if (r < ntok && ch * 8 < ncol) {
         const int64_t gr = t0 + r, c8 = (c0 >> 3) + ch;
-        const uint32_t packed = encode_row_chunk<kSR>(v, e, gr, cols, c8, seed, offset);
+        const uint32_t packed = encode_row_chunk<kSR, kIdx32>(v, e, gr, cols, c8, seed, offset);
         *reinterpret_cast<uint32_t*>(row_codes + gr * (cols >> 1) + c8 * 4) = packed;
         if ((ch & 3) == 0) row_scales[gr * (cols >> 5) + (c8 >> 2)] = (uint8_t)(e + 127);
       }
@@ -473,7 +482,10 @@ fp4_status fp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
   gy = std::min<int64_t>(gy, kMaxGridY);
   dim3 grid((unsigned)gx, (unsigned)gy);
   hipStream_t s = as_stream(stream);
-  if (mode == FP4_SR)
+  if (mode == FP4_SR && rows <= (int64_t(1) << 34) / cols)   // counters below 2^32
+    hipLaunchKernelGGL((quant_rows_kernel<true, true>), grid, dim3(kThreads), 0, s, x, rows, cols, ldx, codes,
+                       scales, seed, offset);
+  else if (mode == FP4_SR)
     hipLaunchKernelGGL(quant_rows_kernel<true>, grid, dim3(kThreads), 0, s, x, rows, cols, ldx, codes,
                        scales, seed, offset);
   else
@@ -518,9 +530,16 @@ fp4_status fp4_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
   dim3 grid((unsigned)gx, (unsigned)gy);
   hipStream_t s = as_stream(stream);
   const uint32_t m16 = hadamard == 32 ? (sign_mask16 & 0xFFFFu) : 0u;
-  if (mode == FP4_SR && hadamard == 32)
+  const bool idx32 = rows <= (int64_t(1) << 34) / cols;  // counters below 2^32
+  if (mode == FP4_SR && hadamard == 32 && idx32)
+    hipLaunchKernelGGL((quant_dual_kernel<true, true, true>), grid, dim3(kDualThreads), 0, s, x, rows, cols, ldx,
+                       row_codes, row_scales, seed, offset, codes_t, scales_t, m16);
+  else if (mode == FP4_SR && hadamard == 32)
     hipLaunchKernelGGL((quant_dual_kernel<true, true>), grid, dim3(kDualThreads), 0, s, x, rows, cols, ldx, row_codes,
                        row_scales, seed, offset, codes_t, scales_t, m16);
+  else if (mode == FP4_SR && idx32)
+    hipLaunchKernelGGL((quant_dual_kernel<true, false, true>), grid, dim3(kDualThreads), 0, s, x, rows, cols, ldx,
+                       row_codes, row_scales, seed, offset, codes_t, scales_t, m16);
   else if (mode == FP4_SR)
     hipLaunchKernelGGL((quant_dual_kernel<true, false>), grid, dim3(kDualThreads), 0, s, x, rows, cols, ldx, row_codes,
                        row_scales, seed, offset, codes_t, scales_t, m16);
