@@ -140,7 +140,8 @@ __global__ __launch_bounds__(256) void nv_amax_kernel(const uint16_t* __restrict
 // encoding either.
 constexpr int kNvRowsPerPass = 2;
 
-template <bool kSR>
+// kIdx32 (SR only): at most 2^34 elements, every Philox counter's second word 0.
+template <bool kSR, bool kIdx32 = false>
 __device__ __forceinline__ void nv_row_chunk(uint4 v, int64_t r, int64_t cols, int64_t c8, bool col_ok,
                                              uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                              float* __restrict__ factors, const uint32_t* __restrict__ amax,
@@ -157,7 +158,14 @@ __device__ __forceinline__ void nv_row_chunk(uint4 v, int64_t r, int64_t cols, i
   uint32_t packed;
   if constexpr (kSR) {
     const uint64_t blk = ((uint64_t)r * (uint64_t)cols + (uint64_t)c8 * 8u) >> 2;
-    const u32x4 a = sr_words(blk, seed, offset), b = sr_words(blk + 1u, seed, offset);
+    u32x4 a, b;
+    if constexpr (kIdx32) {
+      a = sr_words32((uint32_t)blk, seed, offset);
+      b = sr_words32((uint32_t)blk + 1u, seed, offset);
+    } else {
+      a = sr_words(blk, seed, offset);
+      b = sr_words(blk + 1u, seed, offset);
+    }
     const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     packed = nv_sr8(w, rr, u);
   } else {
@@ -170,7 +178,7 @@ __device__ __forceinline__ void nv_row_chunk(uint4 v, int64_t r, int64_t cols, i
   }
 }
 
-template <bool kSR>
+template <bool kSR, bool kIdx32 = false>
 __global__ __launch_bounds__(256) void nv_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                       int64_t ldx, uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales, float* __restrict__ factors,
@@ -191,7 +199,7 @@ __global__ __launch_bounds__(256) void nv_rows_kernel(const uint16_t* __restrict
     for (int j = 0; j < kNvRowsPerPass; ++j) {
       const int64_t r = r0 + j * rstep;
       if (r < rows)                                      // uniform over the workgroup
-        nv_row_chunk<kSR>(v[j], r, cols, c8, col_ok, codes, scales, factors, amax, seed, offset);
+        nv_row_chunk<kSR, kIdx32>(v[j], r, cols, c8, col_ok, codes, scales, factors, amax, seed, offset);
     }
   }
 }
@@ -572,7 +580,10 @@ fp4_status fp4_nv_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
   hipLaunchKernelGGL(nv_fill_kernel, dim3((unsigned)ceil_div(panels, 256)), dim3(256), 0, s, amax, panels);
   hipLaunchKernelGGL(nv_amax_kernel, dim3((unsigned)gx, (unsigned)gya), dim3(256), 0, s, x, rows, cols, ldx, amax, 1,
                      nb);
-  if (mode == FP4_SR)
+  if (mode == FP4_SR && rows <= (int64_t(1) << 34) / cols)   // counters below 2^32
+    hipLaunchKernelGGL((nv_rows_kernel<true, true>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x, rows, cols,
+                       ldx, codes, scales, factors, amax, seed, offset);
+  else if (mode == FP4_SR)
     hipLaunchKernelGGL(nv_rows_kernel<true>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x, rows, cols, ldx,
                        codes, scales, factors, amax, seed, offset);
   else
