@@ -117,8 +117,9 @@ def test_grouped_fills_a_part_empty_round(gpu_lib):
 
 
 def test_grouped_with_generic_and_empty_problems(gpu_lib):
-    """K % 256 != 0 and K = 0 problems run as calls of their own beside the
-    shared launch; an empty C is a no-op."""
+    """K % 256 != 0 (plain and pair form, the pair accumulating) and K = 0
+    problems run as calls of their own beside the shared launch; an empty C
+    is a no-op."""
     mx = gpu_lib
     a0, b0 = quantized(mx, 256, 256, 1.0, 31), quantized(mx, 512, 256, 0.02, 32)
     a1, b1 = quantized(mx, 96, 288, 1.0, 33), quantized(mx, 160, 288, 0.02, 34)
@@ -127,12 +128,15 @@ def test_grouped_with_generic_and_empty_problems(gpu_lib):
     zb = torch.zeros((96, 0), dtype=torch.uint8, device="cuda")
     e = torch.zeros((0, 128), dtype=torch.uint8, device="cuda")
     es = torch.zeros((0, 8), dtype=torch.uint8, device="cuda")
-    probs = [prob(a1, b1), prob((z, zs), (zb, zb)), prob(a0, b0)]
+    a2, b2 = quantized(mx, 96, 288, 1e-3, 36), quantized(mx, 160, 288, 0.02, 37)
+    probs = [prob(a1, b1), prob((z, zs), (zb, zb)), prob(a0, b0), prob(a1, b1, a2, b2, accumulate=True,
+                                                                       prev=torch.ones((96, 160), device="cuda"))]
     grouped, separate = run_both(mx, probs)
     for q, (cg, cs) in enumerate(zip(grouped, separate)):
         assert same_bytes(cg, cs), f"problem {q}"
     assert not host(grouped[1]).any()                      # empty sums
     assert within_oracle(grouped[0], [(a1, b1)])
+    assert within_oracle(grouped[3], [(a1, b1), (a2, b2)], c_prev=np.ones((96, 160), dtype=np.float32))
     bd = quantized(mx, 64, 256, 1.0, 35)
     out = mx.fp4_gemm_grouped([prob((e, es), bd), prob(a0, b0)])
     assert out[0].shape == (0, 64) and within_oracle(out[1], [(a0, b0)])
