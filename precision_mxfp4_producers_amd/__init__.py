@@ -83,6 +83,10 @@ def _stream():
 def _dev(t, name):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise Fp4Error(f"{name} must be a CUDA (HIP) tensor")
+    # the kernels run on the current device's current stream: a tensor on
+    # another device would be read through that device's memory, unmapped here
+    if t.device.index != torch.cuda.current_device():
+        raise Fp4Error(f"{name} is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
     return t
 
 
