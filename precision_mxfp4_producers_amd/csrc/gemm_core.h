@@ -273,7 +273,15 @@ __device__ __forceinline__ void main_loop_generic(uint8_t* buf0, uint8_t* buf1, 
 //     interleaved eight-wave loop.
 // Ablations of this loop: without the global loads 251 us, without the LDS
 // writes 225 us, with all-zero operands (less power, higher clock) 209 us; the
-// MFMA pipe itself sustains about 5.6 PFLOP/s on random FP4 data.
+// MFMA pipe itself sustains about 5.6 PFLOP/s on random FP4 data.  (These
+// figures date from when the loop was written; the same launch now takes
+// about 230 us.)  Later, with every load an L2 hit (all K steps reading the
+// lines of step 0): 4% faster at this shape and up to 15% on the short-K ones,
+// at the same clock -- load latency beyond L2, which the one K step between a
+// part's load and its LDS write does not always cover.  Prefetching the lines
+// of step s+6 (one dword per line, into an LDS sink or into registers) ran
+// 11-12% slower: vector loads complete in order, so the prefetch's own miss
+// holds up the next real load.
 constexpr int kLdsA = 0, kLdsB = 2 * BM * BKB, kLdsSA = 4 * BM * BKB, kLdsSB = kLdsSA + 2 * BM * 8;
 static_assert(kLdsSB + 2 * BN * 8 == kSmemBytes, "fast path LDS layout");
 
