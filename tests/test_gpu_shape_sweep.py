@@ -206,3 +206,51 @@ def test_sweep_swiglu_backward_producer(gpu_lib):
         for g, w, nm in zip(got, want, ("dA rows", "dB rows", "dA cols", "dB cols")):
             same(g[0], w[0], nm + " codes")
             same(g[1], w[1], nm + " scales")
+
+
+def test_sweep_nvfp4(gpu_lib):
+    """CTA-local NVFP4: rows (RTN and SR, strided input) and 2D16 weights
+    bit-exact against the oracle, and the contraction over rows x rows and
+    rows x 2D16 columns (one common factor) within the GEMM bound."""
+    from oracle import nvfp4 as N
+    mx = gpu_lib
+
+    def same_f32(got, want, what):
+        same(got.view(torch.int32), np.asarray(want, dtype=np.float32).view(np.int32), what)
+
+    def factors(f, rows):
+        f = np.asarray(f, dtype=np.float32).reshape(-1)
+        return np.repeat(f, (rows + N.PANEL - 1) // N.PANEL) if f.size == 1 else f
+
+    rng = np.random.default_rng(2029)
+    for i in range(CASES):
+        m, n = dims(rng, 20)
+        k = 64 * int(rng.integers(1, 17))
+        seed, off = int(rng.integers(0, 2 ** 63)), int(rng.integers(0, 2 ** 40))
+        case(f"nvfp4 {m}x{n}x{k}")
+        x = synthetic.tensor((m, k), std=float(10.0 ** rng.uniform(-4, 0)), seed=1000 + i, outlier_rate=0.005,
+                             outlier_scale=30.0)
+        w = synthetic.tensor((n, k), std=0.02, seed=1100 + i)
+        mode = N.SR if i % 2 else N.RTN
+        a = mx.fp4_nv_quantize_rows(strided(x, rng), mode, seed, off)
+        for g, wv, nm in zip(a, N.quantize_rows(x, mode, seed, off), ("codes", "scales", "factors", "maxima")):
+            if nm in ("factors", "maxima"):
+                same_f32(g, wv, f"rows {nm}")
+            else:
+                same(g, wv, f"rows {nm}")
+        b = mx.fp4_nv_quantize_rows(dev16(w))
+        c = mx.fp4_nv_gemm(*a[:3], *b[:3])
+        ref, e = N.gemm_ref(host(a[0]), host(a[1]), factors(host(a[2]), m), host(b[0]), host(b[1]),
+                            factors(host(b[2]), n))
+        assert G.within_bound(host(c), ref, e, k=k).all(), "rows x rows outside the bound"
+        # the Dgrad route: W [k][n] in 2D16, its column view [n][k] with one factor
+        wt = synthetic.tensor((k, n), std=0.02, seed=1200 + i)
+        got = mx.fp4_nv_quantize_w2d16(strided(wt, rng))
+        want = N.quantize_w2d16(wt)
+        for g, wv, nm in zip(got[:4], want[:4], ("row codes", "row scales", "col codes", "col scales")):
+            same(g, wv, f"2D16 {nm}")
+        same_f32(got[4], [want[4]], "2D16 factor")
+        c = mx.fp4_nv_gemm(*a[:3], got[2], got[3], got[4])
+        ref, e = N.gemm_ref(host(a[0]), host(a[1]), factors(host(a[2]), m), host(got[2]), host(got[3]),
+                            factors(host(got[4]), n))
+        assert G.within_bound(host(c), ref, e, k=k).all(), "rows x 2D16 columns outside the bound"
