@@ -803,7 +803,7 @@ def cpu_baseline_nv(name, seed=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark measures one GPU's share of the step; --gpus must be 1",
                           "gpus_requested": args.gpus}))
         sys.exit(2)
     import torch

@@ -42,3 +42,17 @@ def test_ffn_workload_shapes_reproduce_parameter_count():
     n = layers * per_layer + D + 2 * vocab * D
     assert vocab * D == g["N_emb"]
     assert n == g["N"]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py --gpus 2 exits with status 2 and a JSON error line before it
+    touches a GPU."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert out.returncode == 2
+    line = json.loads(out.stdout.strip().splitlines()[-1])
+    assert line["gpus_requested"] == 2 and "--gpus must be 1" in line["error"]
