@@ -12,7 +12,7 @@ E2M1 itself (1 sign, 2 exponent, 1 fraction bit; largest magnitude 6) is stated
 in the paper's notation paragraph; its eight magnitudes are
 {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
 
-Readings where the pages leave a step open (each listed in the design doc):
+Readings where the pages leave a step open:
   * ties in round-to-nearest go to the even code (IEEE RNE on one fraction bit);
   * the sign bit is the sign of the input, so -0 and small negatives that round
     to zero encode as 0x8;

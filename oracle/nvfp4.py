@@ -18,7 +18,7 @@
     its whole block and that a saturating scale encoder avoids overflow past
     E4M3's largest finite value, 448.
 
-Readings where the pages leave a step open (each listed in the design doc):
+Readings where the pages leave a step open:
   * E4M3 is the OCP E4M3FN format: bias 7, subnormals m * 2^-9, largest
     finite value 448, no infinity; rounding to nearest, ties to even, saturating
     at 448; 0x7F (NaN) is never produced.
