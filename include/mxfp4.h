@@ -322,9 +322,9 @@ fp4_status fp4_swiglu_backward_producer(int64_t t, int64_t f, const float* dh, i
 
 /*
  * W2 data gradient with the fused SwiGLU backward producer in its epilogue
- * (§3.2: the backward combines the W2 data gradient with the SiLU derivative
- * and produces the representations the W1/W3 data- and weight-gradient
- * contractions consume; §3.1).  Bit-identical to
+ * (§3.2: the gate's derivative is applied to the W2 Dgrad output within the
+ * fused backward step, which emits the operands of the W1/W3 Dgrad and Wgrad
+ * contractions; §3.1).  Bit-identical to
  *   fp4_gemm(t, f, d, dy_codes, dy_scales, w2c_codes, w2c_scales) -> dH (fp32)
  *   fp4_swiglu_backward_producer(t, f, dH, f, a, b, seed, offset_a, offset_b,
  *                                sign_mask16, ...)

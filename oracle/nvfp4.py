@@ -7,8 +7,8 @@
   * §2.2.2 and the §1/§2.2 summaries -- CTA-local NVFP4 derives its outer
     factors inside the tile that owns them (a row factor for the first operand's
     rows, a column factor for the second's) instead of from a tensor-wide
-    maximum; they stay fixed over the K reduction and their product is applied
-    in the GEMM epilogue.
+    maximum; the contraction's inner sum runs on the factor-free values and
+    the two factors multiply the finished sum once, after the K loop.
   * §2.4 -- the CTA-local weight producer keeps the 2D16 invariant: one E4M3
     scale per 16x16 tile, one common fp32 outer factor for both orientations,
     decoded values equal in both layouts.

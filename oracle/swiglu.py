@@ -1,10 +1,11 @@
 """SwiGLU producer arithmetic: the shared exp, forward h and backward dA/dB.
 
 "Format-Aware Fusion for Fast FP4 Pretraining", §3.2 (gated FFN): the paired
-W1/W3 projections are scheduled together and the SiLU-gated product is emitted
-directly as the FP4 input of W2; backward combines the W2 data gradient with
-the SiLU derivative; exact BF16 values stay available where autograd needs them,
-and fusion changes data movement, not the model.
+W1/W3 projections run as one producer whose output, h = SiLU(a) * b, goes out
+already in FP4 for W2; in the backward pass the gradient that W2's Dgrad
+returns is multiplied through the gate's derivative inside the same fused
+step; the saved a and b stay exact bf16, and the fusion moves data only: the
+model computed is unchanged.
 
 Reading of the precision chain (the pages print none): the serial BF16
 schedule.  a, b are the fp32 GEMM outputs rounded to bf16 (RNE) and saved;

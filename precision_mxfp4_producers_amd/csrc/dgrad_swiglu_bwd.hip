@@ -1,8 +1,8 @@
 // W2 data gradient with the SwiGLU backward and the dA/dB producers in its
-// epilogue ("Format-Aware Fusion for Fast FP4 Pretraining", §3.2: the backward
-// combines the W2 data gradient with the SiLU derivative and produces the
-// representations the W1/W3 data- and weight-gradient contractions consume;
-// §3.1: a producer completes every layout its consumers read).
+// epilogue ("Format-Aware Fusion for Fast FP4 Pretraining", §3.2: the gate's
+// derivative is applied to the W2 Dgrad output within the fused backward step,
+// which emits the operands of the W1/W3 Dgrad and Wgrad contractions; §3.1:
+// a producer completes every layout its consumers read).
 //
 // One workgroup owns a 256-token x 256-column tile of dH = dec(dY_r) dec(W2_c)^T
 // (the fast main loop of the GEMM, 8 waves).  The fp32 dH never leaves the
