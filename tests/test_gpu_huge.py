@@ -73,6 +73,14 @@ def test_huge_rows_and_dual_sr(gpu_lib):
     wc = Q.quantize_cols(blk, 32, mask)
     assert np.array_equal(host(cc[:, 16 * tb:16 * tb + 16]), wc[0]), "dual column codes"
     assert np.array_equal(host(cs[:, tb:tb + 1]), wc[1]), "dual column scales"
+    del rc, rs, cc, cs
+    torch.cuda.empty_cache()
+    print(f"[huge] dual SR, plain columns {R}x{C}", flush=True)
+    rc, rs, cc, cs = mx.fp4_quantize_dual(x, mx.FP4_SR, seed, off, 0, 0)
+    assert np.array_equal(rows_of(rc, ROWS), want[0]), "dual (no H32) row codes"
+    wc = Q.quantize_cols(blk, 0, 0)
+    assert np.array_equal(host(cc[:, 16 * tb:16 * tb + 16]), wc[0]), "dual (no H32) column codes"
+    assert np.array_equal(host(cs[:, tb:tb + 1]), wc[1]), "dual (no H32) column scales"
 
 
 def test_huge_nv_rows_sr(gpu_lib):
