@@ -22,7 +22,16 @@ ROWS = [0, 1, 65536, 131071, 131072, 131100, 131135]     # row 131072 starts at 
 GIB = 1 << 30
 
 
+@pytest.fixture(autouse=True)
+def release_memory():
+    """Hand the cached blocks back after each test, so that the next one's
+    free-memory check sees them."""
+    yield
+    torch.cuda.empty_cache()
+
+
 def need(gib):
+    torch.cuda.empty_cache()
     free, _ = torch.cuda.mem_get_info()
     if free < gib * GIB:
         pytest.skip(f"needs {gib} GiB of free device memory, {free / GIB:.0f} free")
